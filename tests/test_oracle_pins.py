@@ -1,0 +1,438 @@
+"""Pins for the fp64 oracle: every check here compares the oracle with something
+it does not compute itself (pure-Python brute force on a dense, unpaged
+layout; closed forms; torch's own attention routine; worked numbers printed on
+the pages).  A second group plants plausible mistakes in the oracle and checks
+that at least one pin catches each.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import step as ostep
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BS = 16
+
+
+# ---------------------------------------------------------------------------
+# helpers written here, independently of the oracle
+# ---------------------------------------------------------------------------
+
+def bits(x):
+    """float array -> bf16 bits by round-to-nearest-even (test-side copy)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def as_float(b):
+    return [float(np.array([int(v) << 16], dtype=np.uint32).view(np.float32)[0]) for v in np.ravel(b)]
+
+
+def page_dense(K, V, block_ids, num_blocks):
+    """Place dense per-position K/V [L, Hkv, D] (bits) into fresh pools."""
+    L, Hkv, D = K.shape
+    kp = np.full((num_blocks, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+    vp = np.full((num_blocks, Hkv, D, BS), 0xFFFF, dtype=np.uint16)
+    for p in range(L):
+        b = block_ids[p // BS]
+        for g in range(Hkv):
+            kp[b, g, p % BS, :] = K[p, g]
+            vp[b, g, :, p % BS] = V[p, g]
+    return kp, vp
+
+
+def brute_force(q_bits, K_bits, V_bits, c, scale, Hkv):
+    """Pure-Python loops over a dense layout: out[j][h][d] for a chunk of n
+    queries at context c, explicit [n, c+n] visibility matrix."""
+    n, Hq, D = q_bits.shape
+    G = Hq // Hkv
+    L = c + n
+    qf = np.array(as_float(q_bits)).reshape(n, Hq, D)
+    Kf = np.array(as_float(K_bits)).reshape(L, Hkv, D)
+    Vf = np.array(as_float(V_bits)).reshape(L, Hkv, D)
+    mask = [[k <= c + j for k in range(L)] for j in range(n)]
+    out = np.zeros((n, Hq, D))
+    for j in range(n):
+        for h in range(Hq):
+            g = h // G
+            sc = []
+            for k in range(L):
+                if mask[j][k]:
+                    dot = 0.0
+                    for d in range(D):
+                        dot += qf[j, h, d] * Kf[k, g, d]
+                    sc.append((k, scale * dot))
+            mx = max(v for _, v in sc)
+            ws = [(k, math.exp(v - mx)) for k, v in sc]
+            tot = sum(w for _, w in ws)
+            for d in range(D):
+                out[j, h, d] = sum(w * Vf[k, g, d] for k, w in ws) / tot
+    return out
+
+
+def random_case(rng, Hq, Hkv, D, c, n, num_blocks=None):
+    L = c + n
+    K = bits(rng.standard_normal((L, Hkv, D)))
+    V = bits(rng.standard_normal((L, Hkv, D)))
+    q = bits(rng.standard_normal((n, Hq, D)))
+    npages = math.ceil(L / BS)
+    nb = num_blocks or npages + 3
+    ids = rng.permutation(nb)[:npages]
+    return q, K, V, ids, nb
+
+
+def run_oracle_chunk(q, K, V, ids, nb, c, Hkv, scale):
+    """Oracle on paged inputs: prefix [0,c) placed by the test, chunk appended
+    by oracle.append, then oracle.attention on one row."""
+    n = q.shape[0]
+    kp, vp = page_dense(K[:c], V[:c], ids, nb)
+    bt = np.zeros((1, len(ids)), dtype=np.int32)
+    bt[0, :] = ids
+    kp, vp = oracle.append(kp, vp, K[c:], V[c:], [0, n], [c], bt)
+    out, lse = oracle.attention(q, kp, vp, [0, n], [c], bt, Hkv, scale)
+    return out, lse, kp, vp, bt
+
+
+# ---------------------------------------------------------------------------
+# C3 attention pins
+# ---------------------------------------------------------------------------
+
+BRUTE_CASES = [
+    (Hq, G, D, c, n)
+    for (Hq, G) in [(1, 1), (4, 1), (4, 2)]
+    for D in (4, 8)
+    for c in (0, 1, 15, 16, 17)
+    for n in (1, 2, 5, 16)
+]
+
+
+@pytest.mark.parametrize("Hq,G,D,c,n", BRUTE_CASES)
+def test_brute_force_dense(Hq, G, D, c, n):
+    rng = np.random.default_rng(hash((Hq, G, D, c, n)) % 2**32)
+    Hkv = Hq // G
+    scale = 1.0 / math.sqrt(D)
+    q, K, V, ids, nb = random_case(rng, Hq, Hkv, D, c, n)
+    out, _, _, _, _ = run_oracle_chunk(q, K, V, ids, nb, c, Hkv, scale)
+    ref = brute_force(q, K, V, c, scale, Hkv)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_softmax_rows_sum_to_one_and_reproduce_output():
+    rng = np.random.default_rng(7)
+    Hq, Hkv, D, c, n = 4, 2, 8, 21, 9
+    scale = 0.3
+    q, K, V, ids, nb = random_case(rng, Hq, Hkv, D, c, n)
+    out, _, kp, vp, bt = run_oracle_chunk(q, K, V, ids, nb, c, Hkv, scale)
+    Vf = np.array(as_float(V)).reshape(c + n, Hkv, D)
+    for j in range(n):
+        for h in range(Hq):
+            w = oracle.softmax_weights(q, kp, bt[0], c, 0, j, h, Hkv, scale)
+            assert w.shape == (c + j + 1,)
+            assert abs(w.sum() - 1.0) < 1e-12
+            assert np.all(w > 0)
+            recon = w @ Vf[: c + j + 1, h // (Hq // Hkv)]
+            assert np.max(np.abs(recon - out[j, h])) < 1e-12
+
+
+@pytest.mark.parametrize("L", [256, 201])
+def test_chunking_invariance(L):
+    """Any chunk size gives the one-shot causal prefill's outputs (P2 section 3;
+    P5 'The payoff'; P4 7.2 asks that chunked and unchunked prefill agree)."""
+    rng = np.random.default_rng(L)
+    Hq, Hkv, D = 4, 2, 16
+    scale = 1.0 / math.sqrt(D)
+    K = bits(rng.standard_normal((L, Hkv, D)))
+    V = bits(rng.standard_normal((L, Hkv, D)))
+    q = bits(rng.standard_normal((L, Hq, D)))
+    npages = math.ceil(L / BS)
+    nb = npages + 5
+    ids = rng.permutation(nb)[:npages]
+    bt = ids[None, :].astype(np.int32)
+    results = {}
+    for C in (1, 3, 16, 64, 100, L):
+        kp = np.full((nb, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+        vp = np.full((nb, Hkv, D, BS), 0xFFFF, dtype=np.uint16)
+        outs = []
+        for a in range(0, L, C):
+            b = min(L, a + C)
+            kp, vp = oracle.append(kp, vp, K[a:b], V[a:b], [0, b - a], [a], bt)
+            o, _ = oracle.attention(q[a:b], kp, vp, [0, b - a], [a], bt, Hkv, scale)
+            outs.append(o)
+        results[C] = np.concatenate(outs)
+    one_shot = results[L]
+    for C, o in results.items():
+        assert np.max(np.abs(o - one_shot)) < 1e-12, C
+
+
+def test_decode_row_equals_last_prefill_row():
+    rng = np.random.default_rng(11)
+    Hq, Hkv, D, n = 8, 2, 32, 77
+    scale = 1.0 / math.sqrt(D)
+    q, K, V, ids, nb = random_case(rng, Hq, Hkv, D, 0, n)
+    full, full_lse, _, _, _ = run_oracle_chunk(q, K, V, ids, nb, 0, Hkv, scale)
+    dec, dec_lse, _, _, _ = run_oracle_chunk(q[n - 1:], K, V, ids, nb, n - 1, Hkv, scale)
+    assert np.max(np.abs(dec[0] - full[n - 1])) < 1e-12
+    assert np.max(np.abs(dec_lse[0] - full_lse[n - 1])) < 1e-12
+
+
+def test_closed_form_single_key():
+    """Context 0 and one query: the only visible key is the token itself, so the
+    output is its V exactly and lse is its scaled score."""
+    rng = np.random.default_rng(3)
+    Hq, Hkv, D = 4, 4, 8
+    q, K, V, ids, nb = random_case(rng, Hq, Hkv, D, 0, 1)
+    out, lse, _, _, _ = run_oracle_chunk(q, K, V, ids, nb, 0, Hkv, 0.5)
+    Vf = np.array(as_float(V)).reshape(1, Hkv, D)
+    assert np.array_equal(out[0], Vf[0])
+    qf = np.array(as_float(q)).reshape(1, Hq, D)
+    Kf = np.array(as_float(K)).reshape(1, Hkv, D)
+    assert np.allclose(lse[0], 0.5 * (qf[0] * Kf[0]).sum(-1), atol=1e-12)
+
+
+@pytest.mark.parametrize("c", [0, 5, 16, 33])
+def test_closed_form_zero_query_cumulative_mean(c):
+    """q = 0 makes every visible key weigh the same, so row j is the mean of V
+    over keys 0..c+j; consecutive rows show exactly which key became visible."""
+    rng = np.random.default_rng(c + 100)
+    Hq, Hkv, D, n = 4, 2, 8, 19
+    _, K, V, ids, nb = random_case(rng, Hq, Hkv, D, c, n)
+    q = np.zeros((n, Hq, D), dtype=np.uint16)
+    out, lse, _, _, _ = run_oracle_chunk(q, K, V, ids, nb, c, Hkv, 0.125)
+    Vf = np.array(as_float(V)).reshape(c + n, Hkv, D)
+    G = Hq // Hkv
+    for j in range(n):
+        for h in range(Hq):
+            mean = Vf[: c + j + 1, h // G].mean(axis=0)
+            assert np.max(np.abs(out[j, h] - mean)) < 1e-12
+            assert abs(lse[j, h] - math.log(c + j + 1)) < 1e-12
+
+
+@pytest.mark.parametrize("c,n", [(0, 40), (37, 23), (64, 1)])
+def test_matches_torch_sdpa_float64(c, n):
+    """Library special case: torch's scaled_dot_product_attention in float64 on
+    the CPU with an explicit boolean mask (c = 0 also with is_causal)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(c * 1000 + n)
+    Hq, Hkv, D = 8, 2, 16
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    q, K, V, ids, nb = random_case(rng, Hq, Hkv, D, c, n)
+    out, _, _, _, _ = run_oracle_chunk(q, K, V, ids, nb, c, Hkv, scale)
+    qt = torch.tensor(as_float(q), dtype=torch.float64).reshape(n, Hq, D).permute(1, 0, 2)
+    Kt = torch.tensor(as_float(K), dtype=torch.float64).reshape(c + n, Hkv, D).permute(1, 0, 2)
+    Vt = torch.tensor(as_float(V), dtype=torch.float64).reshape(c + n, Hkv, D).permute(1, 0, 2)
+    Kt = Kt.repeat_interleave(G, dim=0)
+    Vt = Vt.repeat_interleave(G, dim=0)
+    mask = torch.tensor([[k <= c + j for k in range(c + n)] for j in range(n)])
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask, scale=scale)
+    assert np.max(np.abs(ref.permute(1, 0, 2).numpy() - out)) < 1e-10
+    if c == 0:
+        ref2 = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, is_causal=True, scale=scale)
+        assert np.max(np.abs(ref2.permute(1, 0, 2).numpy() - out)) < 1e-10
+
+
+def test_token_subset_matches_full():
+    rng = np.random.default_rng(5)
+    Hq, Hkv, D, c, n = 4, 2, 8, 10, 30
+    q, K, V, ids, nb = random_case(rng, Hq, Hkv, D, c, n)
+    kp, vp = page_dense(K[:c], V[:c], ids, nb)
+    bt = ids[None, :].astype(np.int32)
+    kp, vp = oracle.append(kp, vp, K[c:], V[c:], [0, n], [c], bt)
+    full, _ = oracle.attention(q, kp, vp, [0, n], [c], bt, Hkv, 0.3, row_chunk=7)
+    sub, _ = oracle.attention(q, kp, vp, [0, n], [c], bt, Hkv, 0.3, tokens=np.array([0, 13, 29]))
+    for t in (0, 13, 29):
+        assert np.array_equal(sub[t], full[t])
+    assert np.isnan(sub[1]).all()
+
+
+# ---------------------------------------------------------------------------
+# C2 append pins
+# ---------------------------------------------------------------------------
+
+def test_append_touches_exactly_the_new_slots_and_is_idempotent():
+    rng = np.random.default_rng(9)
+    Hkv, D = 2, 8
+    ctx = [0, 5, 16, 31]
+    nq = [3, 1, 20, 16]
+    nb = 40
+    bt = rng.permutation(nb)[: 4 * 4].reshape(4, 4).astype(np.int32)
+    T = sum(nq)
+    qsl = np.concatenate([[0], np.cumsum(nq)]).tolist()
+    kp0 = bits(rng.standard_normal((nb, Hkv, BS, D)))
+    vp0 = bits(rng.standard_normal((nb, Hkv, D, BS)))
+    kn = bits(rng.standard_normal((T, Hkv, D)))
+    vn = bits(rng.standard_normal((T, Hkv, D)))
+    kp, vp = oracle.append(kp0, vp0, kn, vn, qsl, ctx, bt)
+    # slots each token must land in, listed here independently
+    slots = set()
+    for s in range(4):
+        for i in range(nq[s]):
+            p = ctx[s] + i
+            slots.add((int(bt[s, p // BS]), p % BS))
+            t = qsl[s] + i
+            assert np.array_equal(kp[bt[s, p // BS], :, p % BS, :], kn[t])
+            assert np.array_equal(vp[bt[s, p // BS], :, :, p % BS], vn[t])
+    assert len(slots) == T  # injective
+    kdiff = np.any(kp != kp0, axis=(1, 3))  # [nb, slot]
+    vdiff = np.any(vp != vp0, axis=(1, 2))
+    changed = {(b, o) for b, o in zip(*np.nonzero(kdiff | vdiff))}
+    assert changed <= slots
+    kp2, vp2 = oracle.append(kp, vp, kn, vn, qsl, ctx, bt)
+    assert np.array_equal(kp2, kp) and np.array_equal(vp2, vp)
+    # input pools are not modified
+    assert not np.shares_memory(kp, kp0)
+
+
+# ---------------------------------------------------------------------------
+# C1 scheduler pins (worked numbers printed on the pages)
+# ---------------------------------------------------------------------------
+
+def load_pins():
+    with open(os.path.join(GOLDEN, "scheduler_pins.json")) as f:
+        return json.load(f)
+
+
+def users_and_prompt(running, prompt):
+    reqs = [oracle.Request(i, 100 + i, 101 + i, True) for i in range(running)]
+    reqs.append(oracle.Request(running, 0, prompt, False))
+    return reqs
+
+
+def run_prompt(running, prompt, budget, cap=0):
+    """Steps until the prompt is fully prefilled; returns (passes, tokens the
+    running users received meanwhile, per-pass chunk sizes)."""
+    reqs = users_and_prompt(running, prompt)
+    passes, delivered, chunks = 0, 0, []
+    while not reqs[-1].is_decode:
+        sch = oracle.schedule(reqs, budget, cap)
+        got = dict(zip(sch["order"], sch["num_scheduled"]))
+        chunks.append(got.get(running, 0))
+        delivered += sum(got.get(i, 0) for i in range(running))
+        passes += 1
+        reqs = oracle.advance(reqs, sch)
+        assert passes < 10000
+    return passes, delivered, chunks
+
+
+def test_pin_chunk_size_vs_budget():
+    pins = load_pins()["chunk_vs_budget"]
+    for budget, chunk in pins["cases"]:
+        sch = oracle.schedule(users_and_prompt(pins["running"], pins["prompt"]), budget)
+        assert sch["num_scheduled"][-1] == chunk
+        assert sch["num_tokens"] == budget
+
+
+def test_pin_passes_and_delivered_tokens():
+    pins = load_pins()["passes_for_prompt"]
+    for case in pins["cases"]:
+        passes, delivered, _ = run_prompt(pins["running"], pins["prompt"], case["budget"])
+        assert passes == case["passes"]
+        if "tokens_to_users" in case:
+            assert delivered == case["tokens_to_users"]
+    one = load_pins()["one_user"]
+    passes, delivered, _ = run_prompt(one["running"], one["prompt"], one["budget"])
+    assert passes == one["passes"] and delivered == one["tokens_to_users"]
+
+
+def test_pin_budget_floor():
+    pins = load_pins()["budget_floor"]
+    with pytest.raises(oracle.BudgetError):
+        oracle.schedule(users_and_prompt(pins["running"], 8192), pins["budget"])
+    # exactly enough budget for the decodes is allowed; the prompt gets nothing
+    sch = oracle.schedule(users_and_prompt(pins["running"], 8192), pins["running"])
+    assert sch["num_seqs"] == pins["running"]
+
+
+def test_pin_page2_step_table():
+    pins = load_pins()["page2_step_table"]
+    reqs = [oracle.Request(0, 500, 501, True), oracle.Request(1, 900, 901, True),
+            oracle.Request(2, 0, pins["prompt"], False)]
+    bounds = []
+    for step in range(len(pins["chunk_bounds"])):
+        sch = oracle.schedule(reqs, pins["budget"], pins["long_prefill_cap"])
+        if step == 0:
+            assert sch["num_scheduled"] == pins["scheduled_first_step"]
+            assert sch["num_tokens"] == pins["total"]
+            assert sch["query_start_loc"] == [0, 1, 2, 2050]
+        c = sch["context_lens"][-1]
+        bounds.append([c, c + sch["num_scheduled"][-1]])
+        reqs = oracle.advance(reqs, sch)
+    assert bounds == pins["chunk_bounds"]
+    assert reqs[2].is_decode  # the prompt decodes from the next step on
+    sch = oracle.schedule(reqs, pins["budget"], pins["long_prefill_cap"])
+    assert sch["num_scheduled"] == [1, 1, 1] and sch["num_decodes"] == 3
+
+
+def test_pin_page4_block_count():
+    pins = load_pins()["page4_blocks"]
+    sch = oracle.schedule([oracle.Request(0, 0, pins["tokens"], False)], 4096)
+    assert sch["new_blocks"] == [pins["blocks"]]
+    # a chunk that starts mid-page only needs the pages it newly reaches
+    sch = oracle.schedule([oracle.Request(0, 20, 100, False)], 30)
+    assert sch["new_blocks"] == [math.ceil(50 / 16) - math.ceil(20 / 16)]
+
+
+def test_schedule_several_prefills_fcfs_and_skip():
+    reqs = [oracle.Request(0, 0, 100, False), oracle.Request(1, 50, 50, False),
+            oracle.Request(2, 10, 30, True), oracle.Request(3, 0, 500, False),
+            oracle.Request(4, 0, 10, False)]
+    sch = oracle.schedule(reqs, 160, 0)
+    assert sch["order"] == [2, 0, 3]
+    assert sch["num_scheduled"] == [1, 100, 59]
+    assert sch["num_decodes"] == 1
+    sch = oracle.schedule(reqs, 160, 40)
+    assert sch["order"] == [2, 0, 3, 4]
+    assert sch["num_scheduled"] == [1, 40, 40, 10]
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin above
+# ---------------------------------------------------------------------------
+
+def _pins_pass():
+    try:
+        for args in [(4, 2, 8, 17, 5), (4, 1, 4, 0, 16), (1, 1, 8, 16, 2)]:
+            test_brute_force_dense(*args)
+        test_closed_form_zero_query_cumulative_mean(5)
+        test_decode_row_equals_last_prefill_row()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_pins_pass_unmutated():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("mutation", ["mask_off_by_one", "mask_strict", "head_map_modulo",
+                                      "v_read_as_k_layout", "drop_scale"])
+def test_planted_mistake_is_caught(monkeypatch, mutation):
+    if mutation == "mask_off_by_one":
+        monkeypatch.setattr(ostep, "_visible", lambda pos, c, js: pos[None, :] <= (c + js + 1)[:, None])
+    elif mutation == "mask_strict":
+        monkeypatch.setattr(ostep, "_visible",
+                            lambda pos, c, js: (pos[None, :] < (c + js)[:, None]) | (pos[None, :] == 0))
+    elif mutation == "head_map_modulo":
+        monkeypatch.setattr(ostep, "_kv_head", lambda h, G: h % 2 if G > 1 else h)
+    elif mutation == "v_read_as_k_layout":
+        orig = ostep._row_keys
+
+        def bad(k_pool, v_pool, bt_row, g, length):
+            Ks, Vs = orig(k_pool, v_pool, bt_row, g, length)
+            return Ks, Vs[::-1].copy()
+        monkeypatch.setattr(ostep, "_row_keys", bad)
+    elif mutation == "drop_scale":
+        orig_att = ostep.attention
+
+        def no_scale(*a, **k):
+            a = list(a)
+            a[7] = 1.0
+            return orig_att(*a, **k)
+        monkeypatch.setattr(oracle, "attention", no_scale)
+    assert not _pins_pass()
