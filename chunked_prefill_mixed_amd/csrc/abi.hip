@@ -1,0 +1,98 @@
+// C-ABI device entry points: argument checks, then kernel launches on the
+// caller's stream.  Declarations and contracts are in include/cpa.h.
+
+#include "../../include/cpa.h"
+#include "internal.h"
+#include "tiles.h"
+
+namespace {
+
+int check_heads(int num_q_heads, int num_kv_heads, int head_dim, int block_size) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return CPA_ERR_INVALID;
+  if (block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_group(num_q_heads / num_kv_heads)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_head_dim(head_dim)) return CPA_ERR_UNSUPPORTED;
+  return CPA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? CPA_OK : CPA_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" int cpa_append_kv(const void* k_new, const void* v_new, const int32_t* d_query_start_loc,
+                             const int32_t* d_context_lens, const int32_t* d_block_table,
+                             int bt_stride, int num_seqs, int num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, void* k_cache, void* v_cache,
+                             void* stream) {
+  if (head_dim <= 0 || num_kv_heads <= 0) return CPA_ERR_INVALID;
+  if (block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_head_dim(head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_seqs < 0 || bt_stride <= 0) return CPA_ERR_INVALID;
+  if (num_tokens == 0) return CPA_OK;
+  if (num_seqs == 0 || !k_new || !v_new || !d_query_start_loc || !d_context_lens ||
+      !d_block_table || !k_cache || !v_cache)
+    return CPA_ERR_INVALID;
+  return status_of(cpa::launch_append(k_new, v_new, d_query_start_loc, d_context_lens,
+                                      d_block_table, bt_stride, num_seqs, num_tokens, num_kv_heads,
+                                      head_dim, k_cache, v_cache, (hipStream_t)stream));
+}
+
+extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* d_block_table, int bt_stride,
+                             const int32_t* d_query_start_loc, const int32_t* d_seq_lens,
+                             const int32_t* d_context_lens, const int32_t* d_plan,
+                             const cpa_plan_counts_t* counts, int num_seqs, int num_decodes,
+                             int num_tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  (void)d_seq_lens;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != CPA_OK) return st;
+  if (!counts || num_seqs < 0 || num_decodes < 0 || num_decodes > num_seqs || num_tokens < 0 ||
+      bt_stride <= 0)
+    return CPA_ERR_INVALID;
+  const cpa_plan_counts_t& n = *counts;
+  if (n.num_decode_splits < 0 || n.num_decode_merges < 0 || n.num_chunk_tiles < 0 ||
+      n.num_partials < 0)
+    return CPA_ERR_INVALID;
+  if (num_tokens == 0) return CPA_OK;
+  if (!q || !k_cache || !v_cache || !d_block_table || !d_query_start_loc || !d_context_lens ||
+      !d_plan || !out)
+    return CPA_ERR_INVALID;
+  if (!(softmax_scale > 0.f)) return CPA_ERR_INVALID;
+  const size_t need = cpa_workspace_size(counts, num_q_heads, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CPA_ERR_CAPACITY;
+
+  hipStream_t s = (hipStream_t)stream;
+  const float sl2 = softmax_scale * 1.4426950408889634f;
+  cpa::Partials ws{nullptr, nullptr, nullptr};
+  if (n.num_partials > 0) {
+    float* base = static_cast<float*>(workspace);
+    ws.acc = base;
+    ws.m = base + (size_t)n.num_partials * num_q_heads * head_dim;
+    ws.l = ws.m + (size_t)n.num_partials * num_q_heads;
+  }
+  const int32_t* splits = d_plan;
+  const int32_t* merges = splits + (size_t)n.num_decode_splits * CPA_DECODE_SPLIT_WORDS;
+  const int32_t* tiles = merges + (size_t)n.num_decode_merges * CPA_DECODE_MERGE_WORDS;
+
+  if (n.num_decode_splits > 0) {
+    st = status_of(cpa::launch_decode(q, k_cache, v_cache, d_block_table, bt_stride,
+                                      d_query_start_loc, splits, n.num_decode_splits, num_q_heads,
+                                      num_kv_heads, head_dim, sl2, out, lse, ws, s));
+    if (st != CPA_OK) return st;
+  }
+  if (n.num_decode_merges > 0) {
+    st = status_of(cpa::launch_merge(merges, n.num_decode_merges, d_query_start_loc, num_q_heads,
+                                     head_dim, ws, out, lse, s));
+    if (st != CPA_OK) return st;
+  }
+  if (n.num_chunk_tiles > 0) {
+    st = status_of(cpa::launch_chunk(q, k_cache, v_cache, d_block_table, bt_stride,
+                                     d_query_start_loc, d_context_lens, tiles, n.num_chunk_tiles,
+                                     num_q_heads, num_kv_heads, head_dim, sl2, out, lse, s));
+    if (st != CPA_OK) return st;
+  }
+  return CPA_OK;
+}

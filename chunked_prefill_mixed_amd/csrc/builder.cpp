@@ -1,0 +1,222 @@
+// Host-side decode-first budget split and device work plan (cpa_build_metadata).
+//
+// Budget split: every running decode takes one token, the rest of the budget
+// goes to prefills in queue order and a prompt that does not fit is cut to
+// what remains ("Chunked Prefill" (deepconcepts.dev), "Why a chunk can be
+// nearly free"; "05. Chunked Prefill" section 5; tbr8.org deep dive 3.1;
+// "How Chunked Prefill Stops Decode Starvation", "The fix").  A budget below
+// the number of decodes is rejected ("Chunked Prefill", "The budget points in
+// two directions").
+//
+// Work plan: decode rows are cut into key splits of a fixed page-aligned size
+// so lognormal context lengths balance over the GPU; rows with several splits
+// get a log-sum-exp merge entry.  Chunk rows are cut into query tiles of
+// kChunkRows/(Hq/Hkv) tokens, ordered longest key range first.
+//
+// Pure host code: no HIP call, safe to run on a machine without a GPU.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/cpa.h"
+#include "tiles.h"
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_params(const cpa_build_params_t* p) {
+  if (!p) return CPA_ERR_INVALID;
+  if (p->token_budget <= 0 || p->long_prefill_cap < 0 || p->reserved != 0) return CPA_ERR_INVALID;
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0) return CPA_ERR_INVALID;
+  if (p->decode_split_tokens < 0) return CPA_ERR_INVALID;
+  if (p->block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
+  if (p->num_q_heads % p->num_kv_heads) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_group(p->num_q_heads / p->num_kv_heads)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_head_dim(p->head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (p->decode_split_tokens % cpa::kBlock) return CPA_ERR_INVALID;
+  return CPA_OK;
+}
+
+// Keys per decode split: enough splits that about kDecodeWavesTarget waves
+// (split x KV head) cover the decode rows, each split a whole number of pages.
+int pick_split(int64_t decode_keys, int num_kv_heads) {
+  int64_t splits = std::max<int64_t>(1, cpa::kDecodeWavesTarget / num_kv_heads);
+  int64_t per = ceil_div(std::max<int64_t>(decode_keys, 1), splits);
+  per = ceil_div(per, cpa::kBlock) * cpa::kBlock;
+  return (int)std::min<int64_t>(std::max<int64_t>(per, 128), 4096);
+}
+
+}  // namespace
+
+extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_build_params_t* params,
+                                  const int32_t* bt, int bt_stride, int num_blocks, cpa_meta_t* out) {
+  int st = check_params(params);
+  if (st != CPA_OK) return st;
+  if (!out || n_reqs < 0 || (n_reqs > 0 && !reqs)) return CPA_ERR_INVALID;
+  if (bt && (bt_stride <= 0 || num_blocks <= 0)) return CPA_ERR_INVALID;
+
+  const int budget = params->token_budget;
+  const int cap = params->long_prefill_cap;
+  const int group = params->num_q_heads / params->num_kv_heads;
+
+  // validate requests; positions must stay addressable as int32 slot indices
+  int n_dec = 0;
+  for (int i = 0; i < n_reqs; ++i) {
+    const cpa_req_t& r = reqs[i];
+    if (r.num_computed < 0) return CPA_ERR_INVALID;
+    if (!r.is_decode && r.target_len < r.num_computed) return CPA_ERR_INVALID;
+    if (r.num_computed > (INT32_MAX - budget)) return CPA_ERR_INVALID;
+    n_dec += r.is_decode ? 1 : 0;
+  }
+  if (n_dec > budget) return CPA_ERR_BUDGET;
+
+  // decode-first split of the budget
+  std::vector<int32_t> order, nsched;
+  order.reserve(n_reqs);
+  nsched.reserve(n_reqs);
+  for (int i = 0; i < n_reqs; ++i)
+    if (reqs[i].is_decode) {
+      order.push_back(i);
+      nsched.push_back(1);
+    }
+  int remaining = budget - n_dec;
+  for (int i = 0; i < n_reqs && remaining > 0; ++i) {
+    const cpa_req_t& r = reqs[i];
+    if (r.is_decode) continue;
+    int want = r.target_len - r.num_computed;
+    if (cap) want = std::min(want, cap);
+    int n = std::min(want, remaining);
+    if (n > 0) {
+      order.push_back(i);
+      nsched.push_back(n);
+      remaining -= n;
+    }
+  }
+
+  const int nseq = (int)order.size();
+  if (nseq > out->max_seqs) return CPA_ERR_CAPACITY;
+  if (!out->order || !out->num_scheduled || !out->query_start_loc || !out->seq_lens ||
+      !out->context_lens)
+    return CPA_ERR_INVALID;
+
+  int32_t qsl = 0;
+  int64_t decode_keys = 0;
+  out->query_start_loc[0] = 0;
+  for (int s = 0; s < nseq; ++s) {
+    const cpa_req_t& r = reqs[order[s]];
+    out->order[s] = order[s];
+    out->num_scheduled[s] = nsched[s];
+    out->context_lens[s] = r.num_computed;
+    out->seq_lens[s] = r.num_computed + nsched[s];
+    if (out->new_blocks)
+      out->new_blocks[s] = (int32_t)(ceil_div(out->seq_lens[s], cpa::kBlock) -
+                                     ceil_div(r.num_computed, cpa::kBlock));
+    qsl += nsched[s];
+    out->query_start_loc[s + 1] = qsl;
+    if (s < n_dec) decode_keys += out->seq_lens[s];
+  }
+  out->num_seqs = nseq;
+  out->num_decodes = n_dec;
+  out->num_tokens = qsl;
+
+  // optional host block-table checks and slot mapping
+  if (bt) {
+    if (out->slot_mapping && out->max_tokens < qsl) return CPA_ERR_CAPACITY;
+    std::vector<int64_t> fresh, cached;
+    fresh.reserve(qsl);
+    for (int s = 0; s < nseq; ++s) {
+      const int32_t* row = bt + (int64_t)order[s] * bt_stride;
+      const int c = out->context_lens[s], L = out->seq_lens[s];
+      const int64_t pages = ceil_div(L, cpa::kBlock);
+      if (pages > bt_stride) return CPA_ERR_INVALID;
+      for (int64_t pg = 0; pg < pages; ++pg)
+        if (row[pg] < 0 || row[pg] >= num_blocks) return CPA_ERR_INVALID;
+      for (int p = 0; p < L; ++p) {
+        int64_t slot = (int64_t)row[p / cpa::kBlock] * cpa::kBlock + p % cpa::kBlock;
+        if (p >= c) {
+          if (out->slot_mapping) out->slot_mapping[out->query_start_loc[s] + (p - c)] = slot;
+          fresh.push_back(slot);
+        } else {
+          cached.push_back(slot);
+        }
+      }
+    }
+    std::sort(fresh.begin(), fresh.end());
+    if (std::adjacent_find(fresh.begin(), fresh.end()) != fresh.end()) return CPA_ERR_INVALID;
+    // a fresh slot that another row reads as cached context would race with it
+    std::sort(cached.begin(), cached.end());
+    size_t a = 0, b = 0;
+    while (a < fresh.size() && b < cached.size()) {
+      if (fresh[a] == cached[b]) return CPA_ERR_INVALID;
+      if (fresh[a] < cached[b]) ++a; else ++b;
+    }
+  }
+
+  // ---- work plan --------------------------------------------------------
+  const int split = params->decode_split_tokens ? params->decode_split_tokens
+                                                : pick_split(decode_keys, params->num_kv_heads);
+  std::vector<int32_t> dsplits, dmerges, tiles;
+  int partials = 0;
+  for (int s = 0; s < n_dec; ++s) {
+    const int L = out->seq_lens[s];
+    const int pieces = (int)ceil_div(L, split);
+    if (pieces == 1) {
+      dsplits.insert(dsplits.end(), {s, 0, L, -1});
+      continue;
+    }
+    dmerges.insert(dmerges.end(), {s, partials, pieces, 0});
+    for (int k = 0; k < pieces; ++k)
+      dsplits.insert(dsplits.end(), {s, k * split, std::min(L, (k + 1) * split), partials + k});
+    partials += pieces;
+  }
+  const int tile_tokens = cpa::chunk_tile_tokens(group);
+  struct Tile { int32_t row, qb, qe; int64_t keys; };
+  std::vector<Tile> tl;
+  for (int s = n_dec; s < nseq; ++s) {
+    const int n = out->num_scheduled[s];
+    for (int qb = 0; qb < n; qb += tile_tokens) {
+      const int qe = std::min(n, qb + tile_tokens);
+      tl.push_back({s, qb, qe, (int64_t)out->context_lens[s] + qe});
+    }
+  }
+  std::stable_sort(tl.begin(), tl.end(), [](const Tile& x, const Tile& y) { return x.keys > y.keys; });
+  for (const Tile& t : tl) tiles.insert(tiles.end(), {t.row, t.qb, t.qe, 0});
+
+  out->counts.num_decode_splits = (int32_t)(dsplits.size() / CPA_DECODE_SPLIT_WORDS);
+  out->counts.num_decode_merges = (int32_t)(dmerges.size() / CPA_DECODE_MERGE_WORDS);
+  out->counts.num_chunk_tiles = (int32_t)(tiles.size() / CPA_CHUNK_TILE_WORDS);
+  out->counts.num_partials = partials;
+  const int64_t words = (int64_t)dsplits.size() + dmerges.size() + tiles.size();
+  out->plan_words = (int32_t)words;
+  if (out->plan) {
+    if (words > out->plan_capacity) return CPA_ERR_CAPACITY;
+    int32_t* w = out->plan;
+    std::memcpy(w, dsplits.data(), dsplits.size() * sizeof(int32_t));
+    w += dsplits.size();
+    std::memcpy(w, dmerges.data(), dmerges.size() * sizeof(int32_t));
+    w += dmerges.size();
+    std::memcpy(w, tiles.data(), tiles.size() * sizeof(int32_t));
+  }
+  return CPA_OK;
+}
+
+extern "C" size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int head_dim) {
+  if (!counts || counts->num_partials <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  size_t bytes = (size_t)counts->num_partials * (size_t)num_q_heads * (size_t)(head_dim + 2) * 4u;
+  return (bytes + 255) / 256 * 256;
+}
+
+extern "C" const char* cpa_status_string(int status) {
+  switch (status) {
+    case CPA_OK: return "CPA_OK";
+    case CPA_ERR_INVALID: return "CPA_ERR_INVALID: malformed input";
+    case CPA_ERR_BUDGET: return "CPA_ERR_BUDGET: more running decodes than budget tokens";
+    case CPA_ERR_CAPACITY: return "CPA_ERR_CAPACITY: output array or workspace too small";
+    case CPA_ERR_UNSUPPORTED: return "CPA_ERR_UNSUPPORTED: shape not supported";
+    case CPA_ERR_DEVICE: return "CPA_ERR_DEVICE: kernel launch failed";
+    default: return "unknown cpa status";
+  }
+}

@@ -1,0 +1,80 @@
+// Device helpers for the gfx950 kernels: bf16 packing, dot products, DPP
+// lane exchanges and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (lowers to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// acc + sum_i a_i * b_i over 8 bf16 pairs held in 4 dwords, fp32 accumulate
+// (v_dot2_f32_bf16: two products per instruction).
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                        __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                        __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                        __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                        __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+
+// DPP lane exchanges inside a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowMirror = 0x140;     // lane i <-> 15-i inside a row
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+  return __shfl_xor(x, mask, 64);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  x += xor_lane(x, 16);
+  x += xor_lane(x, 32);
+  return x;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by linear id.  Remap so
+// each XCD runs one contiguous range of work items: items that share K/V
+// (same KV head of one row) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b & 7, i = b >> 3;
+  const int base = n >> 3, rem = n & 7;
+  return x * base + (x < rem ? x : rem) + i;
+}
+
+}  // namespace cpa

@@ -1,0 +1,36 @@
+// Launchers shared between the kernel files and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpa {
+
+hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* qsl,
+                         const int32_t* ctx, const int32_t* bt, int bt_stride, int num_seqs,
+                         int num_tokens, int num_kv_heads, int head_dim, void* k_cache,
+                         void* v_cache, hipStream_t stream);
+
+// Workspace of fp32 partial results: acc [P][Hq][D], then m [P][Hq] (log2
+// units of the scaled score), then l [P][Hq].
+struct Partials {
+  float* acc;
+  float* m;
+  float* l;
+};
+
+hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* bt, int bt_stride, const int32_t* qsl,
+                         const int32_t* splits, int num_splits, int num_q_heads, int num_kv_heads,
+                         int head_dim, float scale_log2, void* out, float* lse, Partials ws,
+                         hipStream_t stream);
+
+hipError_t launch_merge(const int32_t* merges, int num_merges, const int32_t* qsl, int num_q_heads,
+                        int head_dim, Partials ws, void* out, float* lse, hipStream_t stream);
+
+hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
+                        int bt_stride, const int32_t* qsl, const int32_t* ctx,
+                        const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
+                        int head_dim, float scale_log2, void* out, float* lse, hipStream_t stream);
+
+}  // namespace cpa

@@ -1,0 +1,89 @@
+"""Device buffers for one mixed step and the two launches that run it.
+
+Holds a workload's tensors in HBM (torch allocations), the step metadata
+from ``cpa_build_metadata`` and the work plan, and calls ``cpa_append_kv``
+then ``cpa_attention`` on the current stream.  No arithmetic of the step is
+done here.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import cpa
+
+
+def _bits_to_bf16(a, device):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def bf16_to_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+class DeviceStep:
+    """One step of a workload, resident on the GPU."""
+
+    def __init__(self, w, device="cuda", decode_split_tokens=0, validate=True, with_lse=True):
+        import torch
+        self.w = w
+        self.device = device
+        self.meta = cpa.cpa_build_metadata(
+            w.requests, token_budget=w.token_budget, long_prefill_cap=w.long_prefill_cap,
+            num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+            decode_split_tokens=decode_split_tokens,
+            host_block_table=w.block_table if validate else None, num_blocks=w.num_blocks)
+        m = self.meta
+        self.num_tokens = T = m["num_tokens"]
+        self.num_seqs = m["num_seqs"]
+        self.num_decodes = m["num_decodes"]
+        self.counts = m["counts"]
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        bt_rows = w.block_table[m["order"]] if self.num_seqs else w.block_table[:1]
+        self.block_table = i32(bt_rows)
+        self.query_start_loc = i32(m["query_start_loc"])
+        self.seq_lens = i32(m["seq_lens"])
+        self.context_lens = i32(m["context_lens"])
+        plan = m["plan"] if m["plan"].size else np.zeros(1, dtype=np.int32)
+        self.plan = i32(plan)
+        self.k_cache = _bits_to_bf16(w.k_pool, device)
+        self.v_cache = _bits_to_bf16(w.v_pool, device)
+        self.q = _bits_to_bf16(w.q[:T], device)
+        self.k_new = _bits_to_bf16(w.k_new[:T], device)
+        self.v_new = _bits_to_bf16(w.v_new[:T], device)
+        self.out = torch.empty((T, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=device)
+        self.lse = (torch.empty((T, w.num_q_heads), dtype=torch.float32, device=device)
+                    if with_lse else None)
+        ws = cpa.cpa_workspace_size(self.counts, w.num_q_heads, w.head_dim)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device) if ws else None
+        self.scale = w.scale
+
+    def append(self, stream=None):
+        cpa.cpa_append_kv(self.k_new, self.v_new, self.query_start_loc, self.context_lens,
+                          self.block_table, self.k_cache, self.v_cache, num_seqs=self.num_seqs,
+                          num_tokens=self.num_tokens, stream=stream)
+
+    def attention(self, stream=None):
+        cpa.cpa_attention(self.q, self.k_cache, self.v_cache, self.block_table,
+                          self.query_start_loc, self.seq_lens, self.context_lens, self.plan,
+                          self.counts, num_seqs=self.num_seqs, num_decodes=self.num_decodes,
+                          num_tokens=self.num_tokens, softmax_scale=self.scale, out=self.out,
+                          lse=self.lse, workspace=self.workspace, stream=stream)
+
+    def run(self, stream=None):
+        self.append(stream)
+        self.attention(stream)
+
+    # host copies for checking
+    def pools_bits(self):
+        return bf16_to_bits(self.k_cache), bf16_to_bits(self.v_cache)
+
+    def out_f64(self):
+        import torch
+        return self.out.detach().float().cpu().numpy().astype(np.float64)
+
+    def lse_f64(self):
+        return None if self.lse is None else self.lse.detach().cpu().numpy().astype(np.float64)

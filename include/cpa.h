@@ -1,0 +1,225 @@
+/*
+ * cpa.h -- C ABI of the chunked-prefill mixed-batch attention library (libcpa.so)
+ *
+ * One continuous-batching step packs decode rows (one query each) and prefill
+ * chunks (C query tokens each) into a single token batch.  Each chunk token
+ * attends to every earlier chunk's K/V already in the paged cache plus a
+ * causal mask inside its own chunk; the step's own K/V is appended first.
+ *
+ * Sources, by page title and section:
+ *   [P1] "Chunked Prefill" (deepconcepts.dev): the token budget; decodes take
+ *        one token each and the prompt gets the rest ("Why a chunk can be nearly
+ *        free"); a budget below the running count can never finish a prompt
+ *        ("The budget points in two directions").
+ *   [P2] "05. Chunked Prefill" (vLLM learning book): section 3, a chunk's
+ *        queries see all cached earlier chunks plus a causal mask inside the
+ *        chunk; section 4, all rows are packed into one 1-D token tensor told
+ *        apart by query_start_loc / seq_lens; section 5, decode-first hybrid
+ *        split of the budget; section 8, attention reads the cache including
+ *        the K/V the current chunk just wrote.
+ *   [P4] tbr8.org chunked-prefill deep dive: 3.1, decode tokens first and the
+ *        remaining budget to prefill; 3.3, a chunk carries the length of the
+ *        prefix already cached; 4.1, a chunk never sees later chunks; 4.2,
+ *        16-token KV pages and per-chunk page allocation.
+ *   [P5] "How Chunked Prefill Stops Decode Starvation": "The fix", a prefill
+ *        that does not fit the remaining budget is chunked.
+ *
+ * Conventions shared by every call
+ *   - All sizes are int32 unless stated.  bf16 tensors are passed as void*
+ *     holding IEEE bfloat16 bit patterns.
+ *   - Every buffer is allocated and owned by the caller.  The library
+ *     allocates no memory, keeps no pointer after a call returns and has no
+ *     global mutable state; calls are re-entrant.
+ *   - Device calls are asynchronous on the given HIP stream and are ordered
+ *     only by that stream.  Device-side integer inputs are trusted: validation
+ *     happens on the host in cpa_build_metadata.
+ *   - Status: CPA_OK (0) or a negative CPA_ERR_*; the library never aborts and
+ *     never throws across the ABI.  CPA_ERR_DEVICE carries a launch failure
+ *     reported by hipGetLastError.
+ *   - Supported shapes: head_dim in {64, 128}; num_q_heads / num_kv_heads in
+ *     {1, 2, 4, 8}; block_size 16; bf16 only.
+ *
+ * KV cache layout (one tensor each for K and V; the same page id in both)
+ *   k_cache [num_blocks][num_kv_heads][16][head_dim]   token-major in a page
+ *   v_cache [num_blocks][num_kv_heads][head_dim][16]   transposed in a page
+ *   Position p of a row lives in page block_table[row][p / 16], slot p % 16.
+ *
+ * Packed tensors
+ *   q     [num_tokens][num_q_heads][head_dim]   bf16
+ *   k_new [num_tokens][num_kv_heads][head_dim]  bf16
+ *   v_new [num_tokens][num_kv_heads][head_dim]  bf16
+ *   out   [num_tokens][num_q_heads][head_dim]   bf16
+ *   lse   [num_tokens][num_q_heads]             fp32, natural log (optional)
+ *   Row s owns packed tokens [query_start_loc[s], query_start_loc[s+1]).
+ *   Rows [0, num_decodes) are decode rows (one token each); the rest are
+ *   prefill chunks.  Query head h reads KV head h / (num_q_heads/num_kv_heads).
+ */
+#ifndef CPA_H
+#define CPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPA_OK 0
+#define CPA_ERR_INVALID (-1)     /* malformed input (lengths, ordering, block ids, slots) */
+#define CPA_ERR_BUDGET (-2)      /* more running decodes than budget tokens [P1] */
+#define CPA_ERR_CAPACITY (-3)    /* a caller-provided array or workspace is too small */
+#define CPA_ERR_UNSUPPORTED (-4) /* head_dim, head ratio or block size not supported */
+#define CPA_ERR_DEVICE (-5)      /* a kernel launch failed */
+
+#define CPA_BLOCK_SIZE 16
+
+/* Plan entry sizes in int32 words (see cpa_plan_counts_t). */
+#define CPA_DECODE_SPLIT_WORDS 4 /* {row, kv_begin, kv_end, partial slot or -1} */
+#define CPA_DECODE_MERGE_WORDS 4 /* {row, first partial slot, num partials, 0} */
+#define CPA_CHUNK_TILE_WORDS 4   /* {row, q_begin, q_end, 0}  (q_* are chunk-local) */
+
+/* One queued request, in queue order: running decodes, then prefills first
+ * come first served (a continued chunked prompt precedes newer prompts). */
+typedef struct {
+  int32_t id;           /* caller's tag; copied nowhere, for the caller's use */
+  int32_t num_computed; /* tokens already in the KV cache ([P4] 3.3 cached_prefix_len) */
+  int32_t target_len;   /* prompt length of a prefill; ignored for a decode */
+  int32_t is_decode;    /* nonzero: wants exactly one token this step */
+} cpa_req_t;
+
+typedef struct {
+  int32_t token_budget;        /* max tokens this step, decodes included [P1][P2 5] */
+  int32_t long_prefill_cap;    /* per-request cap on a prefill's share, 0 = none
+                                  ([P1] "Checking it on a real system") */
+  int32_t block_size;          /* must be 16 [P4 4.2] */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t decode_split_tokens; /* keys per decode split, multiple of 16; 0 = chosen by size */
+  int32_t reserved;            /* must be 0 */
+} cpa_build_params_t;
+
+/* Counts of the device work plan built by cpa_build_metadata.  The plan is one
+ * int32 array: num_decode_splits entries of CPA_DECODE_SPLIT_WORDS, then
+ * num_decode_merges entries of CPA_DECODE_MERGE_WORDS, then num_chunk_tiles
+ * entries of CPA_CHUNK_TILE_WORDS. */
+typedef struct {
+  int32_t num_decode_splits; /* one wave per (split, KV head) */
+  int32_t num_decode_merges; /* decode rows whose keys were split in several pieces */
+  int32_t num_chunk_tiles;   /* one workgroup per (tile, KV head) */
+  int32_t num_partials;      /* fp32 partial-result slots needed in the workspace */
+} cpa_plan_counts_t;
+
+/* Host arrays filled by cpa_build_metadata; the caller provides them with the
+ * stated capacities.  Unused optional outputs may be NULL. */
+typedef struct {
+  int32_t max_seqs;         /* capacity of the per-row arrays */
+  int32_t* order;           /* [max_seqs]  request index (into reqs) of each row */
+  int32_t* num_scheduled;   /* [max_seqs]  tokens of each row this step */
+  int32_t* query_start_loc; /* [max_seqs+1] prefix sums of num_scheduled */
+  int32_t* seq_lens;        /* [max_seqs]  context_len + num_scheduled */
+  int32_t* context_lens;    /* [max_seqs]  tokens cached before this step */
+  int32_t* new_blocks;      /* [max_seqs]  pages the row newly reaches (nullable) */
+  int32_t max_tokens;       /* capacity of slot_mapping */
+  int64_t* slot_mapping;    /* [max_tokens] page*16+slot per packed token (nullable;
+                               needs a host block table) */
+  int32_t plan_capacity;    /* capacity of plan in int32 words */
+  int32_t* plan;            /* [plan_capacity] device work plan (nullable: then only
+                               the counts are produced) */
+  /* outputs */
+  int32_t num_seqs;
+  int32_t num_decodes;
+  int32_t num_tokens;
+  int32_t plan_words;       /* int32 words written to plan */
+  cpa_plan_counts_t counts;
+} cpa_meta_t;
+
+/*
+ * cpa_build_metadata -- host-side decode-first budget split and work plan.
+ *
+ * Every decode request gets one token; the remaining budget goes to prefill
+ * requests in queue order, each taking min(remaining prompt, long_prefill_cap,
+ * remaining budget) tokens, so a prompt that does not fit is chunked
+ * ([P1] second section: budget 512 with 32 users gives 480-token chunks;
+ * [P2] section 5; [P4] 3.1; [P5] "The fix").  Rows are emitted decodes first
+ * (queue order) then prefills (queue order); a request given no token is left
+ * out.  new_blocks = ceil(seq_len/16) - ceil(context_len/16) ([P4] 4.2, for
+ * chunks that start mid-page too).
+ *
+ * If host_block_table is given ([n_reqs][bt_stride] int32, rows indexed by
+ * request, not by output row) the call also checks that every row's pages
+ * cover seq_len, that ids are in [0, num_blocks), that no two scheduled tokens
+ * share a slot, and fills slot_mapping.
+ *
+ * Synchronous, pure, host only (no HIP call).  Returns CPA_OK,
+ * CPA_ERR_BUDGET (decodes > token_budget), CPA_ERR_INVALID (negative lengths,
+ * target_len < num_computed, bad block ids, duplicate slots, nonzero
+ * reserved), CPA_ERR_CAPACITY (an output array too small) or
+ * CPA_ERR_UNSUPPORTED (shape outside the supported set).  On error the
+ * outputs are unspecified.
+ */
+int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_build_params_t* params,
+                       const int32_t* host_block_table, int bt_stride, int num_blocks,
+                       cpa_meta_t* out);
+
+/*
+ * cpa_append_kv -- write the step's K/V into the paged cache ([P2] section 8:
+ * the chunk's own K/V is in the cache when attention runs; [P4] 4.2).
+ *
+ * For packed token t of row s at position p = context_lens[s] + t -
+ * query_start_loc[s]:  k_cache page block_table[s][p/16], slot p%16 <- k_new[t]
+ * and the same for V (transposed layout).  Exactly num_tokens*num_kv_heads
+ * slots of each cache are written; nothing else is touched.  Enqueue it
+ * before cpa_attention of the same step on the same stream.
+ *
+ * d_* pointers are device int32 arrays: query_start_loc [num_seqs+1],
+ * context_lens [num_seqs], block_table [num_seqs][bt_stride] (rows in output
+ * row order).  Returns CPA_OK, CPA_ERR_UNSUPPORTED, CPA_ERR_INVALID (negative
+ * sizes) or CPA_ERR_DEVICE.
+ */
+int cpa_append_kv(const void* k_new, const void* v_new, const int32_t* d_query_start_loc,
+                  const int32_t* d_context_lens, const int32_t* d_block_table, int bt_stride,
+                  int num_seqs, int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                  void* k_cache, void* v_cache, void* stream);
+
+/*
+ * cpa_workspace_size -- bytes of device workspace cpa_attention needs for a
+ * plan with these counts: num_partials * num_q_heads * (head_dim + 2) * 4
+ * (fp32 partial sums plus running max and sum per head), rounded up to 256.
+ */
+size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int head_dim);
+
+/*
+ * cpa_attention -- attention of every packed query over the paged cache.
+ *
+ * Query j of row s (position context_lens[s] + j) attends to keys
+ * k <= context_lens[s] + j of its row: all earlier chunks plus causal inside
+ * its own chunk ([P2] section 3; [P4] 4.1; [P5] "The fix").  Decode rows are
+ * the one-query case.  out[t][h] = sum_k softmax(scale * <q[t][h], K[k]>) V[k]
+ * with bf16 inputs, fp32 accumulation and a bf16 result (round to nearest
+ * even); lse[t][h] = log(sum_k exp(scale * <q, K[k]>)) if lse is non-NULL.
+ *
+ * d_plan is the plan from cpa_build_metadata copied to the device, with its
+ * counts in *counts (host pointer).  workspace must hold
+ * cpa_workspace_size(counts, ...) bytes (may be NULL when num_partials is 0).
+ * The append of this step must already be enqueued on the same stream.
+ * seq_lens is read for validation of the plan only on the host side and may
+ * be NULL.  Returns CPA_OK, CPA_ERR_UNSUPPORTED, CPA_ERR_CAPACITY (workspace
+ * too small), CPA_ERR_INVALID or CPA_ERR_DEVICE.
+ */
+int cpa_attention(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* d_block_table, int bt_stride, const int32_t* d_query_start_loc,
+                  const int32_t* d_seq_lens, const int32_t* d_context_lens, const int32_t* d_plan,
+                  const cpa_plan_counts_t* counts, int num_seqs, int num_decodes, int num_tokens,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  float softmax_scale, void* out, float* lse, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* cpa_status_string -- static, human-readable name of a status code. */
+const char* cpa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPA_H */

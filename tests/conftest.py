@@ -15,5 +15,7 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def lib():
     """The built C-ABI library (host-only calls are safe without a GPU)."""
-    from chunked_prefill_mixed_amd import cpa
+    from chunked_prefill_mixed_amd import build_lib, cpa
+    if not __import__("os").path.exists(cpa.LIB_PATH):
+        build_lib.build()
     return cpa.load()

@@ -1,0 +1,233 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bar: the whole KV pool bit-identical to the oracle's after the append (it
+starts from a sentinel-filled pool, so a stray write shows up); attention
+outputs within max |err| <= 2e-2 of the fp64 oracle (bf16 inputs, fp32
+accumulation, bf16 output); lse within 1e-2.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_prefill_mixed_amd import cpa, workloads
+from chunked_prefill_mixed_amd.step import DeviceStep
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+LSE_TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(lib):
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+
+
+def oracle_step(w, meta, tokens=None):
+    """Oracle append + attention for the step the builder scheduled."""
+    bt = w.block_table[meta["order"]]
+    T = meta["num_tokens"]
+    kp, vp = oracle.append(w.k_pool, w.v_pool, w.k_new[:T], w.v_new[:T], meta["query_start_loc"],
+                           meta["context_lens"], bt)
+    out, lse = oracle.attention(w.q[:T], kp, vp, meta["query_start_loc"], meta["context_lens"], bt,
+                                w.num_kv_heads, w.scale, tokens=tokens)
+    return kp, vp, out, lse
+
+
+def sample_tokens(meta, rng, per_chunk=48):
+    """All decode tokens plus, per chunk row, its first and last 16 tokens and
+    random ones in between."""
+    qsl, nd = meta["query_start_loc"], meta["num_decodes"]
+    toks = list(range(qsl[nd]))
+    for s in range(nd, meta["num_seqs"]):
+        a, b = qsl[s], qsl[s + 1]
+        toks += list(range(a, min(b, a + 16))) + list(range(max(a, b - 16), b))
+        if b - a > 32:
+            toks += list(rng.choice(np.arange(a + 16, b - 16), size=min(per_chunk, b - a - 32),
+                                    replace=False))
+    return np.unique(np.asarray(toks, dtype=np.int64))
+
+
+def check_step(w, decode_split_tokens=0, tokens=None, label=""):
+    import torch
+    ds = DeviceStep(w, decode_split_tokens=decode_split_tokens)
+    ds.run()
+    torch.cuda.synchronize()
+    kp, vp, out, lse = oracle_step(w, ds.meta, tokens)
+    gk, gv = ds.pools_bits()
+    assert np.array_equal(gk, kp), f"{label}: K pool differs at {np.argwhere(gk != kp)[:5]}"
+    assert np.array_equal(gv, vp), f"{label}: V pool differs at {np.argwhere(gv != vp)[:5]}"
+    got = ds.out_f64()
+    sel = np.arange(ds.num_tokens) if tokens is None else np.asarray(tokens)
+    err = np.max(np.abs(got[sel] - out[sel])) if sel.size else 0.0
+    assert np.isfinite(got[sel]).all(), label
+    assert err <= OUT_TOL, f"{label}: max |err| {err}"
+    lerr = np.max(np.abs(ds.lse_f64()[sel] - lse[sel])) if sel.size else 0.0
+    assert lerr <= LSE_TOL, f"{label}: lse err {lerr}"
+    return ds, err
+
+
+def test_tiny_four_steps_carry_the_pool():
+    """Config 1: a 256-token prompt in 4 chunks of 64 beside 4 decode rows;
+    the pool is carried from step to step on both sides."""
+    import torch
+    run = workloads.tiny_run()
+    kp, vp = run.k_pool, run.v_pool
+    gk, gv = kp, vp
+    for step in range(4):
+        w = run.step_workload(step, gk, gv)
+        ds = DeviceStep(w)
+        assert ds.num_tokens == 68 and ds.num_decodes == 4
+        ds.run()
+        torch.cuda.synchronize()
+        wo = run.step_workload(step, kp, vp)
+        kp, vp, out, lse = oracle_step(wo, ds.meta)
+        gk, gv = ds.pools_bits()
+        assert np.array_equal(gk, kp) and np.array_equal(gv, vp), step
+        assert np.max(np.abs(ds.out_f64() - out)) <= OUT_TOL, step
+        assert np.max(np.abs(ds.lse_f64() - lse)) <= LSE_TOL, step
+
+
+SMALL = [
+    # (Hq, Hkv, D, decode contexts, chunks as (num_computed, prompt_len), split)
+    (4, 4, 64, [0, 1, 15, 16, 17, 250], [(0, 64), (64, 128)], 0),
+    (8, 4, 64, [3, 200], [(17, 17 + 33), (0, 1), (5, 6)], 16),
+    (16, 4, 128, [1000, 31, 77], [(100, 230), (0, 129)], 64),
+    (32, 8, 128, [500, 1, 2048], [(1000, 1130), (3, 70)], 0),
+    (32, 4, 128, [0, 300], [(511, 600), (0, 17)], 32),
+    (8, 8, 128, [100, 64, 65], [(0, 200), (48, 49)], 16),
+    (16, 2, 64, [40, 4000], [(2000, 2100)], 0),
+    (8, 1, 128, [7, 129], [(70, 110)], 48),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_mixed_steps(case):
+    Hq, Hkv, D, dec, chunks, split = SMALL[case]
+    w = workloads.random_workload(500 + case, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  decode_ctx=dec, chunks=chunks)
+    check_step(w, decode_split_tokens=split, label=f"small{case}")
+
+
+def test_zero_query_gives_cumulative_mean():
+    """q = 0: every visible key has the same weight; row j is the mean of V
+    over keys 0..c+j (pins the visibility boundary key by key)."""
+    w = workloads.random_workload(77, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                  decode_ctx=[33], chunks=[(21, 21 + 70)])
+    w.q[:] = 0
+    ds, _ = check_step(w, decode_split_tokens=16, label="q0")
+    # and against the closed form directly
+    out = ds.out_f64()
+    bt = w.block_table[ds.meta["order"]]
+    kp, vp = oracle.append(w.k_pool, w.v_pool, w.k_new[:ds.num_tokens], w.v_new[:ds.num_tokens],
+                           ds.meta["query_start_loc"], ds.meta["context_lens"], bt)
+    s = 1
+    c = ds.meta["context_lens"][s]
+    for j in (0, 1, 37, 69):
+        t = ds.meta["query_start_loc"][s] + j
+        keys = np.arange(c + j + 1)
+        V = oracle.bf16_bits_to_f64(vp[bt[s][keys // 16], 0, :, keys % 16])
+        assert np.max(np.abs(out[t, 0] - V.mean(axis=0))) <= OUT_TOL
+
+
+def test_first_token_sees_only_itself():
+    """Context 0, chunk starting at 0: token 0's output is its own V exactly."""
+    w = workloads.random_workload(78, num_q_heads=4, num_kv_heads=4, head_dim=64, decode_ctx=[],
+                                  chunks=[(0, 40)])
+    ds, _ = check_step(w, label="self")
+    v0 = oracle.bf16_bits_to_f64(w.v_new[0])  # [Hkv, D]
+    assert np.array_equal(ds.out_f64()[0], v0)
+
+
+def test_decode_row_equals_one_token_chunk_row():
+    """The same query as a decode row (split-KV kernel) and as a one-token
+    prefill row (MFMA kernel) gives the same output."""
+    import torch
+    w = workloads.random_workload(79, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                  decode_ctx=[700], chunks=[(700, 701)])
+    # same query and new K/V for both rows, and identical cached context
+    w.q[1] = w.q[0]
+    w.k_new[1] = w.k_new[0]
+    w.v_new[1] = w.v_new[0]
+    pages = 701 // 16 + 1
+    w.k_pool[w.block_table[1, :pages]] = w.k_pool[w.block_table[0, :pages]]
+    w.v_pool[w.block_table[1, :pages]] = w.v_pool[w.block_table[0, :pages]]
+    ds = DeviceStep(w, decode_split_tokens=0)
+    assert ds.num_decodes == 1 and ds.num_seqs == 2 and ds.counts.num_chunk_tiles == 1
+    ds.run()
+    torch.cuda.synchronize()
+    out = ds.out_f64()
+    assert np.max(np.abs(out[0] - out[1])) <= 1e-2
+    _, _, ref, _ = oracle_step(w, ds.meta)
+    assert np.max(np.abs(out - ref)) <= OUT_TOL
+
+
+@pytest.mark.parametrize("split", [16, 32, 256, 4096])
+def test_decode_split_count_does_not_change_result(split):
+    w = workloads.random_workload(80, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                  decode_ctx=[4000, 1, 16, 17, 999], chunks=[])
+    check_step(w, decode_split_tokens=split, label=f"split{split}")
+
+
+@pytest.mark.parametrize("C", [1, 7, 16, 64, 100, 256])
+def test_gpu_chunking_invariance(C):
+    """One 256-token prompt prefilled in chunks of C, each chunk appended
+    first then attended; every chunking lands within tolerance of the one-shot
+    causal prefill computed by the oracle."""
+    import torch
+    L, Hq, Hkv, D = 256, 16, 4, 128
+    w = workloads.random_workload(81, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  decode_ctx=[], chunks=[(0, L)], token_budget=L)
+    # one-shot oracle
+    bt = w.block_table
+    kp, vp = oracle.append(w.k_pool, w.v_pool, w.k_new[:L], w.v_new[:L], [0, L], [0], bt)
+    ref, _ = oracle.attention(w.q[:L], kp, vp, [0, L], [0], bt, Hkv, w.scale)
+    gk, gv = w.k_pool, w.v_pool
+    outs = []
+    for a in range(0, L, C):
+        b = min(L, a + C)
+        wc = workloads.Workload(name="inv", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                token_budget=b - a, long_prefill_cap=0,
+                                requests=[workloads.Req(0, a, L, False)], block_table=bt,
+                                k_pool=gk, v_pool=gv, q=w.q[a:b], k_new=w.k_new[a:b],
+                                v_new=w.v_new[a:b], scale=w.scale)
+        ds = DeviceStep(wc)
+        ds.run()
+        torch.cuda.synchronize()
+        outs.append(ds.out_f64())
+        gk, gv = ds.pools_bits()
+    got = np.concatenate(outs)
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+    assert np.max(np.abs(got - ref)) <= OUT_TOL
+
+
+def test_workspace_too_small_is_rejected():
+    import torch
+    w = workloads.random_workload(82, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                  decode_ctx=[300], chunks=[])
+    ds = DeviceStep(w, decode_split_tokens=16)
+    assert ds.counts.num_partials > 0
+    ds.workspace = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(cpa.CpaError) as e:
+        ds.attention()
+    assert e.value.status == cpa.CPA_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("config", [2, 3, 4, 5])
+def test_config_end_to_end(config):
+    """The measured configurations at full size: whole pool bit-exact, outputs
+    of every decode row and of sampled chunk tokens (first/last 16 of each
+    chunk and random ones) against the oracle."""
+    rng = np.random.default_rng(config)
+    for inst in range(workloads.num_instances(config)):
+        w = workloads.make_workload(config, inst)
+        meta = cpa.cpa_build_metadata(
+            w.requests, token_budget=w.token_budget, long_prefill_cap=w.long_prefill_cap,
+            num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim)
+        toks = sample_tokens(meta, rng)
+        check_step(w, tokens=toks, label=f"{w.name}")

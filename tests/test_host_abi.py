@@ -1,0 +1,265 @@
+"""Host-side tests of libcpa.so (no GPU needed): the library loads and exports
+every symbol include/cpa.h declares; cpa_build_metadata agrees with the
+oracle's scheduler element for element, reproduces the pages' worked
+numbers, reports every error path, and emits a work plan that covers each
+row exactly once."""
+
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_prefill_mixed_amd import cpa, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "cpa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert set(syms) == set(cpa.EXPORTED)
+    for s in syms:
+        assert hasattr(lib, s), s
+    import subprocess
+    nm = subprocess.run(["nm", "-D", "--defined-only", cpa.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (cpa_\w+)", nm))
+    assert set(syms) <= exported
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert cpa.cpa_status_string(st).startswith("CPA_")
+    assert "unknown" in cpa.cpa_status_string(7)
+
+
+def build(reqs, budget, cap=0, Hq=32, Hkv=8, D=128, **kw):
+    return cpa.cpa_build_metadata(reqs, token_budget=budget, long_prefill_cap=cap,
+                                  num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, **kw)
+
+
+def same_as_oracle(reqs, budget, cap=0, **kw):
+    got = build(reqs, budget, cap, **kw)
+    ref = oracle.schedule([oracle.Request(r.id, r.num_computed, r.target_len, bool(r.is_decode))
+                           for r in reqs], budget, cap)
+    for k in ("order", "num_scheduled", "query_start_loc", "seq_lens", "context_lens", "new_blocks"):
+        assert list(got[k]) == list(ref[k]), k
+    for k in ("num_seqs", "num_decodes", "num_tokens"):
+        assert got[k] == ref[k], k
+    return got
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_builder_matches_oracle_on_configs(lib, config):
+    for inst in range(workloads.num_instances(config)):
+        w = workloads.make_workload(config, inst)
+        got = same_as_oracle(w.requests, w.token_budget, w.long_prefill_cap,
+                             Hq=w.num_q_heads, Hkv=w.num_kv_heads, D=w.head_dim,
+                             host_block_table=w.block_table, num_blocks=w.num_blocks)
+        check_plan(got, w.num_q_heads // w.num_kv_heads)
+        # slot mapping: page * 16 + slot of every scheduled token (checked here
+        # with the test's own indexing)
+        sm = got["slot_mapping"]
+        for s in range(got["num_seqs"]):
+            r = w.requests[got["order"][s]]
+            for i in range(got["num_scheduled"][s]):
+                p = r.num_computed + i
+                t = got["query_start_loc"][s] + i
+                assert sm[t] == w.block_table[got["order"][s], p // 16] * 16 + p % 16
+        if config >= 4:
+            break
+
+
+def check_plan(m, group, split=None):
+    """Every decode row's keys are covered exactly once by page-aligned splits;
+    merges list exactly the rows with several splits; chunk tiles cover each
+    chunk row's tokens exactly once, longest key range first."""
+    sec = cpa.plan_sections(m["plan"], m["counts"])
+    nd = m["num_decodes"]
+    cover = {s: [] for s in range(nd)}
+    slots = []
+    for row, b, e, slot in sec["decode_splits"]:
+        assert 0 <= row < nd and b % 16 == 0 and b < e
+        cover[row].append((b, e, slot))
+        if slot >= 0:
+            slots.append(slot)
+    merged = {}
+    for row, first, n, _ in sec["decode_merges"]:
+        merged[row] = (first, n)
+    for s in range(nd):
+        pieces = sorted(cover[s])
+        assert pieces[0][0] == 0 and pieces[-1][1] == m["seq_lens"][s]
+        for (b0, e0, _), (b1, _, _) in zip(pieces, pieces[1:]):
+            assert e0 == b1
+        if len(pieces) == 1:
+            assert pieces[0][2] == -1 and s not in merged
+        else:
+            first, n = merged[s]
+            assert n == len(pieces)
+            assert sorted(p[2] for p in pieces) == list(range(first, first + n))
+    assert sorted(slots) == list(range(m["counts"].num_partials))
+    tiles = sec["chunk_tiles"]
+    tt = 128 // group
+    seen = {}
+    for row, qb, qe, _ in tiles:
+        assert nd <= row < m["num_seqs"] and 0 <= qb < qe <= m["num_scheduled"][row]
+        assert qe - qb <= tt and qb % tt == 0
+        seen.setdefault(row, []).append((qb, qe))
+    for s in range(nd, m["num_seqs"]):
+        pieces = sorted(seen[s])
+        assert pieces[0][0] == 0 and pieces[-1][1] == m["num_scheduled"][s]
+        for (a0, b0), (a1, _) in zip(pieces, pieces[1:]):
+            assert b0 == a1
+    keys = [m["context_lens"][r] + qe for r, _, qe, _ in tiles]
+    assert keys == sorted(keys, reverse=True)
+
+
+def users_and_prompt(running, prompt):
+    reqs = [oracle.Request(i, 100 + i, 101 + i, True) for i in range(running)]
+    reqs.append(oracle.Request(running, 0, prompt, False))
+    return reqs
+
+
+def test_builder_reproduces_page_pins(lib):
+    # chunk = budget - running users ("Chunked Prefill", "Why a chunk can be nearly free")
+    for budget, chunk in [(256, 224), (512, 480), (4096, 4064)]:
+        m = build(users_and_prompt(32, 8192), budget)
+        assert m["num_scheduled"][-1] == chunk
+    # passes for an 8192-token prompt beside 32 users ("The budget points in two directions")
+    for budget, passes in [(16384, 1), (2048, 5), (512, 18), (256, 37)]:
+        reqs, n = users_and_prompt(32, 8192), 0
+        while not reqs[-1].is_decode:
+            m = build(reqs, budget)
+            reqs = oracle.advance(reqs, {"order": list(m["order"]),
+                                         "num_scheduled": list(m["num_scheduled"])})
+            n += 1
+        assert n == passes
+    # budget floor
+    with pytest.raises(cpa.CpaError) as e:
+        build(users_and_prompt(32, 8192), 16)
+    assert e.value.status == cpa.CPA_ERR_BUDGET
+    # "05. Chunked Prefill" sections 2 and 4: {A:1, B:1, C:2048} = 2050
+    reqs = [oracle.Request(0, 500, 501, True), oracle.Request(1, 900, 901, True),
+            oracle.Request(2, 0, 8192, False)]
+    m = build(reqs, 8192, 2048)
+    assert list(m["num_scheduled"]) == [1, 1, 2048] and m["num_tokens"] == 2050
+    # tbr8.org 4.2: 2500 tokens need 157 pages
+    m = build([oracle.Request(0, 0, 2500, False)], 4096)
+    assert list(m["new_blocks"]) == [157]
+
+
+def test_builder_random_mixes_match_oracle(lib):
+    rng = np.random.default_rng(2024)
+    for _ in range(300):
+        n = int(rng.integers(0, 40))
+        reqs = []
+        for i in range(n):
+            if rng.random() < 0.6:
+                c = int(rng.integers(0, 5000))
+                reqs.append(oracle.Request(i, c, c + 1, True))
+            else:
+                L = int(rng.integers(1, 9000))
+                c = int(rng.integers(0, L + 1))
+                reqs.append(oracle.Request(i, c, L, False))
+        ndec = sum(r.is_decode for r in reqs)
+        budget = int(rng.integers(max(1, ndec), ndec + 9000))
+        cap = int(rng.choice([0, 0, 16, 100, 2048]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 8]))
+        split = int(rng.choice([0, 0, 16, 128, 512]))
+        m = same_as_oracle(reqs, budget, cap, Hq=G * Hkv, Hkv=Hkv, D=D, decode_split_tokens=split)
+        check_plan(m, G)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("budget_zero", cpa.CPA_ERR_INVALID),
+    ("negative_computed", cpa.CPA_ERR_INVALID),
+    ("target_below_computed", cpa.CPA_ERR_INVALID),
+    ("decodes_over_budget", cpa.CPA_ERR_BUDGET),
+    ("head_dim_96", cpa.CPA_ERR_UNSUPPORTED),
+    ("group_3", cpa.CPA_ERR_UNSUPPORTED),
+    ("heads_not_multiple", cpa.CPA_ERR_UNSUPPORTED),
+    ("block_size_32", cpa.CPA_ERR_UNSUPPORTED),
+    ("split_not_page_multiple", cpa.CPA_ERR_INVALID),
+    ("block_table_too_short", cpa.CPA_ERR_INVALID),
+    ("block_id_out_of_range", cpa.CPA_ERR_INVALID),
+    ("duplicate_slot", cpa.CPA_ERR_INVALID),
+    ("fresh_slot_is_cached_elsewhere", cpa.CPA_ERR_INVALID),
+])
+def test_builder_error_paths(lib, case, status):
+    R = oracle.Request
+    reqs = [R(0, 20, 21, True), R(1, 0, 40, False)]
+    kw = dict(budget=64)
+    bt = np.array([[0, 1, 9], [2, 3, 4]], dtype=np.int32)
+    args = dict(Hq=8, Hkv=2, D=128)
+    if case == "budget_zero":
+        kw["budget"] = 0
+    elif case == "negative_computed":
+        reqs[0] = R(0, -1, 0, True)
+    elif case == "target_below_computed":
+        reqs[1] = R(1, 50, 40, False)
+    elif case == "decodes_over_budget":
+        reqs = [R(i, 5, 6, True) for i in range(10)]
+        kw["budget"] = 9
+    elif case == "head_dim_96":
+        args["D"] = 96
+    elif case == "group_3":
+        args.update(Hq=6, Hkv=2)
+    elif case == "heads_not_multiple":
+        args.update(Hq=7, Hkv=2)
+    elif case == "block_size_32":
+        kw["block_size"] = 32
+    elif case == "split_not_page_multiple":
+        kw["decode_split_tokens"] = 24
+    elif case == "block_table_too_short":
+        kw.update(host_block_table=bt[:, :2], num_blocks=10)
+    elif case == "block_id_out_of_range":
+        kw.update(host_block_table=bt, num_blocks=4)  # row 1 uses page id 4
+    elif case == "duplicate_slot":
+        bt2 = bt.copy()
+        bt2[1, 0] = 1  # row 1's first page is row 0's second page; both get written
+        reqs[0] = R(0, 16, 17, True)
+        kw.update(host_block_table=bt2, num_blocks=10)
+    elif case == "fresh_slot_is_cached_elsewhere":
+        bt2 = bt.copy()
+        bt2[1, 0] = 0  # row 1 would overwrite positions row 0 reads as context
+        kw.update(host_block_table=bt2, num_blocks=10)
+    budget = kw.pop("budget")
+    with pytest.raises(cpa.CpaError) as e:
+        cpa.cpa_build_metadata(reqs, token_budget=budget, long_prefill_cap=0,
+                               num_q_heads=args["Hq"], num_kv_heads=args["Hkv"],
+                               head_dim=args["D"], **kw)
+    assert e.value.status == status
+
+
+def test_builder_valid_block_table_accepted(lib):
+    R = oracle.Request
+    reqs = [R(0, 20, 21, True), R(1, 0, 40, False)]
+    bt = np.array([[0, 1, 9], [2, 3, 4]], dtype=np.int32)
+    m = cpa.cpa_build_metadata(reqs, token_budget=64, long_prefill_cap=0, num_q_heads=8,
+                               num_kv_heads=2, head_dim=128, host_block_table=bt, num_blocks=10)
+    assert m["slot_mapping"][0] == 1 * 16 + 4
+    assert list(m["slot_mapping"][1:4]) == [32, 33, 34]
+
+
+def test_workspace_size(lib):
+    c = cpa.cpa_plan_counts_t(5, 2, 3, 7)
+    assert cpa.cpa_workspace_size(c, 32, 128) == math.ceil(7 * 32 * 130 * 4 / 256) * 256
+    c0 = cpa.cpa_plan_counts_t(5, 0, 3, 0)
+    assert cpa.cpa_workspace_size(c0, 32, 128) == 0
+
+
+def test_empty_step(lib):
+    m = build([], 16)
+    assert m["num_seqs"] == 0 and m["num_tokens"] == 0
+    assert m["counts"].num_decode_splits == 0 and m["counts"].num_chunk_tiles == 0
