@@ -1,0 +1,403 @@
+#!/usr/bin/env python3
+"""Mixed-batch attention throughput on one MI355X.
+
+A step is one pass of the whole path over one packed batch: the host
+decode-first budget split and work plan (cpa_build_metadata), one H2D copy of
+the step metadata, the paged KV append, the split-KV decode kernel, its
+log-sum-exp merge and the MFMA prefill-chunk kernel, all on one stream.
+Inputs (q, new K/V, the paged KV pool) are resident in HBM before timing.
+
+Default workload (Page-1 defaults of the chunked-prefill essay): 32 decode
+rows with contexts uniform in [512, 4096] plus one 480-token chunk (budget
+512) of an 8192-token prompt at prefix 0, 3840 and 7680; Hq=32, Hkv=8,
+D=128, bf16, 16-token pages.  The three prefix instances have their own KV
+pools and are rotated step by step, so no step finds its K/V in the 256 MB
+last-level cache from the previous step.
+
+Prints ONE JSON line on stdout.  Per-kernel durations come from HIP events
+recorded on the launch stream around each launch inside the timed region.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
+METRIC = "mixed-batch attention tokens/s; % HBM GB/s (decode) & % MFMA (chunk)"
+
+WORKLOAD_TEXT = {
+    1: "tiny: Hq=Hkv=4 D=64; 4 decode rows (context U[100,300]) + a 64-token chunk of a 256-token "
+       "prompt, 4 chunk positions rotated; budget 68",
+    2: "page1_defaults: 32 decode rows (context U[512,4096]) + a 480-token chunk of an 8192-token "
+       "prompt at prefix 0/3840/7680 (3 instances rotated per step); Hq=32 Hkv=8 D=128 bf16, "
+       "16-token pages, budget 512",
+    3: "budget8192: 2 decode rows (context 1000, 3000) + a 2048-token chunk of an 8192-token prompt "
+       "at prefix 0/2048/4096/6144 (4 instances rotated); cap 2048; Hq=32 Hkv=8 D=128",
+    4: "long_context: final 1024-token chunk of a 32768-token prompt (prefix 31744) + 64 decode "
+       "rows (context lognormal, median 2048, sigma 0.75, cap 32768); Hq=32 Hkv=8 D=128",
+    5: "heavy_mixed: 256 decode rows (context lognormal, median 1024, sigma 0.75, cap 16384) + "
+       "chunks of 2048, 2048 and 3840 tokens at random prefixes in [0,16384]; budget 8192; "
+       "2 GiB KV pool; Hq=32 Hkv=8 D=128",
+}
+
+KERNEL_SOURCES = {
+    "decode_kernel": ["decode.hip", "device.h", "tiles.h"],
+    "chunk_kernel": ["chunk.hip", "device.h", "tiles.h"],
+    "append_kernel": ["append.hip", "device.h", "tiles.h"],
+    "merge_kernel": ["decode.hip", "device.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "chunked_prefill_mixed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one step (what the method must move or compute)
+# ---------------------------------------------------------------------------
+
+def step_work(meta, Hq, Hkv, D):
+    nd = meta["num_decodes"]
+    seq = meta["seq_lens"]
+    ctx = meta["context_lens"]
+    nsch = meta["num_scheduled"]
+    dec_keys = sum(int(seq[s]) for s in range(nd))
+    dec_pages = sum(math.ceil(int(seq[s]) / 16) for s in range(nd))
+    decode_bytes = dec_keys * Hkv * D * 2 * 2 + nd * Hq * D * 2 * 2 + dec_pages * 4
+    chunk_flops = 0
+    chunk_min_bytes = 0
+    for s in range(nd, meta["num_seqs"]):
+        n, c = int(nsch[s]), int(ctx[s])
+        chunk_flops += 4 * D * Hq * (n * c + n * (n + 1) // 2)
+        chunk_min_bytes += (c + n) * Hkv * D * 4 + 2 * n * Hq * D * 2
+    T = meta["num_tokens"]
+    append_bytes = T * Hkv * D * 2 * 2 * 2
+    return {"decode_bytes": decode_bytes, "chunk_flops": chunk_flops,
+            "chunk_min_bytes": chunk_min_bytes, "append_bytes": append_bytes, "tokens": T,
+            "decode_keys": dec_keys}
+
+
+# ---------------------------------------------------------------------------
+# one resident instance with its per-step host work prepared
+# ---------------------------------------------------------------------------
+
+class Instance:
+    def __init__(self, w, torch, cpa, DeviceStep):
+        self.w = w
+        self.ds = ds = DeviceStep(w, validate=True, with_lse=False)
+        lib = self.lib = cpa.load()
+        m = ds.meta
+        ns, words = ds.num_seqs, int(m["plan"].size)
+        # packed metadata: [qsl | seq_lens | ctx | plan], each section 16-byte aligned
+        def up4(x):
+            return (x + 3) // 4 * 4
+        self.off = off = {}
+        at = 0
+        for name, n in (("qsl", ns + 1), ("seq", ns), ("ctx", ns), ("plan", max(1, words))):
+            off[name] = at
+            at += up4(n)
+        self.pinned = torch.zeros(at, dtype=torch.int32, pin_memory=True)
+        self.dev = torch.zeros(at, dtype=torch.int32, device="cuda")
+        pn = self.pinned.numpy()
+        i32p = cpa.i32p
+        self.reqs = (cpa.cpa_req_t * max(1, len(w.requests)))()
+        for i, r in enumerate(w.requests):
+            self.reqs[i] = cpa.cpa_req_t(r.id, r.num_computed, r.target_len, int(r.is_decode))
+        self.nreq = len(w.requests)
+        self.params = cpa.cpa_build_params_t(w.token_budget, w.long_prefill_cap, 16, w.num_q_heads,
+                                             w.num_kv_heads, w.head_dim, 0, 0)
+        import numpy as np
+        self.scratch = {k: np.zeros(max(1, self.nreq), dtype=np.int32)
+                        for k in ("order", "nsch", "newb")}
+        meta = self.meta = cpa.cpa_meta_t()
+        meta.max_seqs = max(1, self.nreq)
+        meta.order = self.scratch["order"].ctypes.data_as(i32p)
+        meta.num_scheduled = self.scratch["nsch"].ctypes.data_as(i32p)
+        meta.new_blocks = self.scratch["newb"].ctypes.data_as(i32p)
+        meta.query_start_loc = pn[off["qsl"]:].ctypes.data_as(i32p)
+        meta.seq_lens = pn[off["seq"]:].ctypes.data_as(i32p)
+        meta.context_lens = pn[off["ctx"]:].ctypes.data_as(i32p)
+        meta.max_tokens = 0
+        meta.slot_mapping = None
+        meta.plan_capacity = max(1, words)
+        meta.plan = pn[off["plan"]:].ctypes.data_as(i32p)
+        self.build_host()  # fills the pinned buffer once
+        assert self.meta.num_tokens == ds.num_tokens and self.meta.plan_words == words
+        # device tensors of the step now live in the packed buffer
+        d = self.dev
+        ds.query_start_loc = d[off["qsl"]:off["qsl"] + ns + 1]
+        ds.seq_lens = d[off["seq"]:off["seq"] + ns]
+        ds.context_lens = d[off["ctx"]:off["ctx"] + ns]
+        ds.plan = d[off["plan"]:off["plan"] + max(1, words)]
+        self.dev.copy_(self.pinned)
+        torch.cuda.synchronize()
+        self.copy_done = torch.cuda.Event()
+        self.copy_done.record()
+        self._prepare_calls(torch, cpa)
+        self.work = step_work(m, w.num_q_heads, w.num_kv_heads, w.head_dim)
+
+    def build_host(self):
+        st = self.lib.cpa_build_metadata(self.reqs, self.nreq, ctypes.byref(self.params), None, 0,
+                                         0, ctypes.byref(self.meta))
+        if st != 0:
+            raise RuntimeError(f"cpa_build_metadata failed: {st}")
+
+    def _prepare_calls(self, torch, cpa):
+        ds, w = self.ds, self.w
+        vp = ctypes.c_void_p
+        P = lambda t: vp(t.data_ptr()) if t is not None else None
+        self.stream = vp(torch.cuda.current_stream().cuda_stream)
+        c = ds.counts
+        plan_base = ds.plan.data_ptr()
+        nsp, nmg, ntl, npart = (c.num_decode_splits, c.num_decode_merges, c.num_chunk_tiles,
+                                c.num_partials)
+        self.parts = []
+        common_tail = (ds.num_seqs, ds.num_decodes, ds.num_tokens, w.num_q_heads, w.num_kv_heads,
+                       w.head_dim, 16, ctypes.c_float(w.scale), P(ds.out), None,
+                       P(ds.workspace), ctypes.c_size_t(0 if ds.workspace is None
+                                                        else ds.workspace.numel()),
+                       self.stream)
+        head = (P(ds.q), P(ds.k_cache), P(ds.v_cache), P(ds.block_table),
+                int(ds.block_table.shape[1]), P(ds.query_start_loc), P(ds.seq_lens),
+                P(ds.context_lens))
+        sections = [
+            ("decode", cpa.cpa_plan_counts_t(nsp, 0, 0, npart), 0),
+            ("merge", cpa.cpa_plan_counts_t(0, nmg, 0, npart), nsp * 4),
+            ("chunk", cpa.cpa_plan_counts_t(0, 0, ntl, npart), (nsp + nmg) * 4),
+        ]
+        for name, counts, woff in sections:
+            self.parts.append((name, counts, head + (vp(plan_base + 4 * woff), ctypes.byref(counts))
+                               + common_tail))
+        self.append_args = (P(ds.k_new), P(ds.v_new), P(ds.query_start_loc), P(ds.context_lens),
+                            P(ds.block_table), int(ds.block_table.shape[1]), ds.num_seqs,
+                            ds.num_tokens, w.num_kv_heads, w.head_dim, 16, P(ds.k_cache),
+                            P(ds.v_cache), self.stream)
+
+    def step(self, events):
+        """One full step; events = 5 torch events recorded around the launches."""
+        self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
+        self.build_host()
+        self.dev.copy_(self.pinned, non_blocking=True)
+        self.copy_done.record()
+        lib = self.lib
+        events[0].record()
+        st = lib.cpa_append_kv(*self.append_args)
+        events[1].record()
+        for k, (name, counts, args) in enumerate(self.parts):
+            if st == 0:
+                st = lib.cpa_attention(*args)
+            events[2 + k].record()
+        if st != 0:
+            raise RuntimeError(f"launch failed with status {st}")
+
+
+def traffic_for(kernel: str, config: int):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counter runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config_key(config)}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_hash(kernel):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def config_key(config: int) -> str:
+    from chunked_prefill_mixed_amd import workloads
+    return workloads.CONFIG_NAMES[config]
+
+
+def cpu_baseline(workloads_list, seconds: float):
+    """The fp64 oracle (as it stands) on the host cores, whole steps of the
+    same instances, round-robin until ``seconds`` of CPU work have run."""
+    import numpy as np
+
+    import oracle
+    from chunked_prefill_mixed_amd import cpa
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max((i.get("num_threads", 1) for i in blas), default=1)
+        blas_name = ",".join(sorted({f"{i.get('internal_api')}" for i in blas}))
+    except Exception:  # pragma: no cover
+        cores, blas_name = len(os.sched_getaffinity(0)), "unknown"
+    done_tokens, done_steps, t_total = 0, 0, 0.0
+    k = 0
+    while t_total < seconds or done_steps == 0:
+        w = workloads_list[k % len(workloads_list)]
+        m = cpa.cpa_build_metadata(w.requests, token_budget=w.token_budget,
+                                   long_prefill_cap=w.long_prefill_cap,
+                                   num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                   head_dim=w.head_dim)
+        bt = w.block_table[m["order"]]
+        T = m["num_tokens"]
+        t0 = time.perf_counter()
+        kp, vp = oracle.append(w.k_pool, w.v_pool, w.k_new[:T], w.v_new[:T],
+                               m["query_start_loc"], m["context_lens"], bt)
+        oracle.attention(w.q[:T], kp, vp, m["query_start_loc"], m["context_lens"], bt,
+                         w.num_kv_heads, w.scale)
+        t_total += time.perf_counter() - t0
+        done_tokens += T
+        done_steps += 1
+        k += 1
+        del kp, vp
+    return {"value": done_tokens / t_total, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done_steps} whole steps (append + attention of every token) of the same "
+                      f"instances, round-robin, {t_total:.1f} s of fp64 numpy ({blas_name} BLAS)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=90)
+    ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the path has no collectives or sharding.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunked_prefill_mixed_amd import build_lib, cpa, workloads
+    from chunked_prefill_mixed_amd.step import DeviceStep
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (the HIP library has no CPU path)")
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}))
+        return
+    if not os.path.exists(cpa.LIB_PATH):
+        build_lib.build()
+    cpa.load()
+
+    t_setup = time.perf_counter()
+    ws = [workloads.make_workload(args.config, i)
+          for i in range(workloads.num_instances(args.config))]
+    insts = [Instance(w, torch, cpa, DeviceStep) for w in ws]
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
+        f"{[i.ds.num_tokens for i in insts]} tokens/step")
+
+    K, W = args.steps, args.warmup
+    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for s in range(W):
+        insts[s % len(insts)].step(ev_w)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    order = [(W + s) % len(insts) for s in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        insts[order[s]].step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = ["append_kernel", "decode_kernel", "merge_kernel", "chunk_kernel"]
+    times = {n: 0.0 for n in names}
+    work = {"decode_bytes": 0, "chunk_flops": 0, "append_bytes": 0, "tokens": 0}
+    for s in range(K):
+        ev = events[s]
+        for k, n in enumerate(names):
+            times[n] += ev[k].elapsed_time(ev[k + 1]) * 1e-3
+        wk = insts[order[s]].work
+        for key in work:
+            work[key] += wk[key]
+    tokens = work["tokens"]
+    value = tokens / elapsed
+
+    def rate(n, amount, scale):
+        return amount / times[n] / scale if times[n] > 0 else None
+
+    kernels = {
+        "append_kernel": {"avg_us": times["append_kernel"] / K * 1e6,
+                          "GB/s": rate("append_kernel", work["append_bytes"], 1e9)},
+        "decode_kernel": {"avg_us": times["decode_kernel"] / K * 1e6,
+                          "GB/s": rate("decode_kernel", work["decode_bytes"], 1e9)},
+        "merge_kernel": {"avg_us": times["merge_kernel"] / K * 1e6},
+        "chunk_kernel": {"avg_us": times["chunk_kernel"] / K * 1e6,
+                         "TFLOP/s": rate("chunk_kernel", work["chunk_flops"], 1e12)},
+    }
+    for n, peak, unit in (("append_kernel", HBM_PEAK_GBS, "GB/s"),
+                          ("decode_kernel", HBM_PEAK_GBS, "GB/s"),
+                          ("chunk_kernel", MFMA_BF16_PEAK_TFS, "TFLOP/s")):
+        v = kernels[n].get(unit)
+        kernels[n]["frac_of_peak"] = None if v is None else v / peak
+    kernels["decode_plus_merge_GB/s"] = (
+        work["decode_bytes"] / (times["decode_kernel"] + times["merge_kernel"]) / 1e9
+        if times["decode_kernel"] > 0 else None)
+
+    dominant = max(("decode_kernel", "chunk_kernel", "append_kernel"), key=lambda n: times[n])
+    if dominant == "chunk_kernel":
+        ach = kernels["chunk_kernel"]["TFLOP/s"]
+        roofline = {"bound": "mfma", "kernel": dominant, "achieved": ach,
+                    "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS}
+    else:
+        ach = kernels[dominant]["GB/s"]
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
+    roofline["traffic"] = traffic_for(dominant, args.config)
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "config": config_key(args.config),
+                   "tokens_per_step": sorted({i.ds.num_tokens for i in insts}),
+                   "instances": len(insts)},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host cores ...")
+        result["cpu_baseline"] = cpu_baseline(ws, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
