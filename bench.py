@@ -56,6 +56,7 @@ KERNEL_SOURCES = {
     "chunk_kernel": ["chunk.hip", "device.h", "tiles.h"],
     "append_kernel": ["append.hip", "device.h", "tiles.h"],
     "merge_kernel": ["decode.hip", "device.h"],
+    "chunk_merge_kernel": ["chunk.hip", "device.h", "tiles.h"],
 }
 
 
@@ -168,8 +169,7 @@ class Instance:
         self.stream = vp(torch.cuda.current_stream().cuda_stream)
         c = ds.counts
         plan_base = ds.plan.data_ptr()
-        nsp, nmg, ntl, npart = (c.num_decode_splits, c.num_decode_merges, c.num_chunk_tiles,
-                                c.num_partials)
+        off = cpa.section_offsets(c)
         self.parts = []
         common_tail = (ds.num_seqs, ds.num_decodes, ds.num_tokens, w.num_q_heads, w.num_kv_heads,
                        w.head_dim, 16, ctypes.c_float(w.scale), P(ds.out), None,
@@ -179,21 +179,27 @@ class Instance:
         head = (P(ds.q), P(ds.k_cache), P(ds.v_cache), P(ds.block_table),
                 int(ds.block_table.shape[1]), P(ds.query_start_loc), P(ds.seq_lens),
                 P(ds.context_lens))
+        zero = dict(num_decode_splits=0, num_decode_merges=0, num_chunk_tiles=0,
+                    num_chunk_merges=0)
+        # one launch per call, in the library's own order, so HIP events can
+        # bracket each kernel
         sections = [
-            ("decode", cpa.cpa_plan_counts_t(nsp, 0, 0, npart), 0),
-            ("merge", cpa.cpa_plan_counts_t(0, nmg, 0, npart), nsp * 4),
-            ("chunk", cpa.cpa_plan_counts_t(0, 0, ntl, npart), (nsp + nmg) * 4),
+            ("decode_kernel", "num_decode_splits", "decode_splits"),
+            ("chunk_kernel", "num_chunk_tiles", "chunk_tiles"),
+            ("merge_kernel", "num_decode_merges", "decode_merges"),
+            ("chunk_merge_kernel", "num_chunk_merges", "chunk_merges"),
         ]
-        for name, counts, woff in sections:
-            self.parts.append((name, counts, head + (vp(plan_base + 4 * woff), ctypes.byref(counts))
-                               + common_tail))
+        for name, field, sec in sections:
+            counts = c.copy(**{**zero, field: getattr(c, field)})
+            self.parts.append((name, counts, head + (vp(plan_base + 4 * off[sec]),
+                                                     ctypes.byref(counts)) + common_tail))
         self.append_args = (P(ds.k_new), P(ds.v_new), P(ds.query_start_loc), P(ds.context_lens),
                             P(ds.block_table), int(ds.block_table.shape[1]), ds.num_seqs,
                             ds.num_tokens, w.num_kv_heads, w.head_dim, 16, P(ds.k_cache),
                             P(ds.v_cache), self.stream)
 
     def step(self, events):
-        """One full step; events = 5 torch events recorded around the launches."""
+        """One full step; events = 6 torch events recorded around the launches."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         self.build_host()
         self.dev.copy_(self.pinned, non_blocking=True)
@@ -313,12 +319,13 @@ def main():
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
 
     K, W = args.steps, args.warmup
-    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    NEV = 6
+    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
     for s in range(W):
         insts[s % len(insts)].step(ev_w)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(K)]
     order = [(W + s) % len(insts) for s in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -327,7 +334,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    names = ["append_kernel", "decode_kernel", "merge_kernel", "chunk_kernel"]
+    names = ["append_kernel", "decode_kernel", "chunk_kernel", "merge_kernel", "chunk_merge_kernel"]
     times = {n: 0.0 for n in names}
     work = {"decode_bytes": 0, "chunk_flops": 0, "append_bytes": 0, "tokens": 0}
     for s in range(K):
@@ -349,6 +356,7 @@ def main():
         "decode_kernel": {"avg_us": times["decode_kernel"] / K * 1e6,
                           "GB/s": rate("decode_kernel", work["decode_bytes"], 1e9)},
         "merge_kernel": {"avg_us": times["merge_kernel"] / K * 1e6},
+        "chunk_merge_kernel": {"avg_us": times["chunk_merge_kernel"] / K * 1e6},
         "chunk_kernel": {"avg_us": times["chunk_kernel"] / K * 1e6,
                          "TFLOP/s": rate("chunk_kernel", work["chunk_flops"], 1e12)},
     }
@@ -357,6 +365,9 @@ def main():
                           ("chunk_kernel", MFMA_BF16_PEAK_TFS, "TFLOP/s")):
         v = kernels[n].get(unit)
         kernels[n]["frac_of_peak"] = None if v is None else v / peak
+    kernels["chunk_plus_merge_TFLOP/s"] = (
+        work["chunk_flops"] / (times["chunk_kernel"] + times["chunk_merge_kernel"]) / 1e12
+        if times["chunk_kernel"] > 0 else None)
     kernels["decode_plus_merge_GB/s"] = (
         work["decode_bytes"] / (times["decode_kernel"] + times["merge_kernel"]) / 1e9
         if times["decode_kernel"] > 0 else None)

@@ -52,13 +52,17 @@ def _run(cmd: list[str]) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libcpa.so; returns its path."""
+    """Compile every source and link libcpa.so; returns its path.
+
+    CPA_HIPCC_EXTRA (environment) adds hipcc flags, e.g. -D overrides of the
+    kernels' compile-time tuning macros."""
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
+    extra = os.environ.get("CPA_HIPCC_EXTRA", "").split()
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".host.o"))
         jobs.append(["g++", *GXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])

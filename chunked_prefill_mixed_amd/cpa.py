@@ -25,7 +25,8 @@ CPA_ERR_DEVICE = -5
 BLOCK_SIZE = 16
 DECODE_SPLIT_WORDS = 4
 DECODE_MERGE_WORDS = 4
-CHUNK_TILE_WORDS = 4
+CHUNK_TILE_WORDS = 8
+CHUNK_MERGE_WORDS = 8
 
 EXPORTED = ("cpa_build_metadata", "cpa_append_kv", "cpa_workspace_size", "cpa_attention",
             "cpa_status_string")
@@ -49,12 +50,18 @@ class cpa_build_params_t(ctypes.Structure):
     _fields_ = [("token_budget", ctypes.c_int32), ("long_prefill_cap", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("decode_split_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("decode_split_tokens", ctypes.c_int32), ("chunk_split_tokens", ctypes.c_int32)]
 
 
 class cpa_plan_counts_t(ctypes.Structure):
     _fields_ = [("num_decode_splits", ctypes.c_int32), ("num_decode_merges", ctypes.c_int32),
-                ("num_chunk_tiles", ctypes.c_int32), ("num_partials", ctypes.c_int32)]
+                ("num_chunk_tiles", ctypes.c_int32), ("num_chunk_merges", ctypes.c_int32),
+                ("num_decode_partials", ctypes.c_int32), ("num_chunk_partials", ctypes.c_int32)]
+
+    def copy(self, **changes):
+        vals = {f: getattr(self, f) for f, _ in self._fields_}
+        vals.update(changes)
+        return cpa_plan_counts_t(**vals)
 
 
 class cpa_meta_t(ctypes.Structure):
@@ -113,7 +120,7 @@ def load():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.cpa_append_kv.restype = ctypes.c_int
     lib.cpa_workspace_size.argtypes = [ctypes.POINTER(cpa_plan_counts_t), ctypes.c_int,
-                                       ctypes.c_int]
+                                       ctypes.c_int, ctypes.c_int]
     lib.cpa_workspace_size.restype = ctypes.c_size_t
     lib.cpa_attention.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
                                   ctypes.POINTER(cpa_plan_counts_t), ctypes.c_int, ctypes.c_int,
@@ -136,8 +143,8 @@ def _i32(a):
 
 
 def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads, num_kv_heads,
-                       head_dim, decode_split_tokens=0, host_block_table=None, num_blocks=0,
-                       block_size=BLOCK_SIZE) -> dict:
+                       head_dim, decode_split_tokens=0, chunk_split_tokens=0,
+                       host_block_table=None, num_blocks=0, block_size=BLOCK_SIZE) -> dict:
     """Decode-first budget split + work plan (host only, no GPU needed).
 
     ``requests``: sequence of objects with id, num_computed, target_len,
@@ -151,7 +158,7 @@ def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads,
         reqs[i] = cpa_req_t(int(r.id), int(r.num_computed), int(r.target_len), int(bool(r.is_decode)))
     params = cpa_build_params_t(int(token_budget), int(long_prefill_cap), int(block_size),
                                 int(num_q_heads), int(num_kv_heads), int(head_dim),
-                                int(decode_split_tokens), 0)
+                                int(decode_split_tokens), int(chunk_split_tokens))
     max_seqs = max(1, n)
     bufs = {k: np.zeros(max_seqs + (1 if k == "query_start_loc" else 0), dtype=np.int32)
             for k in ("order", "num_scheduled", "query_start_loc", "seq_lens", "context_lens",
@@ -187,26 +194,42 @@ def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads,
     out.update(
         num_seqs=ns, num_decodes=meta.num_decodes, num_tokens=meta.num_tokens,
         plan=plan[: meta.plan_words].copy(),
-        counts=cpa_plan_counts_t(meta.counts.num_decode_splits, meta.counts.num_decode_merges,
-                                 meta.counts.num_chunk_tiles, meta.counts.num_partials),
+        counts=meta.counts.copy(),
     )
     if host_block_table is not None:
         out["slot_mapping"] = slots[: meta.num_tokens].copy()
     return out
 
 
+SECTIONS = (("decode_splits", "num_decode_splits", DECODE_SPLIT_WORDS),
+            ("decode_merges", "num_decode_merges", DECODE_MERGE_WORDS),
+            ("chunk_tiles", "num_chunk_tiles", CHUNK_TILE_WORDS),
+            ("chunk_merges", "num_chunk_merges", CHUNK_MERGE_WORDS))
+
+
+def section_offsets(counts) -> dict:
+    """Word offset of each plan section."""
+    out, at = {}, 0
+    for name, field, words in SECTIONS:
+        out[name] = at
+        at += getattr(counts, field) * words
+    out["end"] = at
+    return out
+
+
 def plan_sections(plan: np.ndarray, counts) -> dict:
-    """Split a plan array into its three entry tables (for inspection)."""
-    a = counts.num_decode_splits * DECODE_SPLIT_WORDS
-    b = a + counts.num_decode_merges * DECODE_MERGE_WORDS
-    c = b + counts.num_chunk_tiles * CHUNK_TILE_WORDS
-    return {"decode_splits": plan[:a].reshape(-1, DECODE_SPLIT_WORDS),
-            "decode_merges": plan[a:b].reshape(-1, DECODE_MERGE_WORDS),
-            "chunk_tiles": plan[b:c].reshape(-1, CHUNK_TILE_WORDS)}
+    """Split a plan array into its four entry tables (for inspection)."""
+    off = section_offsets(counts)
+    res = {}
+    for name, field, words in SECTIONS:
+        a = off[name]
+        res[name] = plan[a:a + getattr(counts, field) * words].reshape(-1, words)
+    return res
 
 
-def cpa_workspace_size(counts, num_q_heads: int, head_dim: int) -> int:
-    return int(load().cpa_workspace_size(ctypes.byref(counts), int(num_q_heads), int(head_dim)))
+def cpa_workspace_size(counts, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(load().cpa_workspace_size(ctypes.byref(counts), int(num_q_heads),
+                                         int(num_kv_heads), int(head_dim)))
 
 
 # ---------------------------------------------------------------------------

@@ -54,44 +54,54 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
     return CPA_ERR_INVALID;
   const cpa_plan_counts_t& n = *counts;
   if (n.num_decode_splits < 0 || n.num_decode_merges < 0 || n.num_chunk_tiles < 0 ||
-      n.num_partials < 0)
+      n.num_chunk_merges < 0 || n.num_decode_partials < 0 || n.num_chunk_partials < 0)
     return CPA_ERR_INVALID;
   if (num_tokens == 0) return CPA_OK;
   if (!q || !k_cache || !v_cache || !d_block_table || !d_query_start_loc || !d_context_lens ||
       !d_plan || !out)
     return CPA_ERR_INVALID;
   if (!(softmax_scale > 0.f)) return CPA_ERR_INVALID;
-  const size_t need = cpa_workspace_size(counts, num_q_heads, head_dim);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CPA_ERR_CAPACITY;
+  const cpa::WorkspaceLayout wl =
+      cpa::workspace_layout(n.num_decode_partials, n.num_chunk_partials, num_q_heads, num_kv_heads,
+                            head_dim);
+  if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total)) return CPA_ERR_CAPACITY;
 
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = softmax_scale * 1.4426950408889634f;
-  cpa::Partials ws{nullptr, nullptr, nullptr};
-  if (n.num_partials > 0) {
-    float* base = static_cast<float*>(workspace);
-    ws.acc = base;
-    ws.m = base + (size_t)n.num_partials * num_q_heads * head_dim;
-    ws.l = ws.m + (size_t)n.num_partials * num_q_heads;
+  cpa::Partials dws{nullptr, nullptr, nullptr}, cws{nullptr, nullptr, nullptr};
+  if (wl.total > 0) {
+    char* base = static_cast<char*>(workspace);
+    dws = {reinterpret_cast<float*>(base + wl.dec_acc), reinterpret_cast<float*>(base + wl.dec_m),
+           reinterpret_cast<float*>(base + wl.dec_l)};
+    cws = {reinterpret_cast<float*>(base + wl.chk_acc), reinterpret_cast<float*>(base + wl.chk_m),
+           reinterpret_cast<float*>(base + wl.chk_l)};
   }
   const int32_t* splits = d_plan;
-  const int32_t* merges = splits + (size_t)n.num_decode_splits * CPA_DECODE_SPLIT_WORDS;
-  const int32_t* tiles = merges + (size_t)n.num_decode_merges * CPA_DECODE_MERGE_WORDS;
+  const int32_t* dmerges = splits + (size_t)n.num_decode_splits * CPA_DECODE_SPLIT_WORDS;
+  const int32_t* tiles = dmerges + (size_t)n.num_decode_merges * CPA_DECODE_MERGE_WORDS;
+  const int32_t* cmerges = tiles + (size_t)n.num_chunk_tiles * CPA_CHUNK_TILE_WORDS;
 
+  // decode splits and chunk tiles are independent; merges follow what they merge
   if (n.num_decode_splits > 0) {
     st = status_of(cpa::launch_decode(q, k_cache, v_cache, d_block_table, bt_stride,
                                       d_query_start_loc, splits, n.num_decode_splits, num_q_heads,
-                                      num_kv_heads, head_dim, sl2, out, lse, ws, s));
-    if (st != CPA_OK) return st;
-  }
-  if (n.num_decode_merges > 0) {
-    st = status_of(cpa::launch_merge(merges, n.num_decode_merges, d_query_start_loc, num_q_heads,
-                                     head_dim, ws, out, lse, s));
+                                      num_kv_heads, head_dim, sl2, out, lse, dws, s));
     if (st != CPA_OK) return st;
   }
   if (n.num_chunk_tiles > 0) {
     st = status_of(cpa::launch_chunk(q, k_cache, v_cache, d_block_table, bt_stride,
                                      d_query_start_loc, d_context_lens, tiles, n.num_chunk_tiles,
-                                     num_q_heads, num_kv_heads, head_dim, sl2, out, lse, s));
+                                     num_q_heads, num_kv_heads, head_dim, sl2, out, lse, cws, s));
+    if (st != CPA_OK) return st;
+  }
+  if (n.num_decode_merges > 0) {
+    st = status_of(cpa::launch_merge(dmerges, n.num_decode_merges, d_query_start_loc, num_q_heads,
+                                     head_dim, dws, out, lse, s));
+    if (st != CPA_OK) return st;
+  }
+  if (n.num_chunk_merges > 0) {
+    st = status_of(cpa::launch_chunk_merge(cmerges, n.num_chunk_merges, d_query_start_loc,
+                                           num_q_heads, num_kv_heads, head_dim, cws, out, lse, s));
     if (st != CPA_OK) return st;
   }
   return CPA_OK;

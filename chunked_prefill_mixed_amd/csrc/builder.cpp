@@ -29,14 +29,16 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int check_params(const cpa_build_params_t* p) {
   if (!p) return CPA_ERR_INVALID;
-  if (p->token_budget <= 0 || p->long_prefill_cap < 0 || p->reserved != 0) return CPA_ERR_INVALID;
+  if (p->token_budget <= 0 || p->long_prefill_cap < 0) return CPA_ERR_INVALID;
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0) return CPA_ERR_INVALID;
-  if (p->decode_split_tokens < 0) return CPA_ERR_INVALID;
+  if (p->decode_split_tokens < 0 || p->chunk_split_tokens < 0) return CPA_ERR_INVALID;
   if (p->block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
   if (p->num_q_heads % p->num_kv_heads) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_group(p->num_q_heads / p->num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_head_dim(p->head_dim)) return CPA_ERR_UNSUPPORTED;
-  if (p->decode_split_tokens % cpa::kBlock) return CPA_ERR_INVALID;
+  if (p->decode_split_tokens % cpa::kBlock || p->decode_split_tokens > cpa::kDecodeMaxSplit)
+    return CPA_ERR_INVALID;
+  if (p->chunk_split_tokens % cpa::kKvTile) return CPA_ERR_INVALID;
   return CPA_OK;
 }
 
@@ -46,7 +48,16 @@ int pick_split(int64_t decode_keys, int num_kv_heads) {
   int64_t splits = std::max<int64_t>(1, cpa::kDecodeWavesTarget / num_kv_heads);
   int64_t per = ceil_div(std::max<int64_t>(decode_keys, 1), splits);
   per = ceil_div(per, cpa::kBlock) * cpa::kBlock;
-  return (int)std::min<int64_t>(std::max<int64_t>(per, 128), 4096);
+  return (int)std::min<int64_t>(std::max<int64_t>(per, 128), cpa::kDecodeMaxSplit);
+}
+
+// Prefix keys per chunk piece: none split when the tiles alone give enough
+// workgroups; otherwise about kChunkWgTarget pieces (x KV heads) overall.
+int64_t pick_chunk_split(int64_t tiles, int64_t total_keys, int num_kv_heads) {
+  if (tiles * num_kv_heads >= cpa::kChunkWgTarget) return INT64_MAX;
+  int64_t per = ceil_div(total_keys * num_kv_heads, cpa::kChunkWgTarget);
+  per = ceil_div(per, cpa::kKvTile) * cpa::kKvTile;
+  return std::max<int64_t>(per, cpa::kChunkMinSplit);
 }
 
 }  // namespace
@@ -160,53 +171,100 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
                                                 : pick_split(decode_keys, params->num_kv_heads);
   std::vector<int32_t> dsplits, dmerges, tiles;
   int partials = 0;
+  // a row of L keys is cut into n = ceil(L / split) pieces of nearly equal,
+  // page-aligned size; pieces are emitted longest first so the last waves to
+  // start are short ones
+  struct DPiece { int32_t row, kb, ke, slot; };
+  std::vector<DPiece> dp;
   for (int s = 0; s < n_dec; ++s) {
     const int L = out->seq_lens[s];
-    const int pieces = (int)ceil_div(L, split);
-    if (pieces == 1) {
-      dsplits.insert(dsplits.end(), {s, 0, L, -1});
+    const int64_t pages = ceil_div(L, cpa::kBlock);
+    const int n = (int)ceil_div(L, split);
+    if (n == 1) {
+      dp.push_back({s, 0, L, -1});
       continue;
     }
-    dmerges.insert(dmerges.end(), {s, partials, pieces, 0});
-    for (int k = 0; k < pieces; ++k)
-      dsplits.insert(dsplits.end(), {s, k * split, std::min(L, (k + 1) * split), partials + k});
-    partials += pieces;
+    dmerges.insert(dmerges.end(), {s, partials, n, 0});
+    for (int k = 0; k < n; ++k) {
+      const int32_t kb = (int32_t)(pages * k / n) * cpa::kBlock;
+      const int32_t ke = k + 1 < n ? (int32_t)(pages * (k + 1) / n) * cpa::kBlock : L;
+      dp.push_back({s, kb, ke, partials + k});
+    }
+    partials += n;
   }
+  std::stable_sort(dp.begin(), dp.end(),
+                   [](const DPiece& x, const DPiece& y) { return x.ke - x.kb > y.ke - y.kb; });
+  for (const DPiece& p : dp) dsplits.insert(dsplits.end(), {p.row, p.kb, p.ke, p.slot});
+
+  // chunk tiles: 128 (token, head) rows of one KV head each.  Keys below
+  // context + q_begin are visible to every row of the tile, so a long prefix
+  // may be cut into pieces at multiples of the split size; the last piece
+  // holds the rest, including the causal diagonal.
   const int tile_tokens = cpa::chunk_tile_tokens(group);
-  struct Tile { int32_t row, qb, qe; int64_t keys; };
+  struct Tile { int32_t row, qb, qe; int64_t prefix, keys; };
   std::vector<Tile> tl;
+  int64_t chunk_keys = 0;
   for (int s = n_dec; s < nseq; ++s) {
     const int n = out->num_scheduled[s];
     for (int qb = 0; qb < n; qb += tile_tokens) {
       const int qe = std::min(n, qb + tile_tokens);
-      tl.push_back({s, qb, qe, (int64_t)out->context_lens[s] + qe});
+      const int64_t c = out->context_lens[s];
+      tl.push_back({s, qb, qe, c + qb, c + qe});
+      chunk_keys += c + qe;
     }
   }
-  std::stable_sort(tl.begin(), tl.end(), [](const Tile& x, const Tile& y) { return x.keys > y.keys; });
-  for (const Tile& t : tl) tiles.insert(tiles.end(), {t.row, t.qb, t.qe, 0});
+  const int64_t csplit = params->chunk_split_tokens
+                             ? (int64_t)params->chunk_split_tokens
+                             : pick_chunk_split((int64_t)tl.size(), chunk_keys, params->num_kv_heads);
+  struct Piece { int32_t row, qb, qe, kb, ke, slot; };
+  std::vector<Piece> pieces;
+  std::vector<int32_t> cmerges;
+  int cpartials = 0;
+  for (const Tile& t : tl) {
+    const int64_t n = t.prefix / csplit + 1;  // last piece starts at or before the prefix end
+    if (n == 1) {
+      pieces.push_back({t.row, t.qb, t.qe, 0, (int32_t)t.keys, -1});
+      continue;
+    }
+    cmerges.insert(cmerges.end(), {t.row, t.qb, t.qe, cpartials, (int32_t)n, 0, 0, 0});
+    for (int64_t k = 0; k < n; ++k) {
+      const int64_t kb = k * csplit, ke = (k + 1 < n) ? (k + 1) * csplit : t.keys;
+      pieces.push_back({t.row, t.qb, t.qe, (int32_t)kb, (int32_t)ke, cpartials + (int32_t)k});
+    }
+    cpartials += (int)n;
+  }
+  // longest key range first, so the last workgroups to start are short ones
+  std::stable_sort(pieces.begin(), pieces.end(),
+                   [](const Piece& x, const Piece& y) { return x.ke - x.kb > y.ke - y.kb; });
+  for (const Piece& p : pieces) tiles.insert(tiles.end(), {p.row, p.qb, p.qe, p.kb, p.ke, p.slot, 0, 0});
 
   out->counts.num_decode_splits = (int32_t)(dsplits.size() / CPA_DECODE_SPLIT_WORDS);
   out->counts.num_decode_merges = (int32_t)(dmerges.size() / CPA_DECODE_MERGE_WORDS);
   out->counts.num_chunk_tiles = (int32_t)(tiles.size() / CPA_CHUNK_TILE_WORDS);
-  out->counts.num_partials = partials;
-  const int64_t words = (int64_t)dsplits.size() + dmerges.size() + tiles.size();
+  out->counts.num_chunk_merges = (int32_t)(cmerges.size() / CPA_CHUNK_MERGE_WORDS);
+  out->counts.num_decode_partials = partials;
+  out->counts.num_chunk_partials = cpartials;
+  const int64_t words = (int64_t)dsplits.size() + dmerges.size() + tiles.size() + cmerges.size();
+  if (words > INT32_MAX) return CPA_ERR_CAPACITY;
   out->plan_words = (int32_t)words;
   if (out->plan) {
     if (words > out->plan_capacity) return CPA_ERR_CAPACITY;
     int32_t* w = out->plan;
-    std::memcpy(w, dsplits.data(), dsplits.size() * sizeof(int32_t));
-    w += dsplits.size();
-    std::memcpy(w, dmerges.data(), dmerges.size() * sizeof(int32_t));
-    w += dmerges.size();
-    std::memcpy(w, tiles.data(), tiles.size() * sizeof(int32_t));
+    for (const std::vector<int32_t>* sec : {&dsplits, &dmerges, &tiles, &cmerges}) {
+      std::memcpy(w, sec->data(), sec->size() * sizeof(int32_t));
+      w += sec->size();
+    }
   }
   return CPA_OK;
 }
 
-extern "C" size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int head_dim) {
-  if (!counts || counts->num_partials <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  size_t bytes = (size_t)counts->num_partials * (size_t)num_q_heads * (size_t)(head_dim + 2) * 4u;
-  return (bytes + 255) / 256 * 256;
+extern "C" size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads,
+                                     int num_kv_heads, int head_dim) {
+  if (!counts || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  const cpa::WorkspaceLayout w =
+      cpa::workspace_layout(counts->num_decode_partials, counts->num_chunk_partials, num_q_heads,
+                            num_kv_heads, head_dim);
+  return w.total;
 }
 
 extern "C" const char* cpa_status_string(int status) {

@@ -25,6 +25,16 @@
 // next tile's global loads are in flight while the current one is computed.
 // Only tiles that reach past the first query's last visible key apply the
 // causal mask.
+//
+// A work item may cover only a piece [kv_begin, kv_end) of its tile's keys
+// (a long, fully visible prefix is cut into pieces so small chunks still fill
+// the GPU); such a piece writes its unnormalised fp32 output, running max and
+// sum, and chunk_merge_kernel combines the pieces:
+//   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
+// The running max used as the exponent reference is only moved when a tile's
+// max exceeds it by more than 2^8, so the 16-64 accumulator rescale almost
+// never runs; the sums stay exact because numerator and denominator share the
+// reference, and each probability stays below 2^8.
 
 #include "device.h"
 #include "internal.h"
@@ -38,7 +48,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials part) {
   constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;               // 32-row d blocks of O^T
   constexpr int KSTR = D + 8;              // padded K row in LDS (elements)
@@ -52,11 +62,12 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
 
   const int item = xcd_remap(blockIdx.x, num_tiles * num_kv_heads);
   const int g = item / num_tiles;
-  const int4 te = reinterpret_cast<const int4*>(tiles)[item % num_tiles];
-  const int row = te.x, qb = te.y, qe = te.z;
+  const int4* tp = reinterpret_cast<const int4*>(tiles) + 2 * (item % num_tiles);
+  const int4 te0 = tp[0], te1 = tp[1];
+  const int row = te0.x, qb = te0.y, qe = te0.z, kv_begin = te0.w;
+  const int kv_end = te1.x, slot = te1.y;  // kv_end <= context + qe
   const int c = ctx[row];
   const int t0 = qsl[row];
-  const int kv_end = c + qe;  // keys visible to the tile's last query
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ncol = lane & 31, half = lane >> 5;
@@ -89,10 +100,29 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
 
   const int32_t* btrow = bt + (int64_t)row * bt_stride;
+  const int kt0 = kv_begin / kKvTile;
   const int n_kv = (kv_end + kKvTile - 1) / kKvTile;
 
   uint4 kreg[PER_THREAD], vreg[PER_THREAD];
-  auto load_tile = [&](int kt) {
+  // page ids of the pages this thread stages, read one tile ahead of their use
+  auto load_ids = [&](int kt, int (&ids)[PER_THREAD]) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int pg = kt * 4 + (tid + 256 * i) / (PAGE / 8);
+      ids[i] = pg * kBlock < kv_end ? btrow[pg] : 0;
+    }
+  };
+  auto load_tile = [&](int kt, const int (&ids)[PER_THREAD]) {
+    if ((kt + 1) * kKvTile <= kv_end) {  // whole tile below the end: no checks
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        const int cidx = tid + 256 * i;
+        const int64_t base = ((int64_t)ids[i] * num_kv_heads + g) * PAGE + (cidx % (PAGE / 8)) * 8;
+        kreg[i] = *reinterpret_cast<const uint4*>(k_cache + base);
+        vreg[i] = *reinterpret_cast<const uint4*>(v_cache + base);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int cidx = tid + 256 * i;
@@ -101,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       const int pg = kt * 4 + kp;
       const int key0 = pg * kBlock;
       if (key0 < kv_end) {
-        const int64_t base = ((int64_t)btrow[pg] * num_kv_heads + g) * PAGE;
+        const int64_t base = ((int64_t)ids[i] * num_kv_heads + g) * PAGE;
         kreg[i] = *reinterpret_cast<const uint4*>(k_cache + base + w * 8);
         uint4 v = *reinterpret_cast<const uint4*>(v_cache + base + w * 8);
         // V piece w covers d = w/2 and page slots 8*(w%2)..+8; zero slots
@@ -131,18 +161,27 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       const int kp = cidx / (PAGE / 8);
       const int w = cidx % (PAGE / 8);
       const int key = kp * kBlock + w / (D / 8);
-      const int part = w % (D / 8);
-      *reinterpret_cast<uint4*>(&k_lds[key * KSTR + part * 8]) = kreg[i];
-      *reinterpret_cast<uint4*>(&v_lds[kp * PAGE + w * 8]) = vreg[i];
+      const int dpiece = w % (D / 8);
+      *reinterpret_cast<uint4*>(&k_lds[key * KSTR + dpiece * 8]) = kreg[i];
+      // V^T row d = w/2 keeps its two 8-key halves swapped when bit 3 of d is
+      // set, so 16 lanes reading half 0 of rows d..d+15 hit distinct banks
+      const int d = w >> 1, hh = (w & 1) ^ ((d >> 3) & 1);
+      *reinterpret_cast<uint4*>(&v_lds[kp * PAGE + d * kBlock + 8 * hh]) = vreg[i];
     }
   };
 
-  load_tile(0);
-  for (int kt = 0; kt < n_kv; ++kt) {
+  int ids[PER_THREAD];
+  load_ids(kt0, ids);
+  load_tile(kt0, ids);
+  load_ids(min(kt0 + 1, n_kv - 1), ids);
+  for (int kt = kt0; kt < n_kv; ++kt) {
     __syncthreads();  // every wave is done with the previous tile
     store_tile();
     __syncthreads();
-    if (kt + 1 < n_kv) load_tile(kt + 1);
+    // next tile's K/V (the last tile again at the end: an L2 hit that keeps
+    // the loads unconditional) and the page ids of the tile after it
+    load_tile(min(kt + 1, n_kv - 1), ids);
+    load_ids(min(kt + 2, n_kv - 1), ids);
 
     // S^T = K Q^T for two 32-key blocks
     f32x16_t s[2];
@@ -177,7 +216,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
     mx = fmaxf(mx, xor_lane(mx, 32));
-    const float mn = fmaxf(m, mx);
+    // move the reference max only when this tile exceeds it by more than 2^8
+    // (always on a row's first tile, where m is -inf)
+    const bool grow = (mx - m) * scale_log2 > 8.f;
+    const float mn = grow ? mx : m;
     const float alpha = fast_exp2((m - mn) * scale_log2);
     m = mn;
     const float msc = mn * scale_log2;
@@ -196,18 +238,21 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
     }
     lsum = lsum * alpha + psum;
+    if (__any(grow)) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
 
     // O^T += V^T P^T, one page (16 keys) per MFMA
+    const int vh = half ^ ((ncol >> 3) & 1);  // the swizzled half holding keys 8*half..
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kp = 0; kp < 4; ++kp) {
         const uint4 a =
-            *reinterpret_cast<const uint4*>(&v_lds[kp * PAGE + (32 * db + ncol) * kBlock + 8 * half]);
+            *reinterpret_cast<const uint4*>(&v_lds[kp * PAGE + (32 * db + ncol) * kBlock + 8 * vh]);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                         __builtin_bit_cast(bf16x8_t, pb[kp]),
                                                         o[db], 0, 0, 0);
@@ -215,7 +260,23 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   }
 
   lsum += xor_lane(lsum, 32);
-  if (row_ok) {
+  if (row_ok && slot >= 0) {
+    // one piece of a split tile: unnormalised partial for chunk_merge_kernel
+    const int64_t pr = ((int64_t)slot * num_kv_heads + g) * kChunkRows + r;
+    float* acc = part.acc + pr * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * half;
+        *reinterpret_cast<float4*>(acc + d) =
+            make_float4(o[db][4 * g4 + 0], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
+      }
+    if (half == 0) {
+      part.m[pr] = m * scale_log2;
+      part.l[pr] = lsum;
+    }
+  } else if (row_ok) {
     const float inv = 1.f / lsum;
     uint16_t* orow = out + ((int64_t)(t0 + j) * num_q_heads + hq) * D;
 #pragma unroll
@@ -233,31 +294,107 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   }
 }
 
+// Combine the pieces of split chunk tiles.  A workgroup takes RPW rows of
+// one (merge entry, KV head); each row is handled by LPR = D/4 lanes, each
+// owning 4 consecutive d values, so a partial row is one contiguous sweep.
+// The lanes of a row read the pieces' max and sum in parallel (one piece per
+// lane), then every lane sums the pieces' fp32 partials for its 4 values
+// with up to 8 loads in flight.
+template <int D, int G>
+__global__ __launch_bounds__(256) void chunk_merge_kernel(
+    const int32_t* __restrict__ merges, const int32_t* __restrict__ qsl, int num_q_heads,
+    int num_kv_heads, Partials part, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int LPR = D / 4;             // lanes per row
+  constexpr int RPW = 256 / LPR;         // rows per workgroup
+  constexpr int RG = kChunkRows / RPW;   // workgroups per (merge entry, KV head)
+  const int rg = blockIdx.x % RG;
+  const int g = (blockIdx.x / RG) % num_kv_heads;
+  const int4* ep = reinterpret_cast<const int4*>(merges) + 2 * (blockIdx.x / (RG * num_kv_heads));
+  const int4 e0 = ep[0], e1 = ep[1];
+  const int row = e0.x, qb = e0.y, qe = e0.z, first = e0.w, n = e1.x;
+  const int li = threadIdx.x % LPR;
+  const int r = rg * RPW + threadIdx.x / LPR;
+  const int j = qb + r / G;
+  if (j >= qe) return;  // past the chunk end (no barrier below)
+  const int64_t stride = (int64_t)num_kv_heads * kChunkRows;  // rows between consecutive slots
+  const int64_t base = ((int64_t)first * num_kv_heads + g) * kChunkRows + r;
+
+  float M = neg_inf();
+  for (int i = li; i < n; i += LPR) M = fmaxf(M, part.m[base + i * stride]);
+#pragma unroll
+  for (int k = 1; k < LPR; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, LPR));
+  float L = 0.f;
+  for (int i = li; i < n; i += LPR) L += part.l[base + i * stride] * fast_exp2(part.m[base + i * stride] - M);
+#pragma unroll
+  for (int k = 1; k < LPR; k <<= 1) L += __shfl_xor(L, k, LPR);
+
+  const int d = 4 * li;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < n; i0 += LPR) {
+    const float wl = (i0 + li < n) ? fast_exp2(part.m[base + (i0 + li) * stride] - M) : 0.f;
+    const int cnt = min(LPR, n - i0);
+#pragma unroll 8
+    for (int k = 0; k < cnt; ++k) {
+      const float w = __shfl(wl, k, LPR);
+      const float4 a = *reinterpret_cast<const float4*>(part.acc + (base + (i0 + k) * stride) * D + d);
+      o.x += w * a.x; o.y += w * a.y; o.z += w * a.z; o.w += w * a.w;
+    }
+  }
+  const float inv = 1.f / L;
+  const int hq = g * G + (r % G);
+  const int t0 = qsl[row];
+  uint2 v;
+  v.x = pack_bf16x2(o.x * inv, o.y * inv);
+  v.y = pack_bf16x2(o.z * inv, o.w * inv);
+  *reinterpret_cast<uint2*>(out + ((int64_t)(t0 + j) * num_q_heads + hq) * D + d) = v;
+  if (lse && li == 0) lse[(int64_t)(t0 + j) * num_q_heads + hq] = (M + __log2f(L)) * kLn2;
+}
+
 template <int D, int G>
 static void launch_chunk_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
                            const int32_t* tiles, int num_tiles, int hq, int hkv, float sl2,
-                           void* out, float* lse, hipStream_t stream) {
+                           void* out, float* lse, Partials part, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_kernel<D, G>), dim3(num_tiles * hkv), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), bt, bt_stride, qsl, ctx, tiles, num_tiles,
-                     hq, hkv, sl2, static_cast<uint16_t*>(out), lse);
+                     hq, hkv, sl2, static_cast<uint16_t*>(out), lse, part);
 }
 
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-                        int head_dim, float scale_log2, void* out, float* lse, hipStream_t stream) {
+                        int head_dim, float scale_log2, void* out, float* lse, Partials part,
+                        hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
 #define CPA_CHK(DD, GG)                                                                        \
   if (head_dim == DD && G == GG) {                                                              \
     launch_chunk_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,      \
-                           num_q_heads, num_kv_heads, scale_log2, out, lse, stream);            \
+                           num_q_heads, num_kv_heads, scale_log2, out, lse, part, stream);      \
     return hipGetLastError();                                                                   \
   }
   CPA_CHK(128, 1) CPA_CHK(128, 2) CPA_CHK(128, 4) CPA_CHK(128, 8)
   CPA_CHK(64, 1) CPA_CHK(64, 2) CPA_CHK(64, 4) CPA_CHK(64, 8)
 #undef CPA_CHK
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_merge(const int32_t* merges, int num_merges, const int32_t* qsl,
+                              int num_q_heads, int num_kv_heads, int head_dim, Partials part,
+                              void* out, float* lse, hipStream_t stream) {
+  const int G = num_q_heads / num_kv_heads;
+  const int groups = kChunkRows / (256 / (head_dim / 4));
+  dim3 grid(num_merges * num_kv_heads * groups), block(256);
+  auto* o = static_cast<uint16_t*>(out);
+#define CPA_CMG(DD, GG)                                                                        \
+  if (head_dim == DD && G == GG) {                                                              \
+    hipLaunchKernelGGL((chunk_merge_kernel<DD, GG>), grid, block, 0, stream, merges, qsl,       \
+                       num_q_heads, num_kv_heads, part, o, lse);                                \
+    return hipGetLastError();                                                                   \
+  }
+  CPA_CMG(128, 1) CPA_CMG(128, 2) CPA_CMG(128, 4) CPA_CMG(128, 8)
+  CPA_CMG(64, 1) CPA_CMG(64, 2) CPA_CMG(64, 4) CPA_CMG(64, 8)
+#undef CPA_CMG
   return hipErrorInvalidValue;
 }
 

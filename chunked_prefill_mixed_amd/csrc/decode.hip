@@ -8,10 +8,10 @@
 //
 // One wave per (key split, KV head).  All G query heads that share the KV
 // head are served by the one read of each 16-token page.
-//   K page [16][D]: lane l owns key l/4 and the 8-wide d pieces
-//     (l%4)*8 + 32j; the wave's four 16-byte loads per lane read 64-byte
-//     runs of each key row.  Scores: v_dot2_f32_bf16 over the lane's d
-//     pieces, then a 2-step DPP sum inside each quad.
+//   K page [16][D]: lane l owns keys l/8 and l/8 + 8 and the 8-wide d
+//     pieces (l%8)*8 + 64j; each 16-byte load instruction of the wave reads
+//     8 whole 128-byte lines (8 lanes per key row).  Scores: v_dot2_f32_bf16
+//     over the lane's d pieces, then a 3-step DPP sum over the row's 8 lanes.
 //   V page [D][16] (transposed): lane l owns d = 32j + l/2 and keys
 //     8*(l%2)..+8, one contiguous 16-byte load per j; the whole wave reads
 //     the 4 KiB page in 1 KiB contiguous sweeps.  P*V: v_dot2 over the
@@ -26,33 +26,54 @@
 #include "internal.h"
 #include "tiles.h"
 
+#ifndef CPA_DECODE_WAVES_PER_WG
+#define CPA_DECODE_WAVES_PER_WG 4   // independent (split, KV head) items per workgroup
+#endif
+
 namespace cpa {
 
+constexpr int kDecodeWaves = CPA_DECODE_WAVES_PER_WG;
+
+// Orders one wave's LDS writes before its own later LDS reads by other lanes
+// (LDS executes a wave's operations in order; this stops the compiler from
+// moving them and makes the writes visible at wavefront scope).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(64) void decode_kernel(
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ splits, int num_q_heads,
-    int num_kv_heads, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    Partials ws) {
-  constexpr int J = D / 32;  // 16-byte pieces per lane per page, for K and for V
-  __shared__ __align__(16) uint16_t pbuf[2][G][kBlock];
+    int num_kv_heads, int num_items, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, Partials ws) {
+  constexpr int J = D / 32;   // 16-byte V pieces per lane per page
+  constexpr int JK = D / 64;  // 16-byte K pieces per lane per key (2 keys per lane)
+  __shared__ __align__(16) uint16_t pbuf_all[kDecodeWaves][2][G][kBlock];
 
-  const int lane = threadIdx.x;
-  const int g = blockIdx.x % num_kv_heads;
-  const int sp = blockIdx.x / num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int item = blockIdx.x * kDecodeWaves + wave;
+  if (item >= num_items) return;  // whole wave; no workgroup barrier below
+  auto& pbuf = pbuf_all[wave];
+  const int g = item % num_kv_heads;
+  const int sp = item / num_kv_heads;
   const int4 e = reinterpret_cast<const int4*>(splits)[sp];
   const int row = e.x, kv_begin = e.y, kv_end = e.z, slot = e.w;
-  const int t = qsl[row];
-  const int kk = lane >> 2, qd = lane & 3, par = lane & 1;
+  // decode rows come first and hold one token each, so row s is packed token s
+  const int t = row;
+  (void)qsl;
+  const int kg = lane >> 3, dp = lane & 7, par = lane & 1;
 
-  uint4 qf[G][J];
+  uint4 qf[G][JK];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int j = 0; j < J; ++j)
+    for (int j = 0; j < JK; ++j)
       qf[h][j] = *reinterpret_cast<const uint4*>(
-          q + ((int64_t)t * num_q_heads + g * G + h) * D + qd * 8 + 32 * j);
+          q + ((int64_t)t * num_q_heads + g * G + h) * D + dp * 8 + 64 * j);
 
   float m[G], lsum[G], acc[G][J];
 #pragma unroll
@@ -64,39 +85,71 @@ __global__ __launch_bounds__(64) void decode_kernel(
   }
 
   const int32_t* btrow = bt + (int64_t)row * bt_stride;
-  const int pg0 = kv_begin / kBlock, pg1 = (kv_end + kBlock - 1) / kBlock;
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const int buf = (pg - pg0) & 1;
-    const int64_t page = ((int64_t)btrow[pg] * num_kv_heads + g) * (kBlock * D);
-    uint4 kf[J], vf[J];
+  // a split spans at most 64 pages (the planner guarantees it): one coalesced
+  // load of its page ids, then v_readlane per page
+  const int pg0 = kv_begin / kBlock, npages = (kv_end + kBlock - 1) / kBlock - pg0;
+  const int my_blk = lane < npages ? btrow[pg0 + lane] : 0;
+  auto page_base = [&](int i) -> int64_t {
+    const int blk = __builtin_amdgcn_readlane(my_blk, i);
+    return ((int64_t)blk * num_kv_heads + g) * (kBlock * D);
+  };
+  // per-lane offsets inside a (page, KV head) piece, in 16-byte units; the
+  // page base is wave-uniform, so every load is scalar base + fixed 32-bit
+  // lane offset and no address register is rewritten per page
+  const uint32_t koff = (uint32_t)(kg * D + dp * 8) / 8;
+  const uint32_t voff = (uint32_t)lane;
+  // two register sets, used in turn: while one page is computed the other's
+  // loads are in flight, and each compute waits only for its own page
+  uint4 ka[2 * JK], va[J], kb[2 * JK], vb[J];
+  auto load_page = [&](int64_t page, uint4 (&kd)[2 * JK], uint4 (&vd)[J]) {
+    const uint4* kp = reinterpret_cast<const uint4*>(k_cache + page);
+    const uint4* vp = reinterpret_cast<const uint4*>(v_cache + page);
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      kf[j] = *reinterpret_cast<const uint4*>(k_cache + page + kk * D + qd * 8 + 32 * j);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      vf[j] = *reinterpret_cast<const uint4*>(v_cache + page + j * 512 + lane * 8);
-
-    const bool valid = pg * kBlock + kk < kv_end;
+      for (int j = 0; j < JK; ++j) kd[ks * JK + j] = kp[koff + (8 * ks * D + 64 * j) / 8];
+#pragma unroll
+    for (int j = 0; j < J; ++j) vd[j] = vp[voff + j * 64];
+  };
+  auto compute_page = [&](int i, uint4 (&kc)[2 * JK], uint4 (&vc)[J]) {
+    const int pg = pg0 + i;
+    const int buf = i & 1;
+    const bool valid0 = pg * kBlock + kg < kv_end;
+    const bool valid1 = pg * kBlock + kg + 8 < kv_end;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float a = 0.f;
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < J; ++j) a = dot8_bf16(qf[h][j], kf[j], a);
-      a += dpp<kQuadXor1>(a);
-      a += dpp<kQuadXor2>(a);
-      const float s = valid ? a : neg_inf();
-      float mx = fmaxf(s, dpp<kRowHalfMirror>(s));
+      for (int j = 0; j < JK; ++j) {
+        a0 = dot8_bf16(qf[h][j], kc[j], a0);
+        a1 = dot8_bf16(qf[h][j], kc[JK + j], a1);
+      }
+      a0 += dpp<kQuadXor1>(a0);
+      a1 += dpp<kQuadXor1>(a1);
+      a0 += dpp<kQuadXor2>(a0);
+      a1 += dpp<kQuadXor2>(a1);
+      a0 += dpp<kRowHalfMirror>(a0);
+      a1 += dpp<kRowHalfMirror>(a1);
+      const float s0 = valid0 ? a0 : neg_inf();
+      const float s1 = valid1 ? a1 : neg_inf();
+      float mx = fmaxf(s0, s1);
       mx = fmaxf(mx, dpp<kRowMirror>(mx));
       mx = fmaxf(mx, xor_lane(mx, 16));
       mx = fmaxf(mx, xor_lane(mx, 32));
       const float mn = fmaxf(m[h], mx);
       const float alpha = fast_exp2((m[h] - mn) * scale_log2);
       m[h] = mn;
-      const float p = fast_exp2((s - mn) * scale_log2);
-      lsum[h] = lsum[h] * alpha + (qd == 0 ? p : 0.f);
+      const float p0 = fast_exp2((s0 - mn) * scale_log2);
+      const float p1 = fast_exp2((s1 - mn) * scale_log2);
+      lsum[h] = lsum[h] * alpha + (dp == 0 ? p0 + p1 : 0.f);
 #pragma unroll
       for (int j = 0; j < J; ++j) acc[h][j] *= alpha;
-      if (qd == (h & 3)) pbuf[buf][h][kk] = to_bf16(p);
+      // the row's 8 lanes hold the same two scores; lane dp publishes value
+      // dp, dp+8, ... of the (key slot, head) pairs
+#pragma unroll
+      for (int v = 0; v < 2 * G; v += 8)
+        if (v + dp < 2 * G && (v + dp) % G == h)
+          pbuf[buf][h][kg + 8 * ((v + dp) / G)] = to_bf16((v + dp) / G ? p1 : p0);
     }
     // keys past the split's end in its last page: their V slots may hold
     // anything (even NaN); zero them so 0 * V stays 0
@@ -104,23 +157,37 @@ __global__ __launch_bounds__(64) void decode_kernel(
     if (nvalid < 8) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        uint32_t w[4] = {vf[j].x, vf[j].y, vf[j].z, vf[j].w};
+        uint32_t w[4] = {vc[j].x, vc[j].y, vc[j].z, vc[j].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t keep_lo = (2 * i < nvalid) ? 0xFFFFu : 0u;
-          const uint32_t keep_hi = (2 * i + 1 < nvalid) ? 0xFFFF0000u : 0u;
-          w[i] &= (keep_lo | keep_hi);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t keep_lo = (2 * e2 < nvalid) ? 0xFFFFu : 0u;
+          const uint32_t keep_hi = (2 * e2 + 1 < nvalid) ? 0xFFFF0000u : 0u;
+          w[e2] &= (keep_lo | keep_hi);
         }
-        vf[j] = make_uint4(w[0], w[1], w[2], w[3]);
+        vc[j] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const uint4 pp = *reinterpret_cast<const uint4*>(&pbuf[buf][h][8 * par]);
 #pragma unroll
-      for (int j = 0; j < J; ++j) acc[h][j] = dot8_bf16(pp, vf[j], acc[h][j]);
+      for (int j = 0; j < J; ++j) acc[h][j] = dot8_bf16(pp, vc[j], acc[h][j]);
     }
+  };
+
+  // pages in pairs with no early exit: for an odd count the pair's second
+  // page is past the split end, every key of it is masked (p = 0, the
+  // running max and sums are unchanged) and its loads re-read the last page
+  // (an L2 hit), which keeps the loop free of branches around the loads
+  load_page(page_base(0), ka, va);
+  const int npairs = (npages + 1) / 2;
+  for (int ip = 0; ip < npairs; ++ip) {
+    const int i = 2 * ip;
+    load_page(page_base(min(i + 1, npages - 1)), kb, vb);
+    compute_page(i, ka, va);
+    load_page(page_base(min(i + 2, npages - 1)), ka, va);
+    compute_page(i + 1, kb, vb);
   }
 
 #pragma unroll
@@ -150,26 +217,43 @@ __global__ __launch_bounds__(64) void decode_kernel(
   }
 }
 
+// Combine the splits of a decode row: one wave per (row, query head).  The
+// lanes read the splits' max and sum in parallel; each lane then owns D/64
+// output dimensions and sums the splits' fp32 partials for them.
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const int32_t* __restrict__ merges,
-                                                  const int32_t* __restrict__ qsl, int num_q_heads,
-                                                  Partials ws, uint16_t* __restrict__ out,
-                                                  float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void merge_kernel(const int32_t* __restrict__ merges,
+                                                   const int32_t* __restrict__ qsl, int num_q_heads,
+                                                   Partials ws, uint16_t* __restrict__ out,
+                                                   float* __restrict__ lse) {
+  constexpr int PER = D / 64;
   const int4 e = reinterpret_cast<const int4*>(merges)[blockIdx.x];
   const int row = e.x, first = e.y, n = e.z;
-  const int h = blockIdx.y, d = threadIdx.x;
+  const int h = blockIdx.y, lane = threadIdx.x;
   float M = neg_inf();
-  for (int i = 0; i < n; ++i) M = fmaxf(M, ws.m[(int64_t)(first + i) * num_q_heads + h]);
-  float L = 0.f, o = 0.f;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, ws.m[(int64_t)(first + i) * num_q_heads + h]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int i = lane; i < n; i += 64) {
+    const int64_t ph = (int64_t)(first + i) * num_q_heads + h;
+    L += ws.l[ph] * fast_exp2(ws.m[ph] - M);
+  }
+  L = wave_sum(L);
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+#pragma unroll 4
   for (int i = 0; i < n; ++i) {
     const int64_t ph = (int64_t)(first + i) * num_q_heads + h;
     const float w = fast_exp2(ws.m[ph] - M);
-    L += ws.l[ph] * w;
-    o += ws.acc[ph * D + d] * w;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] += w * ws.acc[ph * D + lane + 64 * k];
   }
   const int t = qsl[row];
-  out[((int64_t)t * num_q_heads + h) * D + d] = to_bf16(o / L);
-  if (lse && d == 0) lse[(int64_t)t * num_q_heads + h] = (M + __log2f(L)) * kLn2;
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    out[((int64_t)t * num_q_heads + h) * D + lane + 64 * k] = to_bf16(o[k] * inv);
+  if (lse && lane == 0) lse[(int64_t)t * num_q_heads + h] = (M + __log2f(L)) * kLn2;
 }
 
 template <int D, int G>
@@ -177,10 +261,12 @@ static void launch_decode_t(const void* q, const void* kc, const void* vc, const
                             int bt_stride, const int32_t* qsl, const int32_t* splits,
                             int num_splits, int hq, int hkv, float sl2, void* out, float* lse,
                             Partials ws, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(num_splits * hkv), dim3(64), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), bt, bt_stride, qsl, splits, hq, hkv, sl2,
-                     static_cast<uint16_t*>(out), lse, ws);
+  const int items = num_splits * hkv;
+  hipLaunchKernelGGL((decode_kernel<D, G>), dim3((items + kDecodeWaves - 1) / kDecodeWaves),
+                     dim3(64 * kDecodeWaves), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,
+                     bt_stride, qsl, splits, hq, hkv, items, sl2, static_cast<uint16_t*>(out), lse,
+                     ws);
 }
 
 hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -205,7 +291,7 @@ hipError_t launch_merge(const int32_t* merges, int num_merges, const int32_t* qs
                         int head_dim, Partials ws, void* out, float* lse, hipStream_t stream) {
   dim3 grid(num_merges, num_q_heads);
   if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, merges, qsl, num_q_heads, ws,
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, stream, merges, qsl, num_q_heads, ws,
                        static_cast<uint16_t*>(out), lse);
   else
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, merges, qsl, num_q_heads, ws,

@@ -58,6 +58,16 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  x = fmaxf(x, xor_lane(x, 16));
+  x = fmaxf(x, xor_lane(x, 32));
+  return x;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   x += dpp<kQuadXor1>(x);
   x += dpp<kQuadXor2>(x);

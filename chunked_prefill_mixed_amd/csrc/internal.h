@@ -11,8 +11,8 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* qs
                          int num_tokens, int num_kv_heads, int head_dim, void* k_cache,
                          void* v_cache, hipStream_t stream);
 
-// Workspace of fp32 partial results: acc [P][Hq][D], then m [P][Hq] (log2
-// units of the scaled score), then l [P][Hq].
+// fp32 partial results of split work items (see WorkspaceLayout in tiles.h);
+// m is in log2 units of the scaled score.
 struct Partials {
   float* acc;
   float* m;
@@ -31,6 +31,11 @@ hipError_t launch_merge(const int32_t* merges, int num_merges, const int32_t* qs
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-                        int head_dim, float scale_log2, void* out, float* lse, hipStream_t stream);
+                        int head_dim, float scale_log2, void* out, float* lse, Partials part,
+                        hipStream_t stream);
+
+hipError_t launch_chunk_merge(const int32_t* merges, int num_merges, const int32_t* qsl,
+                              int num_q_heads, int num_kv_heads, int head_dim, Partials part,
+                              void* out, float* lse, hipStream_t stream);
 
 }  // namespace cpa

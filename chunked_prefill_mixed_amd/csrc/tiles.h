@@ -6,7 +6,13 @@ namespace cpa {
 constexpr int kBlock = 16;          // tokens per KV page
 constexpr int kChunkRows = 128;     // (token, head) query rows per chunk workgroup: 4 waves x 32
 constexpr int kKvTile = 64;         // keys per LDS-staged K/V tile in the chunk kernel (4 pages)
-constexpr int kDecodeWavesTarget = 4096;  // decode waves to aim for when sizing splits
+#ifndef CPA_DECODE_WAVES_TARGET
+#define CPA_DECODE_WAVES_TARGET 4096
+#endif
+constexpr int kDecodeWavesTarget = CPA_DECODE_WAVES_TARGET;  // decode waves to aim for
+constexpr int kDecodeMaxSplit = 64 * kBlock;  // a decode split spans at most 64 pages
+constexpr int kChunkWgTarget = 1024;      // chunk workgroups to aim for when sizing KV splits
+constexpr int kChunkMinSplit = 256;       // fewest prefix keys worth a separate chunk piece
 
 // Query tokens one chunk workgroup covers when G query heads share a KV head.
 inline int chunk_tile_tokens(int group) { return kChunkRows / group; }
@@ -15,5 +21,36 @@ inline bool supported_group(int group) {
   return group == 1 || group == 2 || group == 4 || group == 8;
 }
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+}  // namespace cpa
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cpa {
+
+// Byte offsets of the fp32 partial-result regions inside the caller's
+// workspace.  Decode slot: acc [Hq][D], m [Hq], l [Hq].  Chunk slot: acc
+// [Hkv][128 rows][D], m and l [Hkv][128].  Max values are stored in log2
+// units of the scaled score.
+struct WorkspaceLayout {
+  size_t dec_acc, dec_m, dec_l, chk_acc, chk_m, chk_l, total;
+};
+
+inline WorkspaceLayout workspace_layout(int64_t dec_slots, int64_t chk_slots, int num_q_heads,
+                                        int num_kv_heads, int head_dim) {
+  auto up = [](int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); };
+  WorkspaceLayout w;
+  size_t at = 0;
+  const int64_t dr = dec_slots * num_q_heads, cr = chk_slots * num_kv_heads * kChunkRows;
+  w.dec_acc = at; at += up(dr * head_dim * 4);
+  w.dec_m = at;   at += up(dr * 4);
+  w.dec_l = at;   at += up(dr * 4);
+  w.chk_acc = at; at += up(cr * head_dim * 4);
+  w.chk_m = at;   at += up(cr * 4);
+  w.chk_l = at;   at += up(cr * 4);
+  w.total = at;
+  return w;
+}
 
 }  // namespace cpa

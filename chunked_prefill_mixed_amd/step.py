@@ -27,14 +27,15 @@ def bf16_to_bits(t) -> np.ndarray:
 class DeviceStep:
     """One step of a workload, resident on the GPU."""
 
-    def __init__(self, w, device="cuda", decode_split_tokens=0, validate=True, with_lse=True):
+    def __init__(self, w, device="cuda", decode_split_tokens=0, chunk_split_tokens=0,
+                 validate=True, with_lse=True):
         import torch
         self.w = w
         self.device = device
         self.meta = cpa.cpa_build_metadata(
             w.requests, token_budget=w.token_budget, long_prefill_cap=w.long_prefill_cap,
             num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-            decode_split_tokens=decode_split_tokens,
+            decode_split_tokens=decode_split_tokens, chunk_split_tokens=chunk_split_tokens,
             host_block_table=w.block_table if validate else None, num_blocks=w.num_blocks)
         m = self.meta
         self.num_tokens = T = m["num_tokens"]
@@ -57,7 +58,7 @@ class DeviceStep:
         self.out = torch.empty((T, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=device)
         self.lse = (torch.empty((T, w.num_q_heads), dtype=torch.float32, device=device)
                     if with_lse else None)
-        ws = cpa.cpa_workspace_size(self.counts, w.num_q_heads, w.head_dim)
+        ws = cpa.cpa_workspace_size(self.counts, w.num_q_heads, w.num_kv_heads, w.head_dim)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device) if ws else None
         self.scale = w.scale
 

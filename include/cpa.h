@@ -73,10 +73,12 @@ extern "C" {
 
 #define CPA_BLOCK_SIZE 16
 
-/* Plan entry sizes in int32 words (see cpa_plan_counts_t). */
-#define CPA_DECODE_SPLIT_WORDS 4 /* {row, kv_begin, kv_end, partial slot or -1} */
-#define CPA_DECODE_MERGE_WORDS 4 /* {row, first partial slot, num partials, 0} */
-#define CPA_CHUNK_TILE_WORDS 4   /* {row, q_begin, q_end, 0}  (q_* are chunk-local) */
+/* Plan entry sizes in int32 words (see cpa_plan_counts_t).  q_* are chunk-local
+ * token indices; kv_* are key positions of the row. */
+#define CPA_DECODE_SPLIT_WORDS 4 /* {row, kv_begin, kv_end, decode partial slot or -1} */
+#define CPA_DECODE_MERGE_WORDS 4 /* {row, first decode slot, num slots, 0} */
+#define CPA_CHUNK_TILE_WORDS 8   /* {row, q_begin, q_end, kv_begin, kv_end, chunk slot or -1, 0, 0} */
+#define CPA_CHUNK_MERGE_WORDS 8  /* {row, q_begin, q_end, first chunk slot, num slots, 0, 0, 0} */
 
 /* One queued request, in queue order: running decodes, then prefills first
  * come first served (a continued chunked prompt precedes newer prompts). */
@@ -95,19 +97,25 @@ typedef struct {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t decode_split_tokens; /* keys per decode split, multiple of 16; 0 = chosen by size */
-  int32_t reserved;            /* must be 0 */
+  int32_t decode_split_tokens; /* keys per decode split, multiple of 16, at most 1024;
+                                  0 = chosen by size */
+  int32_t chunk_split_tokens;  /* prefix keys per chunk-tile split, multiple of 64;
+                                  0 = chosen by size; a value above every context = no split */
 } cpa_build_params_t;
 
 /* Counts of the device work plan built by cpa_build_metadata.  The plan is one
- * int32 array: num_decode_splits entries of CPA_DECODE_SPLIT_WORDS, then
- * num_decode_merges entries of CPA_DECODE_MERGE_WORDS, then num_chunk_tiles
- * entries of CPA_CHUNK_TILE_WORDS. */
+ * int32 array, in this order: num_decode_splits entries of
+ * CPA_DECODE_SPLIT_WORDS, num_decode_merges of CPA_DECODE_MERGE_WORDS,
+ * num_chunk_tiles of CPA_CHUNK_TILE_WORDS, num_chunk_merges of
+ * CPA_CHUNK_MERGE_WORDS.  A chunk tile covers 128 (token, query head) rows of
+ * one KV head: 128 / (num_q_heads / num_kv_heads) tokens. */
 typedef struct {
-  int32_t num_decode_splits; /* one wave per (split, KV head) */
-  int32_t num_decode_merges; /* decode rows whose keys were split in several pieces */
-  int32_t num_chunk_tiles;   /* one workgroup per (tile, KV head) */
-  int32_t num_partials;      /* fp32 partial-result slots needed in the workspace */
+  int32_t num_decode_splits;   /* one wave per (split, KV head) */
+  int32_t num_decode_merges;   /* decode rows whose keys were split in several pieces */
+  int32_t num_chunk_tiles;     /* one workgroup per (tile, KV head) */
+  int32_t num_chunk_merges;    /* chunk tiles whose prefix keys were split in several pieces */
+  int32_t num_decode_partials; /* decode partial slots: num_q_heads x (head_dim + 2) fp32 each */
+  int32_t num_chunk_partials;  /* chunk partial slots: num_kv_heads x 128 x (head_dim + 2) fp32 */
 } cpa_plan_counts_t;
 
 /* Host arrays filled by cpa_build_metadata; the caller provides them with the
@@ -153,8 +161,8 @@ typedef struct {
  *
  * Synchronous, pure, host only (no HIP call).  Returns CPA_OK,
  * CPA_ERR_BUDGET (decodes > token_budget), CPA_ERR_INVALID (negative lengths,
- * target_len < num_computed, bad block ids, duplicate slots, nonzero
- * reserved), CPA_ERR_CAPACITY (an output array too small) or
+ * target_len < num_computed, bad block ids, duplicate slots, split sizes that
+ * are not whole pages / KV tiles), CPA_ERR_CAPACITY (an output array too small) or
  * CPA_ERR_UNSUPPORTED (shape outside the supported set).  On error the
  * outputs are unspecified.
  */
@@ -184,10 +192,13 @@ int cpa_append_kv(const void* k_new, const void* v_new, const int32_t* d_query_s
 
 /*
  * cpa_workspace_size -- bytes of device workspace cpa_attention needs for a
- * plan with these counts: num_partials * num_q_heads * (head_dim + 2) * 4
- * (fp32 partial sums plus running max and sum per head), rounded up to 256.
+ * plan with these counts: fp32 partial sums plus the running max and sum of
+ * every split piece, i.e. (num_decode_partials * num_q_heads +
+ * num_chunk_partials * num_kv_heads * 128) * (head_dim + 2) * 4 bytes, each
+ * region rounded up to 256 bytes.  0 when nothing is split.
  */
-size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int head_dim);
+size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int num_kv_heads,
+                          int head_dim);
 
 /*
  * cpa_attention -- attention of every packed query over the paged cache.
@@ -200,12 +211,15 @@ size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int 
  * even); lse[t][h] = log(sum_k exp(scale * <q, K[k]>)) if lse is non-NULL.
  *
  * d_plan is the plan from cpa_build_metadata copied to the device, with its
- * counts in *counts (host pointer).  workspace must hold
- * cpa_workspace_size(counts, ...) bytes (may be NULL when num_partials is 0).
- * The append of this step must already be enqueued on the same stream.
- * seq_lens is read for validation of the plan only on the host side and may
- * be NULL.  Returns CPA_OK, CPA_ERR_UNSUPPORTED, CPA_ERR_CAPACITY (workspace
- * too small), CPA_ERR_INVALID or CPA_ERR_DEVICE.
+ * counts in *counts (host pointer).  Any subset of the plan's sections may be
+ * run by passing counts with the other sections set to 0 and d_plan pointing
+ * at the first section run (the sections are independent, except that a
+ * merge section must run after the splits it merges).  workspace must hold
+ * cpa_workspace_size(counts, ...) bytes (may be NULL when nothing is split);
+ * its contents need no initialisation.  The append of this step must already
+ * be enqueued on the same stream.  d_seq_lens is not read (the plan carries
+ * the key ranges) and may be NULL.  Returns CPA_OK, CPA_ERR_UNSUPPORTED,
+ * CPA_ERR_CAPACITY (workspace too small), CPA_ERR_INVALID or CPA_ERR_DEVICE.
  */
 int cpa_attention(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* d_block_table, int bt_stride, const int32_t* d_query_start_loc,

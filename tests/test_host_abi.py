@@ -79,10 +79,14 @@ def test_builder_matches_oracle_on_configs(lib, config):
             break
 
 
-def check_plan(m, group, split=None):
+def check_plan(m, group):
     """Every decode row's keys are covered exactly once by page-aligned splits;
-    merges list exactly the rows with several splits; chunk tiles cover each
-    chunk row's tokens exactly once, longest key range first."""
+    merges list exactly the rows with several splits.  Every chunk row's
+    tokens are covered by tiles of 128/G tokens; each tile's keys
+    [0, context + q_end) are covered exactly once by pieces whose inner
+    boundaries are 64-key aligned and lie in the fully visible prefix
+    (<= context + q_begin); split tiles have a merge entry; pieces come
+    longest first."""
     sec = cpa.plan_sections(m["plan"], m["counts"])
     nd = m["num_decodes"]
     cover = {s: [] for s in range(nd)}
@@ -92,9 +96,8 @@ def check_plan(m, group, split=None):
         cover[row].append((b, e, slot))
         if slot >= 0:
             slots.append(slot)
-    merged = {}
-    for row, first, n, _ in sec["decode_merges"]:
-        merged[row] = (first, n)
+    merged = {row: (first, n) for row, first, n, _ in sec["decode_merges"]}
+    assert len(merged) == m["counts"].num_decode_merges
     for s in range(nd):
         pieces = sorted(cover[s])
         assert pieces[0][0] == 0 and pieces[-1][1] == m["seq_lens"][s]
@@ -106,21 +109,39 @@ def check_plan(m, group, split=None):
             first, n = merged[s]
             assert n == len(pieces)
             assert sorted(p[2] for p in pieces) == list(range(first, first + n))
-    assert sorted(slots) == list(range(m["counts"].num_partials))
-    tiles = sec["chunk_tiles"]
+    assert sorted(slots) == list(range(m["counts"].num_decode_partials))
+
     tt = 128 // group
-    seen = {}
-    for row, qb, qe, _ in tiles:
+    tiles = {}
+    cslots = []
+    for row, qb, qe, kb, ke, slot, z0, z1 in sec["chunk_tiles"]:
         assert nd <= row < m["num_seqs"] and 0 <= qb < qe <= m["num_scheduled"][row]
-        assert qe - qb <= tt and qb % tt == 0
-        seen.setdefault(row, []).append((qb, qe))
+        assert qe - qb <= tt and qb % tt == 0 and z0 == 0 and z1 == 0
+        tiles.setdefault((row, qb, qe), []).append((kb, ke, slot))
+        if slot >= 0:
+            cslots.append(slot)
+    cmerged = {(row, qb, qe): (first, n) for row, qb, qe, first, n, *_ in sec["chunk_merges"]}
+    assert len(cmerged) == m["counts"].num_chunk_merges
     for s in range(nd, m["num_seqs"]):
-        pieces = sorted(seen[s])
-        assert pieces[0][0] == 0 and pieces[-1][1] == m["num_scheduled"][s]
-        for (a0, b0), (a1, _) in zip(pieces, pieces[1:]):
+        spans = sorted((qb, qe) for (row, qb, qe) in tiles if row == s)
+        assert spans[0][0] == 0 and spans[-1][1] == m["num_scheduled"][s]
+        for (a0, b0), (a1, _) in zip(spans, spans[1:]):
             assert b0 == a1
-    keys = [m["context_lens"][r] + qe for r, _, qe, _ in tiles]
-    assert keys == sorted(keys, reverse=True)
+    for (row, qb, qe), pcs in tiles.items():
+        c = m["context_lens"][row]
+        pcs.sort()
+        assert pcs[0][0] == 0 and pcs[-1][1] == c + qe
+        for (b0, e0, _), (b1, _, _) in zip(pcs, pcs[1:]):
+            assert e0 == b1 and e0 % 64 == 0 and e0 <= c + qb
+        if len(pcs) == 1:
+            assert pcs[0][2] == -1 and (row, qb, qe) not in cmerged
+        else:
+            first, n = cmerged[(row, qb, qe)]
+            assert n == len(pcs)
+            assert sorted(p[2] for p in pcs) == list(range(first, first + n))
+    assert sorted(cslots) == list(range(m["counts"].num_chunk_partials))
+    lens = [ke - kb for _, _, _, kb, ke, *_ in sec["chunk_tiles"]]
+    assert lens == sorted(lens, reverse=True)
 
 
 def users_and_prompt(running, prompt):
@@ -177,7 +198,9 @@ def test_builder_random_mixes_match_oracle(lib):
         D = int(rng.choice([64, 128]))
         Hkv = int(rng.choice([1, 2, 8]))
         split = int(rng.choice([0, 0, 16, 128, 512]))
-        m = same_as_oracle(reqs, budget, cap, Hq=G * Hkv, Hkv=Hkv, D=D, decode_split_tokens=split)
+        csplit = int(rng.choice([0, 0, 64, 256, 1024]))
+        m = same_as_oracle(reqs, budget, cap, Hq=G * Hkv, Hkv=Hkv, D=D, decode_split_tokens=split,
+                           chunk_split_tokens=csplit)
         check_plan(m, G)
 
 
@@ -191,6 +214,8 @@ def test_builder_random_mixes_match_oracle(lib):
     ("heads_not_multiple", cpa.CPA_ERR_UNSUPPORTED),
     ("block_size_32", cpa.CPA_ERR_UNSUPPORTED),
     ("split_not_page_multiple", cpa.CPA_ERR_INVALID),
+    ("split_over_64_pages", cpa.CPA_ERR_INVALID),
+    ("chunk_split_not_tile_multiple", cpa.CPA_ERR_INVALID),
     ("block_table_too_short", cpa.CPA_ERR_INVALID),
     ("block_id_out_of_range", cpa.CPA_ERR_INVALID),
     ("duplicate_slot", cpa.CPA_ERR_INVALID),
@@ -221,6 +246,10 @@ def test_builder_error_paths(lib, case, status):
         kw["block_size"] = 32
     elif case == "split_not_page_multiple":
         kw["decode_split_tokens"] = 24
+    elif case == "split_over_64_pages":
+        kw["decode_split_tokens"] = 1040
+    elif case == "chunk_split_not_tile_multiple":
+        kw["chunk_split_tokens"] = 80
     elif case == "block_table_too_short":
         kw.update(host_block_table=bt[:, :2], num_blocks=10)
     elif case == "block_id_out_of_range":
@@ -253,10 +282,25 @@ def test_builder_valid_block_table_accepted(lib):
 
 
 def test_workspace_size(lib):
-    c = cpa.cpa_plan_counts_t(5, 2, 3, 7)
-    assert cpa.cpa_workspace_size(c, 32, 128) == math.ceil(7 * 32 * 130 * 4 / 256) * 256
-    c0 = cpa.cpa_plan_counts_t(5, 0, 3, 0)
-    assert cpa.cpa_workspace_size(c0, 32, 128) == 0
+    up = lambda b: math.ceil(b / 256) * 256
+    c = cpa.cpa_plan_counts_t(5, 2, 3, 1, 7, 3)
+    want = (up(7 * 32 * 128 * 4) + 2 * up(7 * 32 * 4)
+            + up(3 * 8 * 128 * 128 * 4) + 2 * up(3 * 8 * 128 * 4))
+    assert cpa.cpa_workspace_size(c, 32, 8, 128) == want
+    c0 = cpa.cpa_plan_counts_t(5, 0, 3, 0, 0, 0)
+    assert cpa.cpa_workspace_size(c0, 32, 8, 128) == 0
+
+
+def test_chunk_split_sizes(lib):
+    """A small chunk beside a long prefix is cut into pieces (enough work for
+    the GPU); a large chunk is not."""
+    R = oracle.Request
+    m = build([R(0, 7680, 8192, False)], 480)
+    assert m["counts"].num_chunk_merges == 15 and m["counts"].num_chunk_tiles > 15
+    m = build([R(0, 0, 8192, False)], 8192)
+    assert m["counts"].num_chunk_merges == 0 and m["counts"].num_chunk_tiles == 256
+    m = build([R(0, 7680, 8192, False)], 480, chunk_split_tokens=1 << 30)
+    assert m["counts"].num_chunk_merges == 0
 
 
 def test_empty_step(lib):
