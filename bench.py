@@ -102,8 +102,9 @@ def step_work(meta, Hq, Hkv, D):
 # ---------------------------------------------------------------------------
 
 class Instance:
-    def __init__(self, w, torch, cpa, DeviceStep):
+    def __init__(self, w, torch, cpa, DeviceStep, aux_stream=None):
         self.w = w
+        self.aux_stream = aux_stream
         self.ds = ds = DeviceStep(w, validate=True, with_lse=False)
         lib = self.lib = cpa.load()
         m = ds.meta
@@ -193,25 +194,57 @@ class Instance:
             counts = c.copy(**{**zero, field: getattr(c, field)})
             self.parts.append((name, counts, head + (vp(plan_base + 4 * off[sec]),
                                                      ctypes.byref(counts)) + common_tail))
+        self.torch = torch
+        self.aux_parts = {}
+        if self.aux_stream is not None:
+            aux_tail = common_tail[:-1] + (vp(self.aux_stream.cuda_stream),)
+            for name, counts, args in self.parts:
+                self.aux_parts[name] = args[:len(head) + 2] + aux_tail
         self.append_args = (P(ds.k_new), P(ds.v_new), P(ds.query_start_loc), P(ds.context_lens),
                             P(ds.block_table), int(ds.block_table.shape[1]), ds.num_seqs,
                             ds.num_tokens, w.num_kv_heads, w.head_dim, 16, P(ds.k_cache),
                             P(ds.v_cache), self.stream)
 
-    def step(self, events):
-        """One full step; events = 6 torch events recorded around the launches."""
+    def step(self, events, aux=None):
+        """One full step.  events: 8 torch events.  With ``aux`` (a second
+        stream) the chunk kernel and its merge run on it, concurrently with the
+        decode kernel and its merge on the main stream; both wait for the
+        append and the main stream waits for both."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         self.build_host()
         self.dev.copy_(self.pinned, non_blocking=True)
         self.copy_done.record()
         lib = self.lib
-        events[0].record()
-        st = lib.cpa_append_kv(*self.append_args)
-        events[1].record()
-        for k, (name, counts, args) in enumerate(self.parts):
-            if st == 0:
-                st = lib.cpa_attention(*args)
-            events[2 + k].record()
+        main = self.torch.cuda.current_stream()
+        parts = dict((name, args) for name, _, args in self.parts)
+        st = 0
+        events[0].record(main)
+        st |= lib.cpa_append_kv(*self.append_args)
+        events[1].record(main)
+        if aux is None:
+            st |= lib.cpa_attention(*parts["decode_kernel"])
+            events[2].record(main)
+            st |= lib.cpa_attention(*parts["merge_kernel"])
+            events[3].record(main)
+            events[4].record(main)
+            st |= lib.cpa_attention(*parts["chunk_kernel"])
+            events[5].record(main)
+            st |= lib.cpa_attention(*parts["chunk_merge_kernel"])
+            events[6].record(main)
+            events[7].record(main)
+        else:
+            aux.wait_event(events[1])
+            events[4].record(aux)
+            st |= lib.cpa_attention(*self.aux_parts["chunk_kernel"])
+            events[5].record(aux)
+            st |= lib.cpa_attention(*self.aux_parts["chunk_merge_kernel"])
+            events[6].record(aux)
+            st |= lib.cpa_attention(*parts["decode_kernel"])
+            events[2].record(main)
+            st |= lib.cpa_attention(*parts["merge_kernel"])
+            events[3].record(main)
+            main.wait_event(events[6])
+            events[7].record(main)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
 
@@ -282,6 +315,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the chunk kernel after the decode kernel on one stream "
+                         "(default: on a second stream, concurrently)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -314,15 +350,16 @@ def main():
     t_setup = time.perf_counter()
     ws = [workloads.make_workload(args.config, i)
           for i in range(workloads.num_instances(args.config))]
-    insts = [Instance(w, torch, cpa, DeviceStep) for w in ws]
+    aux = None if args.serial else torch.cuda.Stream()  # default priority
+    insts = [Instance(w, torch, cpa, DeviceStep, aux) for w in ws]
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
 
     K, W = args.steps, args.warmup
-    NEV = 6
+    NEV = 8
     ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
     for s in range(W):
-        insts[s % len(insts)].step(ev_w)
+        insts[s % len(insts)].step(ev_w, aux)
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(K)]
@@ -330,17 +367,22 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        insts[order[s]].step(events[s])
+        insts[order[s]].step(events[s], aux)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    names = ["append_kernel", "decode_kernel", "chunk_kernel", "merge_kernel", "chunk_merge_kernel"]
+    # (kernel, start event, end event) on the stream the kernel ran on
+    spans = {"append_kernel": (0, 1), "decode_kernel": (1, 2), "merge_kernel": (2, 3),
+             "chunk_kernel": (4, 5), "chunk_merge_kernel": (5, 6)}
+    names = list(spans)
     times = {n: 0.0 for n in names}
+    gpu_step = 0.0
     work = {"decode_bytes": 0, "chunk_flops": 0, "append_bytes": 0, "tokens": 0}
     for s in range(K):
         ev = events[s]
-        for k, n in enumerate(names):
-            times[n] += ev[k].elapsed_time(ev[k + 1]) * 1e-3
+        for n, (a, b) in spans.items():
+            times[n] += ev[a].elapsed_time(ev[b]) * 1e-3
+        gpu_step += ev[0].elapsed_time(ev[7]) * 1e-3
         wk = insts[order[s]].work
         for key in work:
             work[key] += wk[key]
@@ -401,6 +443,8 @@ def main():
                    "instances": len(insts)},
         "roofline": roofline,
         "kernels": kernels,
+        "streams": "serial" if args.serial else "decode and chunk on two streams, concurrently",
+        "gpu_step_us": gpu_step / K * 1e6,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host cores ...")

@@ -2,10 +2,14 @@
 // attention reads the cache ("05. Chunked Prefill" section 8; tbr8.org deep
 // dive 4.2, 16-token pages).  Pure bit copy.
 //
-// One workgroup per packed token.  K rows are copied as 16-byte pieces into
-// the token-major K page; V is scattered into the transposed V page
-// (slot-minor), 2 bytes per head dimension.  Tokens of one page write the
-// same 32-byte V rows, which the L2 merges before they reach HBM.
+// One workgroup per packed token.  A token t with query_start_loc[t] == t and
+// query_start_loc[t+1] == t+1 is row t's only token (every decode row, which
+// come first); other tokens find their row by a binary search.  K rows are
+// copied as 16-byte pieces into the token-major K page; V is scattered into
+// the transposed V page (slot-minor), 2 bytes per head dimension, lanes
+// walking consecutive d so one store instruction covers 2 KiB of one page.
+// Tokens of one page write the same 32-byte V rows, which the L2 merges
+// before they reach HBM.
 
 #include "device.h"
 #include "internal.h"
@@ -20,34 +24,33 @@ __global__ __launch_bounds__(128) void append_kernel(
     const int32_t* __restrict__ bt, int bt_stride, int num_seqs, int num_kv_heads,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache) {
   const int t = blockIdx.x;
-  // row of token t: the last s with qsl[s] <= t
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  int s;
+  if (t < num_seqs && qsl[t] == t && qsl[t + 1] == t + 1) {
+    s = t;
+  } else {  // the last s with qsl[s] <= t
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
   }
-  const int s = lo;
   const int p = ctx[s] + (t - qsl[s]);
   const int64_t blk = bt[(int64_t)s * bt_stride + p / kBlock];
   const int slot = p % kBlock;
+  const int64_t page0 = blk * num_kv_heads * (int64_t)(kBlock * D);
 
   constexpr int kParts = D / 8;  // 16-byte pieces per head row
-  const int pieces = num_kv_heads * kParts;
   const uint4* ksrc = reinterpret_cast<const uint4*>(k_new + (int64_t)t * num_kv_heads * D);
-  const uint4* vsrc = reinterpret_cast<const uint4*>(v_new + (int64_t)t * num_kv_heads * D);
-  for (int c = threadIdx.x; c < pieces; c += blockDim.x) {
+  for (int c = threadIdx.x; c < num_kv_heads * kParts; c += blockDim.x) {
     const int g = c / kParts, part = c % kParts;
-    const int64_t page = (blk * num_kv_heads + g) * (int64_t)(kBlock * D);
-    const uint4 kv = ksrc[c];
-    *reinterpret_cast<uint4*>(k_cache + page + slot * D + part * 8) = kv;
-    const uint4 vv = vsrc[c];
-    uint16_t* vdst = v_cache + page + (int64_t)(part * 8) * kBlock + slot;
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vdst[(2 * i) * kBlock] = (uint16_t)(w[i] & 0xFFFFu);
-      vdst[(2 * i + 1) * kBlock] = (uint16_t)(w[i] >> 16);
-    }
+    *reinterpret_cast<uint4*>(k_cache + page0 + (int64_t)g * (kBlock * D) + slot * D + part * 8) =
+        ksrc[c];
+  }
+  const uint16_t* vsrc = v_new + (int64_t)t * num_kv_heads * D;
+  for (int c = threadIdx.x; c < num_kv_heads * D; c += blockDim.x) {
+    const int g = c / D, d = c % D;
+    v_cache[page0 + (int64_t)g * (kBlock * D) + d * kBlock + slot] = vsrc[c];
   }
 }
 

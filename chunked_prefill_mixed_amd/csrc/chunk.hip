@@ -36,6 +36,8 @@
 // never runs; the sums stay exact because numerator and denominator share the
 // reference, and each probability stays below 2^8.
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 #include "tiles.h"
@@ -57,8 +59,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   constexpr int PER_THREAD = CHUNKS / 256;
   static_assert(CHUNKS % 256 == 0, "tile must split evenly over 256 threads");
 
-  __shared__ __align__(16) uint16_t k_lds[kKvTile * KSTR];
-  __shared__ __align__(16) uint16_t v_lds[4 * PAGE];
+  // two stages: one tile is read while the next is written
+  __shared__ __align__(16) uint16_t k_lds_buf[2][kKvTile * KSTR];
+  __shared__ __align__(16) uint16_t v_lds_buf[2][4 * PAGE];
 
   const int item = xcd_remap(blockIdx.x, num_tiles * num_kv_heads);
   const int g = item / num_tiles;
@@ -154,7 +157,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    uint16_t* k_lds = k_lds_buf[stage];
+    uint16_t* v_lds = v_lds_buf[stage];
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int cidx = tid + 256 * i;
@@ -174,33 +179,39 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   load_ids(kt0, ids);
   load_tile(kt0, ids);
   load_ids(min(kt0 + 1, n_kv - 1), ids);
-  for (int kt = kt0; kt < n_kv; ++kt) {
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();
-    // next tile's K/V (the last tile again at the end: an L2 hit that keeps
-    // the loads unconditional) and the page ids of the tile after it
-    load_tile(min(kt + 1, n_kv - 1), ids);
-    load_ids(min(kt + 2, n_kv - 1), ids);
+  store_tile(0);
+  __syncthreads();
+  load_tile(min(kt0 + 1, n_kv - 1), ids);
+  load_ids(min(kt0 + 2, n_kv - 1), ids);
 
-    // S^T = K Q^T for two 32-key blocks
+  // one 64-key tile; MASK is a compile-time switch so tiles wholly visible to
+  // every row of the tile carry no masking code at all.  On entry the tile is
+  // in LDS stage (kt - kt0) & 1 and the next tile's K/V are in registers.
+  auto tile = [&](auto mask_tag, int kt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int stage = (kt - kt0) & 1;
+    const uint16_t* k_lds = k_lds_buf[stage];
+    const uint16_t* v_lds = v_lds_buf[stage];
+
+    // S^T = K Q^T for two 32-key blocks, the two accumulator chains interleaved
     f32x16_t s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const uint16_t* krow_p = &k_lds[(32 * kb + krow) * KSTR + 8 * half];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(krow_p + 16 * ks);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 a = *reinterpret_cast<const uint4*>(
+            &k_lds[(32 * kb + krow) * KSTR + 8 * half + 16 * ks]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                         __builtin_bit_cast(bf16x8_t, qf[ks]),
                                                         s[kb], 0, 0, 0);
       }
-    }
 
-    const int key_base = kt * kKvTile;
-    if (key_base + kKvTile - 1 > c + qb) {  // tile reaches past some query's last key
+    if constexpr (MASK) {
+      const int key_base = kt * kKvTile;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -219,10 +230,20 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     // move the reference max only when this tile exceeds it by more than 2^8
     // (always on a row's first tile, where m is -inf)
     const bool grow = (mx - m) * scale_log2 > 8.f;
-    const float mn = grow ? mx : m;
-    const float alpha = fast_exp2((m - mn) * scale_log2);
-    m = mn;
-    const float msc = mn * scale_log2;
+    if (__any(grow)) {
+      // rare: rescale the running sums; the empty asm keeps the compiler from
+      // hoisting this out of the branch and running it on every tile
+      asm volatile("" ::: "memory");
+      const float mn = grow ? mx : m;
+      const float alpha = fast_exp2((m - mn) * scale_log2);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    const float msc = m * scale_log2;
 
     float psum = 0.f;
     uint4 pb[4];
@@ -237,27 +258,38 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       pb[kp] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
     }
-    lsum = lsum * alpha + psum;
-    if (__any(grow)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
+    lsum += psum;
 
-    // O^T += V^T P^T, one page (16 keys) per MFMA
+    // O^T += V^T P^T, one page (16 keys) per MFMA, the DB accumulator chains
+    // interleaved
     const int vh = half ^ ((ncol >> 3) & 1);  // the swizzled half holding keys 8*half..
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int kp = 0; kp < 4; ++kp)
 #pragma unroll
-      for (int kp = 0; kp < 4; ++kp) {
+      for (int db = 0; db < DB; ++db) {
         const uint4 a =
             *reinterpret_cast<const uint4*>(&v_lds[kp * PAGE + (32 * db + ncol) * kBlock + 8 * vh]);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                         __builtin_bit_cast(bf16x8_t, pb[kp]),
                                                         o[db], 0, 0, 0);
       }
-  }
+
+    // stage the next tile into the other buffer (its previous contents, tile
+    // kt - 1, were last read before the barrier that ended that tile), then
+    // start loading the one after it
+    if (kt + 1 < n_kv) {
+      store_tile(stage ^ 1);
+      __syncthreads();
+      load_tile(min(kt + 2, n_kv - 1), ids);
+      load_ids(min(kt + 3, n_kv - 1), ids);
+    }
+  };
+
+  // tile kt needs the causal mask iff its last key is past the tile's first
+  // query's limit: kt*64 + 63 > context + q_begin
+  const int kt_mask = max(kt0, min(n_kv, (c + qb + 1) / kKvTile));
+  for (int kt = kt0; kt < kt_mask; ++kt) tile(std::integral_constant<bool, false>(), kt);
+  for (int kt = kt_mask; kt < n_kv; ++kt) tile(std::integral_constant<bool, true>(), kt);
 
   lsum += xor_lane(lsum, 32);
   if (row_ok && slot >= 0) {

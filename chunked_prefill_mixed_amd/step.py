@@ -78,6 +78,42 @@ class DeviceStep:
         self.append(stream)
         self.attention(stream)
 
+    def _section_call(self, section, stream):
+        """cpa_attention over one plan section only."""
+        import ctypes
+        import torch
+        c = self.counts
+        zero = dict(num_decode_splits=0, num_decode_merges=0, num_chunk_tiles=0,
+                    num_chunk_merges=0)
+        field = {"decode_splits": "num_decode_splits", "decode_merges": "num_decode_merges",
+                 "chunk_tiles": "num_chunk_tiles", "chunk_merges": "num_chunk_merges"}[section]
+        counts = c.copy(**{**zero, field: getattr(c, field)})
+        off = cpa.section_offsets(c)[section]
+        plan_view = self.plan[off:] if off < self.plan.numel() else self.plan
+        cpa.cpa_attention(self.q, self.k_cache, self.v_cache, self.block_table,
+                          self.query_start_loc, self.seq_lens, self.context_lens, plan_view,
+                          counts, num_seqs=self.num_seqs, num_decodes=self.num_decodes,
+                          num_tokens=self.num_tokens, softmax_scale=self.scale, out=self.out,
+                          lse=self.lse, workspace=self.workspace, stream=stream)
+
+    def run_two_streams(self, aux):
+        """Append on the current stream, then the chunk sections on ``aux``
+        concurrently with the decode sections; the current stream waits for
+        both."""
+        import torch
+        main = torch.cuda.current_stream()
+        self.append(main)
+        appended = torch.cuda.Event()
+        appended.record(main)
+        aux.wait_event(appended)
+        self._section_call("chunk_tiles", aux)
+        self._section_call("chunk_merges", aux)
+        self._section_call("decode_splits", main)
+        self._section_call("decode_merges", main)
+        done = torch.cuda.Event()
+        done.record(aux)
+        main.wait_event(done)
+
     # host copies for checking
     def pools_bits(self):
         return bf16_to_bits(self.k_cache), bf16_to_bits(self.v_cache)

@@ -213,8 +213,10 @@ size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int 
  * d_plan is the plan from cpa_build_metadata copied to the device, with its
  * counts in *counts (host pointer).  Any subset of the plan's sections may be
  * run by passing counts with the other sections set to 0 and d_plan pointing
- * at the first section run (the sections are independent, except that a
- * merge section must run after the splits it merges).  workspace must hold
+ * at the first section run.  The decode sections and the chunk sections are
+ * independent (they touch different output rows), so after this step's append
+ * they may run concurrently on two streams; a merge section must run after
+ * the split or tile section it merges, on the same stream or after an event.  workspace must hold
  * cpa_workspace_size(counts, ...) bytes (may be NULL when nothing is split);
  * its contents need no initialisation.  The append of this step must already
  * be enqueued on the same stream.  d_seq_lens is not read (the plan carries

@@ -190,6 +190,21 @@ def test_chunk_split_count_does_not_change_result(csplit):
             assert ds.counts.num_chunk_merges > 0
 
 
+def test_two_streams_match_one_stream():
+    """Decode sections on the main stream and chunk sections on a second
+    stream, concurrently after the append, give the same bits as one stream."""
+    import torch
+    w = workloads.make_workload(2, 2)
+    a = DeviceStep(w)
+    a.run()
+    b = DeviceStep(w)
+    aux = torch.cuda.Stream()
+    b.run_two_streams(aux)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+
+
 @pytest.mark.parametrize("C", [1, 7, 16, 64, 100, 256])
 def test_gpu_chunking_invariance(C):
     """One 256-token prompt prefilled in chunks of C, each chunk appended
