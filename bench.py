@@ -4,7 +4,8 @@
 A step is one pass of the whole path over one packed batch: the host
 decode-first budget split and work plan (cpa_build_metadata), one H2D copy of
 the step metadata, the paged KV append, the split-KV decode kernel, its
-log-sum-exp merge and the MFMA prefill-chunk kernel, all on one stream.
+log-sum-exp merge and the MFMA prefill-chunk kernel with its merge, all on one
+stream (``--two-streams`` runs the chunk kernels on a second stream).
 Inputs (q, new K/V, the paged KV pool) are resident in HBM before timing.
 
 Default workload (Page-1 defaults of the chunked-prefill essay): 32 decode
@@ -315,9 +316,10 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--serial", action="store_true",
-                    help="run the chunk kernel after the decode kernel on one stream "
-                         "(default: on a second stream, concurrently)")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="run the chunk kernel and its merge on a second stream, concurrently "
+                         "with the decode kernel and its merge (default: one stream, so each "
+                         "kernel's HIP-event time is its own)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -350,7 +352,7 @@ def main():
     t_setup = time.perf_counter()
     ws = [workloads.make_workload(args.config, i)
           for i in range(workloads.num_instances(args.config))]
-    aux = None if args.serial else torch.cuda.Stream()  # default priority
+    aux = torch.cuda.Stream() if args.two_streams else None  # default priority
     insts = [Instance(w, torch, cpa, DeviceStep, aux) for w in ws]
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
@@ -443,7 +445,8 @@ def main():
                    "instances": len(insts)},
         "roofline": roofline,
         "kernels": kernels,
-        "streams": "serial" if args.serial else "decode and chunk on two streams, concurrently",
+        "streams": ("decode and chunk on two streams, concurrently" if args.two_streams
+                    else "one stream"),
         "gpu_step_us": gpu_step / K * 1e6,
     }
     if not args.no_cpu_baseline:

@@ -31,6 +31,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# per-source additions: the decode kernel's small 16x16 MFMA accumulators are
+# kept in ordinary VGPRs (no accumulator-register copies around every MFMA)
+FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 GXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include")]
 
 
@@ -62,7 +65,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".host.o"))
         jobs.append(["g++", *GXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])

@@ -8,9 +8,10 @@
 // the number of decodes is rejected ("Chunked Prefill", "The budget points in
 // two directions").
 //
-// Work plan: decode rows are cut into key splits of a fixed page-aligned size
-// so lognormal context lengths balance over the GPU; rows with several splits
-// get a log-sum-exp merge entry.  Chunk rows are cut into query tiles of
+// Work plan: decode rows are cut into page-aligned key pieces sized so that
+// every wave is resident at once and none reads more pages than needed
+// (lognormal context lengths then balance over the GPU); rows with several
+// pieces get a log-sum-exp merge entry.  Chunk rows are cut into query tiles of
 // kChunkRows/(Hq/Hkv) tokens, ordered longest key range first.
 //
 // Pure host code: no HIP call, safe to run on a machine without a GPU.
@@ -42,13 +43,30 @@ int check_params(const cpa_build_params_t* p) {
   return CPA_OK;
 }
 
-// Keys per decode split: enough splits that about kDecodeWavesTarget waves
-// (split x KV head) cover the decode rows, each split a whole number of pages.
-int pick_split(int64_t decode_keys, int num_kv_heads) {
-  int64_t splits = std::max<int64_t>(1, cpa::kDecodeWavesTarget / num_kv_heads);
-  int64_t per = ceil_div(std::max<int64_t>(decode_keys, 1), splits);
-  per = ceil_div(per, cpa::kBlock) * cpa::kBlock;
-  return (int)std::min<int64_t>(std::max<int64_t>(per, 128), cpa::kDecodeMaxSplit);
+// Pages per decode piece when the caller leaves the split size to the
+// planner.  Decode is bound by HBM bandwidth, so its time is the time of the
+// longest wave: pick the fewest passes k of R resident waves (R from
+// decode_waves_target) for which pieces of at most 64 pages exist, then the
+// smallest page count p such that the rows, each cut into ceil(pages/p)
+// pieces, give at most k * R waves (piece x KV head).  Every wave then
+// starts in pass 1..k and no wave reads more than p pages.  p is kept at 8 pages or
+// more: a shorter piece is mostly start-up latency and lengthens the merge.
+int pick_piece_pages(const std::vector<int64_t>& row_pages, int num_kv_heads, int head_dim) {
+  constexpr int64_t kMinPages = 8;
+  const int64_t max_pages = cpa::kDecodeMaxSplit / cpa::kBlock;
+  auto waves = [&](int64_t p) {
+    int64_t n = 0;
+    for (int64_t pg : row_pages) n += ceil_div(pg, p);
+    return n * num_kv_heads;
+  };
+  const int64_t target = cpa::decode_waves_target(head_dim);
+  const int64_t budget = ceil_div(std::max<int64_t>(waves(max_pages), 1), target) * target;
+  int64_t lo = kMinPages, hi = max_pages;  // waves(p) is non-increasing in p; waves(hi) <= budget
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (waves(mid) <= budget) hi = mid; else lo = mid + 1;
+  }
+  return (int)lo;
 }
 
 // Prefix keys per chunk piece: none split when the tiles alone give enough
@@ -114,7 +132,6 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
     return CPA_ERR_INVALID;
 
   int32_t qsl = 0;
-  int64_t decode_keys = 0;
   out->query_start_loc[0] = 0;
   for (int s = 0; s < nseq; ++s) {
     const cpa_req_t& r = reqs[order[s]];
@@ -127,7 +144,6 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
                                      ceil_div(r.num_computed, cpa::kBlock));
     qsl += nsched[s];
     out->query_start_loc[s + 1] = qsl;
-    if (s < n_dec) decode_keys += out->seq_lens[s];
   }
   out->num_seqs = nseq;
   out->num_decodes = n_dec;
@@ -167,19 +183,22 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   }
 
   // ---- work plan --------------------------------------------------------
-  const int split = params->decode_split_tokens ? params->decode_split_tokens
-                                                : pick_split(decode_keys, params->num_kv_heads);
+  // a row of L keys is cut into n pieces of nearly equal, page-aligned size:
+  // n = ceil(L / split) for a caller-given split, else ceil(pages / p) with p
+  // from pick_piece_pages.  Pieces are emitted longest first so the last
+  // waves to start are short ones.
+  std::vector<int64_t> row_pages(n_dec);
+  for (int s = 0; s < n_dec; ++s) row_pages[s] = ceil_div(out->seq_lens[s], cpa::kBlock);
+  const int split = params->decode_split_tokens;
+  const int piece_pages = split ? 0 : pick_piece_pages(row_pages, params->num_kv_heads, params->head_dim);
   std::vector<int32_t> dsplits, dmerges, tiles;
   int partials = 0;
-  // a row of L keys is cut into n = ceil(L / split) pieces of nearly equal,
-  // page-aligned size; pieces are emitted longest first so the last waves to
-  // start are short ones
   struct DPiece { int32_t row, kb, ke, slot; };
   std::vector<DPiece> dp;
   for (int s = 0; s < n_dec; ++s) {
     const int L = out->seq_lens[s];
-    const int64_t pages = ceil_div(L, cpa::kBlock);
-    const int n = (int)ceil_div(L, split);
+    const int64_t pages = row_pages[s];
+    const int n = (int)(split ? ceil_div(L, split) : ceil_div(pages, piece_pages));
     if (n == 1) {
       dp.push_back({s, 0, L, -1});
       continue;

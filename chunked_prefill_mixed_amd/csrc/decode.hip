@@ -3,22 +3,28 @@
 // A decode row's single query reads its whole cached context from HBM each
 // step ("How Chunked Prefill Stops Decode Starvation", "The stall"; tbr8.org
 // deep dive section 1), so this kernel is bound by HBM bandwidth: about 4
-// flops per byte of K/V at 4 query heads per KV head.  It uses VALU dot
-// products and lane exchanges, not matrix cores.
+// flops per byte of K/V at 4 query heads per KV head.
 //
-// One wave per (key split, KV head).  All G query heads that share the KV
-// head are served by the one read of each 16-token page.
-//   K page [16][D]: lane l owns keys l/8 and l/8 + 8 and the 8-wide d
-//     pieces (l%8)*8 + 64j; each 16-byte load instruction of the wave reads
-//     8 whole 128-byte lines (8 lanes per key row).  Scores: v_dot2_f32_bf16
-//     over the lane's d pieces, then a 3-step DPP sum over the row's 8 lanes.
-//   V page [D][16] (transposed): lane l owns d = 32j + l/2 and keys
-//     8*(l%2)..+8, one contiguous 16-byte load per j; the whole wave reads
-//     the 4 KiB page in 1 KiB contiguous sweeps.  P*V: v_dot2 over the
-//     lane's 8 keys with the bf16 probabilities (moved from key-owner lanes
-//     through 64 bytes of LDS per head).
-// Online softmax in fp32 with a wave-uniform running max per head.  A row
-// covered by one split writes its bf16 output directly; otherwise each split
+// One wave per (key piece, KV head).  All G query heads that share the KV
+// head are served by the one read of each 16-token page, and both products
+// run on the matrix cores so the wave's vector work per page stays small
+// next to the time its 8 KiB take to arrive:
+//   S^T[16 keys][16 cols] = K Q^T      v_mfma_f32_16x16x32_bf16, D/32 steps;
+//                                      K page rows are the A operand as
+//                                      loaded, column n of Q^T holds query
+//                                      head n % G (columns n >= G repeat heads
+//                                      and are never stored)
+//   O^T[D][16 cols] += V^T P^T         v_mfma_f32_16x16x16_bf16, D/16 blocks;
+//                                      V pages are stored transposed ([D][16])
+//                                      so each lane loads its A operand as 8
+//                                      contiguous bytes, and P^T is the S^T
+//                                      accumulator itself (lane (g4, n) holds
+//                                      keys 4*g4..+4 of column n in both)
+// Online softmax per column in fp32: the 4 keys of a lane, then across the 4
+// lane groups with two exchanges.  The reference max only moves when a page
+// exceeds it by more than 2^8 (always on the first page), so the accumulator
+// rescale is rare; numerator and denominator share the reference.  A row
+// covered by one piece writes its bf16 output directly; otherwise each piece
 // writes unnormalised fp32 (acc, max, sum) and merge_kernel combines them:
 //   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
 
@@ -26,193 +32,168 @@
 #include "internal.h"
 #include "tiles.h"
 
-#ifndef CPA_DECODE_WAVES_PER_WG
-#define CPA_DECODE_WAVES_PER_WG 4   // independent (split, KV head) items per workgroup
+#ifndef CPA_DECODE_STAGES
+#define CPA_DECODE_STAGES 2   // pages each wave holds in registers: one computed, the rest loading
 #endif
 
 namespace cpa {
 
-constexpr int kDecodeWaves = CPA_DECODE_WAVES_PER_WG;
+constexpr int kDecodeWaves = 4;  // independent (piece, KV head) waves per workgroup
+constexpr int kStages = CPA_DECODE_STAGES;
 
-// Orders one wave's LDS writes before its own later LDS reads by other lanes
-// (LDS executes a wave's operations in order; this stops the compiler from
-// moving them and makes the writes visible at wavefront scope).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 template <int D, int G>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
-    const int32_t* __restrict__ qsl, const int32_t* __restrict__ splits, int num_q_heads,
-    int num_kv_heads, int num_items, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, Partials ws) {
-  constexpr int J = D / 32;   // 16-byte V pieces per lane per page
-  constexpr int JK = D / 64;  // 16-byte K pieces per lane per key (2 keys per lane)
-  __shared__ __align__(16) uint16_t pbuf_all[kDecodeWaves][2][G][kBlock];
+    const int32_t* __restrict__ splits, int num_q_heads, int num_kv_heads, int num_items,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials ws) {
+  constexpr int KK = D / 32;  // S^T steps over d
+  constexpr int MB = D / 16;  // O^T blocks of 16 d rows
+  constexpr int PAGE_BYTES = kBlock * D * 2;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int item = blockIdx.x * kDecodeWaves + wave;
   if (item >= num_items) return;  // whole wave; no workgroup barrier below
-  auto& pbuf = pbuf_all[wave];
   const int g = item % num_kv_heads;
-  const int sp = item / num_kv_heads;
-  const int4 e = reinterpret_cast<const int4*>(splits)[sp];
+  const int4 e = reinterpret_cast<const int4*>(splits)[item / num_kv_heads];
   const int row = e.x, kv_begin = e.y, kv_end = e.z, slot = e.w;
   // decode rows come first and hold one token each, so row s is packed token s
   const int t = row;
-  (void)qsl;
-  const int kg = lane >> 3, dp = lane & 7, par = lane & 1;
+  const int n = lane & 15;   // column: query head n % G of the group
+  const int g4 = lane >> 4;  // lane group: d pieces of S^T, keys 4*g4..+4 of P^T and O^T
+  const int hq = g * G + n % G;
 
-  uint4 qf[G][JK];
+  // B operand of S^T: Q[hq][32 kk + 8 g4 .. +8]
+  uint4 qf[KK];
+  {
+    const uint16_t* qrow = q + ((int64_t)t * num_q_heads + hq) * D + 8 * g4;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int j = 0; j < JK; ++j)
-      qf[h][j] = *reinterpret_cast<const uint4*>(
-          q + ((int64_t)t * num_q_heads + g * G + h) * D + dp * 8 + 64 * j);
-
-  float m[G], lsum[G], acc[G][J];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = neg_inf();
-    lsum[h] = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) acc[h][j] = 0.f;
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
 
   const int32_t* btrow = bt + (int64_t)row * bt_stride;
-  // a split spans at most 64 pages (the planner guarantees it): one coalesced
-  // load of its page ids, then v_readlane per page
+  // a piece spans at most 64 pages (the planner guarantees it): one
+  // coalesced load of its page ids, then v_readlane per page
   const int pg0 = kv_begin / kBlock, npages = (kv_end + kBlock - 1) / kBlock - pg0;
-  const int my_blk = lane < npages ? btrow[pg0 + lane] : 0;
-  auto page_base = [&](int i) -> int64_t {
+  const int my_blk = btrow[pg0 + min(lane, npages - 1)];
+  // Loads go through a buffer resource built per page from the wave-uniform
+  // page address: scalar base, fixed per-lane byte offsets, and the hardware
+  // range check keeps every access inside the one (page, KV head) piece.
+  const uint32_t kbyte = (uint32_t)(n * D + 8 * g4) * 2;   // + 64 kk: K[n][32 kk + 8 g4 ..]
+  const uint32_t vbyte = (uint32_t)(n * kBlock + 4 * g4) * 2;  // + 512 mb: V^T[16 mb + n][4 g4 ..]
+  uint4 kset[kStages][KK];
+  uint2 vset[kStages][MB];
+  auto load_page = [&](int i, uint4 (&kd)[KK], uint2 (&vd)[MB]) {
     const int blk = __builtin_amdgcn_readlane(my_blk, i);
-    return ((int64_t)blk * num_kv_heads + g) * (kBlock * D);
-  };
-  // per-lane offsets inside a (page, KV head) piece, in 16-byte units; the
-  // page base is wave-uniform, so every load is scalar base + fixed 32-bit
-  // lane offset and no address register is rewritten per page
-  const uint32_t koff = (uint32_t)(kg * D + dp * 8) / 8;
-  const uint32_t voff = (uint32_t)lane;
-  // two register sets, used in turn: while one page is computed the other's
-  // loads are in flight, and each compute waits only for its own page
-  uint4 ka[2 * JK], va[J], kb[2 * JK], vb[J];
-  auto load_page = [&](int64_t page, uint4 (&kd)[2 * JK], uint4 (&vd)[J]) {
-    const uint4* kp = reinterpret_cast<const uint4*>(k_cache + page);
-    const uint4* vp = reinterpret_cast<const uint4*>(v_cache + page);
+    const int64_t page = ((int64_t)blk * num_kv_heads + g) * (kBlock * D);
+    const auto kr = make_page_rsrc(k_cache + page, PAGE_BYTES);
+    const auto vr = make_page_rsrc(v_cache + page, PAGE_BYTES);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int kk = 0; kk < KK; ++kk) kd[kk] = buffer_load16(kr, kbyte + 64 * kk);
 #pragma unroll
-      for (int j = 0; j < JK; ++j) kd[ks * JK + j] = kp[koff + (8 * ks * D + 64 * j) / 8];
-#pragma unroll
-    for (int j = 0; j < J; ++j) vd[j] = vp[voff + j * 64];
-  };
-  auto compute_page = [&](int i, uint4 (&kc)[2 * JK], uint4 (&vc)[J]) {
-    const int pg = pg0 + i;
-    const int buf = i & 1;
-    const bool valid0 = pg * kBlock + kg < kv_end;
-    const bool valid1 = pg * kBlock + kg + 8 < kv_end;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < JK; ++j) {
-        a0 = dot8_bf16(qf[h][j], kc[j], a0);
-        a1 = dot8_bf16(qf[h][j], kc[JK + j], a1);
-      }
-      a0 += dpp<kQuadXor1>(a0);
-      a1 += dpp<kQuadXor1>(a1);
-      a0 += dpp<kQuadXor2>(a0);
-      a1 += dpp<kQuadXor2>(a1);
-      a0 += dpp<kRowHalfMirror>(a0);
-      a1 += dpp<kRowHalfMirror>(a1);
-      const float s0 = valid0 ? a0 : neg_inf();
-      const float s1 = valid1 ? a1 : neg_inf();
-      float mx = fmaxf(s0, s1);
-      mx = fmaxf(mx, dpp<kRowMirror>(mx));
-      mx = fmaxf(mx, xor_lane(mx, 16));
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float mn = fmaxf(m[h], mx);
-      const float alpha = fast_exp2((m[h] - mn) * scale_log2);
-      m[h] = mn;
-      const float p0 = fast_exp2((s0 - mn) * scale_log2);
-      const float p1 = fast_exp2((s1 - mn) * scale_log2);
-      lsum[h] = lsum[h] * alpha + (dp == 0 ? p0 + p1 : 0.f);
-#pragma unroll
-      for (int j = 0; j < J; ++j) acc[h][j] *= alpha;
-      // the row's 8 lanes hold the same two scores; lane dp publishes value
-      // dp, dp+8, ... of the (key slot, head) pairs
-#pragma unroll
-      for (int v = 0; v < 2 * G; v += 8)
-        if (v + dp < 2 * G && (v + dp) % G == h)
-          pbuf[buf][h][kg + 8 * ((v + dp) / G)] = to_bf16((v + dp) / G ? p1 : p0);
-    }
-    // keys past the split's end in its last page: their V slots may hold
-    // anything (even NaN); zero them so 0 * V stays 0
-    const int nvalid = kv_end - pg * kBlock - 8 * par;
-    if (nvalid < 8) {
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        uint32_t w[4] = {vc[j].x, vc[j].y, vc[j].z, vc[j].w};
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const uint32_t keep_lo = (2 * e2 < nvalid) ? 0xFFFFu : 0u;
-          const uint32_t keep_hi = (2 * e2 + 1 < nvalid) ? 0xFFFF0000u : 0u;
-          w[e2] &= (keep_lo | keep_hi);
-        }
-        vc[j] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4 pp = *reinterpret_cast<const uint4*>(&pbuf[buf][h][8 * par]);
-#pragma unroll
-      for (int j = 0; j < J; ++j) acc[h][j] = dot8_bf16(pp, vc[j], acc[h][j]);
-    }
+    for (int mb = 0; mb < MB; ++mb) vd[mb] = buffer_load8(vr, vbyte + 512 * mb);
   };
 
-  // pages in pairs with no early exit: for an odd count the pair's second
-  // page is past the split end, every key of it is masked (p = 0, the
-  // running max and sums are unchanged) and its loads re-read the last page
-  // (an L2 hit), which keeps the loop free of branches around the loads
-  load_page(page_base(0), ka, va);
-  const int npairs = (npages + 1) / 2;
-  for (int ip = 0; ip < npairs; ++ip) {
-    const int i = 2 * ip;
-    load_page(page_base(min(i + 1, npages - 1)), kb, vb);
-    compute_page(i, ka, va);
-    load_page(page_base(min(i + 2, npages - 1)), ka, va);
-    compute_page(i + 1, kb, vb);
+  float m = neg_inf(), lsum = 0.f;
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_page = [&](int i, const uint4 (&kc)[KK], uint2 (&vc)[MB]) {
+    const int key0 = (pg0 + i) * kBlock;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[kk]),
+                                                  __builtin_bit_cast(bf16x8_t, qf[kk]), s, 0, 0,
+                                                  0);
+    // the piece's last page (or one past it): mask keys at or past kv_end,
+    // and zero their V entries (unwritten or sentinel data must not reach
+    // P*V, where 0 * NaN would not vanish).  The test is wave-uniform.
+    if (key0 + kBlock > kv_end) {
+      const int nvalid = kv_end - key0 - 4 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r >= nvalid) s[r] = neg_inf();
+      const uint32_t keep0 = (nvalid > 0 ? 0xFFFFu : 0u) | (nvalid > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t keep1 = (nvalid > 2 ? 0xFFFFu : 0u) | (nvalid > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) vc[mb] = make_uint2(vc[mb].x & keep0, vc[mb].y & keep1);
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    // move the reference max only when this page exceeds it by more than 2^8
+    // (always on the first page, where m is -inf)
+    const bool grow = (mx - m) * scale_log2 > 8.f;
+    if (__any(grow)) {
+      // rare: rescale the running sums; the empty asm keeps the compiler from
+      // hoisting this out of the branch and running it on every page
+      asm volatile("" ::: "memory");
+      const float mn = grow ? mx : m;
+      const float alpha = fast_exp2((m - mn) * scale_log2);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+    }
+    const float msc = m * scale_log2;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], scale_log2, -msc));
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    const uint2 pb = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vc[mb]),
+                                                          __builtin_bit_cast(short4_t, pb),
+                                                          acc[mb], 0, 0, 0);
+  };
+
+  // pages in groups of kStages with no early exit: pages past the piece end
+  // are masked in full (p = 0; the running max and sums are unchanged) and
+  // their loads re-read the last page (an L2 hit), which keeps the loop free
+  // of branches around the loads
+#pragma unroll
+  for (int u = 0; u + 1 < kStages; ++u) load_page(min(u, npages - 1), kset[u], vset[u]);
+  for (int i0 = 0; i0 < npages; i0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      constexpr int kLast = kStages - 1;
+      load_page(min(i0 + u + kLast, npages - 1), kset[(u + kLast) % kStages],
+                vset[(u + kLast) % kStages]);
+      compute_page(i0 + u, kset[u], vset[u]);
+    }
   }
 
+  // column sums over the 4 lane groups (each summed its own keys)
+  lsum += xor_lane(lsum, 16);
+  lsum += xor_lane(lsum, 32);
+  if (n >= G) return;
+  const int d0 = 4 * g4;  // this lane's O^T rows inside each 16-row block
+  if (slot < 0) {
+    const float inv = 1.f / lsum;
+    uint16_t* orow = out + ((int64_t)t * num_q_heads + hq) * D + d0;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float l = wave_sum(lsum[h]);
-    const int hq = g * G + h;
+    for (int mb = 0; mb < MB; ++mb)
+      *reinterpret_cast<uint2*>(orow + 16 * mb) =
+          make_uint2(pack_bf16x2(acc[mb][0] * inv, acc[mb][1] * inv),
+                     pack_bf16x2(acc[mb][2] * inv, acc[mb][3] * inv));
+    if (lse && g4 == 0)
+      lse[(int64_t)t * num_q_heads + hq] = (m * scale_log2 + __log2f(lsum)) * kLn2;
+  } else {
+    const int64_t ph = (int64_t)slot * num_q_heads + hq;
+    float* arow = ws.acc + ph * D + d0;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const float a = acc[h][j] + dpp<kQuadXor1>(acc[h][j]);
-      const int d = 32 * j + (lane >> 1);
-      if (par == 0) {
-        if (slot < 0)
-          out[((int64_t)t * num_q_heads + hq) * D + d] = to_bf16(a / l);
-        else
-          ws.acc[((int64_t)slot * num_q_heads + hq) * D + d] = a;
-      }
-    }
-    if (lane == 0) {
-      const float m2 = m[h] * scale_log2;
-      if (slot < 0) {
-        if (lse) lse[(int64_t)t * num_q_heads + hq] = (m2 + __log2f(l)) * kLn2;
-      } else {
-        ws.m[(int64_t)slot * num_q_heads + hq] = m2;
-        ws.l[(int64_t)slot * num_q_heads + hq] = l;
-      }
+    for (int mb = 0; mb < MB; ++mb)
+      *reinterpret_cast<float4*>(arow + 16 * mb) =
+          make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+    if (g4 == 0) {
+      ws.m[ph] = m * scale_log2;
+      ws.l[ph] = lsum;
     }
   }
 }
@@ -258,15 +239,13 @@ __global__ __launch_bounds__(64) void merge_kernel(const int32_t* __restrict__ m
 
 template <int D, int G>
 static void launch_decode_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
-                            int bt_stride, const int32_t* qsl, const int32_t* splits,
-                            int num_splits, int hq, int hkv, float sl2, void* out, float* lse,
-                            Partials ws, hipStream_t stream) {
+                            int bt_stride, const int32_t* splits, int num_splits, int hq, int hkv,
+                            float sl2, void* out, float* lse, Partials ws, hipStream_t stream) {
   const int items = num_splits * hkv;
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3((items + kDecodeWaves - 1) / kDecodeWaves),
                      dim3(64 * kDecodeWaves), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,
-                     bt_stride, qsl, splits, hq, hkv, items, sl2, static_cast<uint16_t*>(out), lse,
-                     ws);
+                     bt_stride, splits, hq, hkv, items, sl2, static_cast<uint16_t*>(out), lse, ws);
 }
 
 hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -277,7 +256,7 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
   const int G = num_q_heads / num_kv_heads;
 #define CPA_DEC(DD, GG)                                                                        \
   if (head_dim == DD && G == GG) {                                                              \
-    launch_decode_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, qsl, splits, num_splits,        \
+    launch_decode_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, splits, num_splits,             \
                             num_q_heads, num_kv_heads, scale_log2, out, lse, ws, stream);       \
     return hipGetLastError();                                                                   \
   }

@@ -43,6 +43,21 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
   return acc;
 }
 
+// Buffer resource (V#) over [base, base + bytes): raw (unstructured) access,
+// stride 0; loads past the range return 0.  The last word holds the
+// gfx9-family default data format for untyped dword access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes at byte offset off of the resource (buffer_load_dwordx4).
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// 8 bytes at byte offset off of the resource (buffer_load_dwordx2).
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // DPP lane exchanges inside a 16-lane row.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -6,10 +6,16 @@ namespace cpa {
 constexpr int kBlock = 16;          // tokens per KV page
 constexpr int kChunkRows = 128;     // (token, head) query rows per chunk workgroup: 4 waves x 32
 constexpr int kKvTile = 64;         // keys per LDS-staged K/V tile in the chunk kernel (4 pages)
-#ifndef CPA_DECODE_WAVES_TARGET
-#define CPA_DECODE_WAVES_TARGET 4096
+// Decode waves resident at once on 256 CUs x 4 SIMDs: the decode kernel's
+// register use leaves room for 3 waves per SIMD at head_dim 128 and 4 at 64.
+inline int decode_waves_target(int head_dim) {
+#ifdef CPA_DECODE_WAVES_TARGET
+  (void)head_dim;
+  return CPA_DECODE_WAVES_TARGET;
+#else
+  return 256 * 4 * (head_dim > 64 ? 3 : 4);
 #endif
-constexpr int kDecodeWavesTarget = CPA_DECODE_WAVES_TARGET;  // decode waves to aim for
+}
 constexpr int kDecodeMaxSplit = 64 * kBlock;  // a decode split spans at most 64 pages
 constexpr int kChunkWgTarget = 1024;      // chunk workgroups to aim for when sizing KV splits
 constexpr int kChunkMinSplit = 256;       // fewest prefix keys worth a separate chunk piece
