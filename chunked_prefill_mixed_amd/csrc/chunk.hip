@@ -199,16 +199,26 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    // K fragments are read kAhead MFMAs before their use, so LDS latency
+    // hides behind the MFMAs in flight
+    constexpr int kAhead = 4;
+    uint4 ka[2 * KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int i = 0; i < 2 * KS; ++i)
+      ka[i] = *reinterpret_cast<const uint4*>(
+          &k_lds[(32 * (i & 1) + krow) * KSTR + 8 * half + 16 * (i >> 1)]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 a = *reinterpret_cast<const uint4*>(
-            &k_lds[(32 * kb + krow) * KSTR + 8 * half + 16 * ks]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, qf[ks]),
-                                                        s[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < 2 * KS; ++i)
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
+                                                         __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
+                                                         s[i & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 
     if constexpr (MASK) {
       const int key_base = kt * kKvTile;
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = fmaxf(mx, xor_lane(mx, 32));
+    mx = half_max(mx);
     // move the reference max only when this tile exceeds it by more than 2^8
     // (always on a row's first tile, where m is -inf)
     const bool grow = (mx - m) * scale_log2 > 8.f;
@@ -245,20 +255,22 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     }
     const float msc = m * scale_log2;
 
-    float psum = 0.f;
     uint4 pb[4];
+    // row sum of the bf16-rounded probabilities the PV product uses, two per
+    // v_dot2, four independent partial sums
+    float ps[4];
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
       float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 8; ++i)
         pv[i] = fast_exp2(__builtin_fmaf(s[kp >> 1][8 * (kp & 1) + i], scale_log2, -msc));
-        psum += pv[i];
-      }
       pb[kp] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+      ps[kp] = sum2_bf16(pb[kp].w,
+                         sum2_bf16(pb[kp].z, sum2_bf16(pb[kp].y, sum2_bf16(pb[kp].x, 0.f))));
     }
-    lsum += psum;
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // O^T += V^T P^T, one page (16 keys) per MFMA, the DB accumulator chains
     // interleaved
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   for (int kt = kt0; kt < kt_mask; ++kt) tile(std::integral_constant<bool, false>(), kt);
   for (int kt = kt_mask; kt < n_kv; ++kt) tile(std::integral_constant<bool, true>(), kt);
 
-  lsum += xor_lane(lsum, 32);
+  lsum = half_sum(lsum);
   if (row_ok && slot >= 0) {
     // one piece of a split tile: unnormalised partial for chunk_merge_kernel
     const int64_t pr = ((int64_t)slot * num_kv_heads + g) * kChunkRows + r;

@@ -73,6 +73,27 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }
 
+// Combine lane i with lane i ^ 32 in every lane.  v_permlane32_swap
+// exchanges lanes 32-63 of one register with lanes 0-31 of another, so after
+// swapping two copies of x each lane holds its own value and its partner's;
+// the leading s_nop covers the VALU-write-to-permlane-read wait states.
+__device__ __forceinline__ float half_max(float x) {
+  float y = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+  return fmaxf(x, y);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float y = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+  return x + y;
+}
+
+// acc + the two bf16 values packed in p (v_dot2_f32_bf16 against 1.0, 1.0)
+__device__ __forceinline__ float sum2_bf16(uint32_t p, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kQuadXor1>(x));
   x = fmaxf(x, dpp<kQuadXor2>(x));
