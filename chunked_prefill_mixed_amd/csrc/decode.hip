@@ -198,9 +198,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
   }
 }
 
-// Combine the splits of a decode row: one wave per (row, query head).  The
-// lanes read the splits' max and sum in parallel; each lane then owns D/64
-// output dimensions and sums the splits' fp32 partials for them.
+// Combine the splits of a decode row: one wave per (row, query head), each
+// lane owning D/64 output dimensions.  Splits are taken kMergeBatch at a
+// time, with every load of a batch (the splits' max and sum, broadcast to all
+// lanes, and this lane's partial values) issued before any is used, so a
+// batch costs one memory round trip; batches fold into a running max, sum and
+// output with the same 2^(m_i - M) rescaling.
+constexpr int kMergeBatch = 16;
+
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const int32_t* __restrict__ merges,
                                                    const int32_t* __restrict__ qsl, int num_q_heads,
@@ -210,24 +215,36 @@ __global__ __launch_bounds__(64) void merge_kernel(const int32_t* __restrict__ m
   const int4 e = reinterpret_cast<const int4*>(merges)[blockIdx.x];
   const int row = e.x, first = e.y, n = e.z;
   const int h = blockIdx.y, lane = threadIdx.x;
-  float M = neg_inf();
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, ws.m[(int64_t)(first + i) * num_q_heads + h]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int i = lane; i < n; i += 64) {
-    const int64_t ph = (int64_t)(first + i) * num_q_heads + h;
-    L += ws.l[ph] * fast_exp2(ws.m[ph] - M);
-  }
-  L = wave_sum(L);
+  float M = neg_inf(), L = 0.f;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < n; ++i) {
-    const int64_t ph = (int64_t)(first + i) * num_q_heads + h;
-    const float w = fast_exp2(ws.m[ph] - M);
+  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+    float mi[kMergeBatch], lv[kMergeBatch], a[kMergeBatch][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] += w * ws.acc[ph * D + lane + 64 * k];
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const bool in = i0 + i < n;
+      const int64_t ph = (int64_t)(first + (in ? i0 + i : i0)) * num_q_heads + h;
+      mi[i] = in ? ws.m[ph] : neg_inf();
+      lv[i] = ws.l[ph];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) a[i][k] = ws.acc[ph * D + lane + 64 * k];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, mi[i]);
+    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
+    L *= alpha;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
+      L += w * lv[i];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] += w * a[i][k];
+    }
+    M = Mb;
   }
   const int t = qsl[row];
   const float inv = 1.f / L;

@@ -17,7 +17,7 @@ inline int decode_waves_target(int head_dim) {
 #endif
 }
 constexpr int kDecodeMaxSplit = 64 * kBlock;  // a decode split spans at most 64 pages
-constexpr int kChunkWgTarget = 1024;      // chunk workgroups to aim for when sizing KV splits
+constexpr int kChunkWgTarget = 512;       // chunk workgroups resident at once (2 per CU): one round
 constexpr int kChunkMinSplit = 256;       // fewest prefix keys worth a separate chunk piece
 
 // Query tokens one chunk workgroup covers when G query heads share a KV head.
