@@ -16,7 +16,9 @@ pools and are rotated step by step, so no step finds its K/V in the 256 MB
 last-level cache from the previous step.
 
 Prints ONE JSON line on stdout.  Per-kernel durations come from HIP events
-recorded on the launch stream around each launch inside the timed region.
+recorded on the launch stream around each launch inside the timed region, on
+every fifth timed step (``--kernel-event-stride``); the other steps carry only
+a start and an end event, so the markers do not serialise the whole run.
 """
 
 from __future__ import annotations
@@ -206,11 +208,13 @@ class Instance:
                             ds.num_tokens, w.num_kv_heads, w.head_dim, 16, P(ds.k_cache),
                             P(ds.v_cache), self.stream)
 
-    def step(self, events, aux=None):
+    def step(self, events, aux=None, per_kernel=True):
         """One full step.  events: 8 torch events.  With ``aux`` (a second
         stream) the chunk kernel and its merge run on it, concurrently with the
         decode kernel and its merge on the main stream; both wait for the
-        append and the main stream waits for both."""
+        append and the main stream waits for both.  Without ``per_kernel`` only
+        the step's first and last events are recorded (no markers between the
+        launches)."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         self.build_host()
         self.dev.copy_(self.pinned, non_blocking=True)
@@ -221,6 +225,13 @@ class Instance:
         st = 0
         events[0].record(main)
         st |= lib.cpa_append_kv(*self.append_args)
+        if aux is None and not per_kernel:
+            for name in ("decode_kernel", "merge_kernel", "chunk_kernel", "chunk_merge_kernel"):
+                st |= lib.cpa_attention(*parts[name])
+            events[7].record(main)
+            if st != 0:
+                raise RuntimeError(f"launch failed with status {st}")
+            return
         events[1].record(main)
         if aux is None:
             st |= lib.cpa_attention(*parts["decode_kernel"])
@@ -320,6 +331,12 @@ def main():
                     help="run the chunk kernel and its merge on a second stream, concurrently "
                          "with the decode kernel and its merge (default: one stream, so each "
                          "kernel's HIP-event time is its own)")
+    ap.add_argument("--kernel-event-stride", type=int, default=5,
+                    help="record the per-kernel HIP events on every n-th timed step only (the "
+                         "others carry just the step's start and end events, since a marker "
+                         "between launches keeps a kernel from starting while the previous one "
+                         "drains); per-kernel durations average the sampled steps.  Keep it "
+                         "coprime to the number of rotated instances so each is sampled")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -368,8 +385,10 @@ def main():
     order = [(W + s) % len(insts) for s in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    stride = max(1, args.kernel_event_stride) if aux is None else 1
+    sampled = [s for s in range(K) if s % stride == 0]
     for s in range(K):
-        insts[order[s]].step(events[s], aux)
+        insts[order[s]].step(events[s], aux, per_kernel=(s % stride == 0))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -380,28 +399,31 @@ def main():
     times = {n: 0.0 for n in names}
     gpu_step = 0.0
     work = {"decode_bytes": 0, "chunk_flops": 0, "append_bytes": 0, "tokens": 0}
+    tokens = 0
     for s in range(K):
+        gpu_step += events[s][0].elapsed_time(events[s][7]) * 1e-3
+        tokens += insts[order[s]].work["tokens"]
+    for s in sampled:  # per-kernel durations and work over the sampled steps
         ev = events[s]
         for n, (a, b) in spans.items():
             times[n] += ev[a].elapsed_time(ev[b]) * 1e-3
-        gpu_step += ev[0].elapsed_time(ev[7]) * 1e-3
         wk = insts[order[s]].work
         for key in work:
             work[key] += wk[key]
-    tokens = work["tokens"]
+    NS = len(sampled)
     value = tokens / elapsed
 
     def rate(n, amount, scale):
         return amount / times[n] / scale if times[n] > 0 else None
 
     kernels = {
-        "append_kernel": {"avg_us": times["append_kernel"] / K * 1e6,
+        "append_kernel": {"avg_us": times["append_kernel"] / NS * 1e6,
                           "GB/s": rate("append_kernel", work["append_bytes"], 1e9)},
-        "decode_kernel": {"avg_us": times["decode_kernel"] / K * 1e6,
+        "decode_kernel": {"avg_us": times["decode_kernel"] / NS * 1e6,
                           "GB/s": rate("decode_kernel", work["decode_bytes"], 1e9)},
-        "merge_kernel": {"avg_us": times["merge_kernel"] / K * 1e6},
-        "chunk_merge_kernel": {"avg_us": times["chunk_merge_kernel"] / K * 1e6},
-        "chunk_kernel": {"avg_us": times["chunk_kernel"] / K * 1e6,
+        "merge_kernel": {"avg_us": times["merge_kernel"] / NS * 1e6},
+        "chunk_merge_kernel": {"avg_us": times["chunk_merge_kernel"] / NS * 1e6},
+        "chunk_kernel": {"avg_us": times["chunk_kernel"] / NS * 1e6,
                          "TFLOP/s": rate("chunk_kernel", work["chunk_flops"], 1e12)},
     }
     for n, peak, unit in (("append_kernel", HBM_PEAK_GBS, "GB/s"),
@@ -448,6 +470,7 @@ def main():
         "streams": ("decode and chunk on two streams, concurrently" if args.two_streams
                     else "one stream"),
         "gpu_step_us": gpu_step / K * 1e6,
+        "kernel_events": {"stride": stride, "sampled_steps": NS},
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host cores ...")
