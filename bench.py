@@ -3,9 +3,10 @@
 
 A step is one pass of the whole path over one packed batch: the host
 decode-first budget split and work plan (cpa_build_metadata), one H2D copy of
-the step metadata, the paged KV append, the split-KV decode kernel, its
-log-sum-exp merge and the MFMA prefill-chunk kernel with its merge, all on one
-stream (``--two-streams`` runs the chunk kernels on a second stream).
+the step metadata, the paged KV append (cpa_append_kv), then cpa_attention:
+the split-KV decode kernel, the MFMA prefill-chunk kernel and one log-sum-exp
+merge launch for the split pieces of both, all on one stream
+(``--two-streams`` runs the chunk kernel on a second stream).
 Inputs (q, new K/V, the paged KV pool) are resident in HBM before timing.
 
 Default workload (Page-1 defaults of the chunked-prefill essay): 32 decode
@@ -58,8 +59,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "device.h", "tiles.h"],
     "chunk_kernel": ["chunk.hip", "device.h", "tiles.h"],
     "append_kernel": ["append.hip", "device.h", "tiles.h"],
-    "merge_kernel": ["decode.hip", "device.h"],
-    "chunk_merge_kernel": ["chunk.hip", "device.h", "tiles.h"],
+    "merge_kernel": ["merge.hip", "device.h", "tiles.h"],
 }
 
 
@@ -186,17 +186,18 @@ class Instance:
         zero = dict(num_decode_splits=0, num_decode_merges=0, num_chunk_tiles=0,
                     num_chunk_merges=0)
         # one launch per call, in the library's own order, so HIP events can
-        # bracket each kernel
+        # bracket each kernel (both merge sections are one launch)
         sections = [
-            ("decode_kernel", "num_decode_splits", "decode_splits"),
-            ("chunk_kernel", "num_chunk_tiles", "chunk_tiles"),
-            ("merge_kernel", "num_decode_merges", "decode_merges"),
-            ("chunk_merge_kernel", "num_chunk_merges", "chunk_merges"),
+            ("decode_kernel", ("num_decode_splits",), "decode_splits"),
+            ("chunk_kernel", ("num_chunk_tiles",), "chunk_tiles"),
+            ("merge_kernel", ("num_decode_merges", "num_chunk_merges"), "decode_merges"),
         ]
-        for name, field, sec in sections:
-            counts = c.copy(**{**zero, field: getattr(c, field)})
+        for name, fields, sec in sections:
+            counts = c.copy(**{**zero, **{f: getattr(c, f) for f in fields}})
             self.parts.append((name, counts, head + (vp(plan_base + 4 * off[sec]),
                                                      ctypes.byref(counts)) + common_tail))
+        # the whole plan in one call, as a caller runs a step
+        self.full_args = head + (vp(plan_base), ctypes.byref(c)) + common_tail
         self.torch = torch
         self.aux_parts = {}
         if self.aux_stream is not None:
@@ -226,8 +227,7 @@ class Instance:
         events[0].record(main)
         st |= lib.cpa_append_kv(*self.append_args)
         if aux is None and not per_kernel:
-            for name in ("decode_kernel", "merge_kernel", "chunk_kernel", "chunk_merge_kernel"):
-                st |= lib.cpa_attention(*parts[name])
+            st |= lib.cpa_attention(*self.full_args)
             events[7].record(main)
             if st != 0:
                 raise RuntimeError(f"launch failed with status {st}")
@@ -236,26 +236,24 @@ class Instance:
         if aux is None:
             st |= lib.cpa_attention(*parts["decode_kernel"])
             events[2].record(main)
-            st |= lib.cpa_attention(*parts["merge_kernel"])
-            events[3].record(main)
-            events[4].record(main)
-            st |= lib.cpa_attention(*parts["chunk_kernel"])
             events[5].record(main)
-            st |= lib.cpa_attention(*parts["chunk_merge_kernel"])
+            st |= lib.cpa_attention(*parts["chunk_kernel"])
             events[6].record(main)
+            events[3].record(main)
+            st |= lib.cpa_attention(*parts["merge_kernel"])
+            events[4].record(main)
             events[7].record(main)
         else:
             aux.wait_event(events[1])
-            events[4].record(aux)
-            st |= lib.cpa_attention(*self.aux_parts["chunk_kernel"])
             events[5].record(aux)
-            st |= lib.cpa_attention(*self.aux_parts["chunk_merge_kernel"])
+            st |= lib.cpa_attention(*self.aux_parts["chunk_kernel"])
             events[6].record(aux)
             st |= lib.cpa_attention(*parts["decode_kernel"])
             events[2].record(main)
-            st |= lib.cpa_attention(*parts["merge_kernel"])
-            events[3].record(main)
             main.wait_event(events[6])
+            events[3].record(main)
+            st |= lib.cpa_attention(*parts["merge_kernel"])
+            events[4].record(main)
             events[7].record(main)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
@@ -328,8 +326,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-streams", action="store_true",
-                    help="run the chunk kernel and its merge on a second stream, concurrently "
-                         "with the decode kernel and its merge (default: one stream, so each "
+                    help="run the chunk kernel on a second stream, concurrently with the "
+                         "decode kernel; the merge follows both (default: one stream, so each "
                          "kernel's HIP-event time is its own)")
     ap.add_argument("--kernel-event-stride", type=int, default=5,
                     help="record the per-kernel HIP events on every n-th timed step only (the "
@@ -393,8 +391,8 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # (kernel, start event, end event) on the stream the kernel ran on
-    spans = {"append_kernel": (0, 1), "decode_kernel": (1, 2), "merge_kernel": (2, 3),
-             "chunk_kernel": (4, 5), "chunk_merge_kernel": (5, 6)}
+    spans = {"append_kernel": (0, 1), "decode_kernel": (1, 2), "chunk_kernel": (5, 6),
+             "merge_kernel": (3, 4)}
     names = list(spans)
     times = {n: 0.0 for n in names}
     gpu_step = 0.0
@@ -422,7 +420,6 @@ def main():
         "decode_kernel": {"avg_us": times["decode_kernel"] / NS * 1e6,
                           "GB/s": rate("decode_kernel", work["decode_bytes"], 1e9)},
         "merge_kernel": {"avg_us": times["merge_kernel"] / NS * 1e6},
-        "chunk_merge_kernel": {"avg_us": times["chunk_merge_kernel"] / NS * 1e6},
         "chunk_kernel": {"avg_us": times["chunk_kernel"] / NS * 1e6,
                          "TFLOP/s": rate("chunk_kernel", work["chunk_flops"], 1e12)},
     }
@@ -431,12 +428,6 @@ def main():
                           ("chunk_kernel", MFMA_BF16_PEAK_TFS, "TFLOP/s")):
         v = kernels[n].get(unit)
         kernels[n]["frac_of_peak"] = None if v is None else v / peak
-    kernels["chunk_plus_merge_TFLOP/s"] = (
-        work["chunk_flops"] / (times["chunk_kernel"] + times["chunk_merge_kernel"]) / 1e12
-        if times["chunk_kernel"] > 0 else None)
-    kernels["decode_plus_merge_GB/s"] = (
-        work["decode_bytes"] / (times["decode_kernel"] + times["merge_kernel"]) / 1e9
-        if times["decode_kernel"] > 0 else None)
 
     dominant = max(("decode_kernel", "chunk_kernel", "append_kernel"), key=lambda n: times[n])
     if dominant == "chunk_kernel":

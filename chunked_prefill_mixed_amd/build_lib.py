@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpa.so")
 
-HIP_SOURCES = ["append.hip", "decode.hip", "chunk.hip", "abi.hip"]
+HIP_SOURCES = ["append.hip", "decode.hip", "chunk.hip", "merge.hip", "abi.hip"]
 HOST_SOURCES = ["builder.cpp"]
 ARCH = os.environ.get("CPA_OFFLOAD_ARCH", "gfx950")
 

@@ -202,8 +202,8 @@ def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads,
 
 
 SECTIONS = (("decode_splits", "num_decode_splits", DECODE_SPLIT_WORDS),
-            ("decode_merges", "num_decode_merges", DECODE_MERGE_WORDS),
             ("chunk_tiles", "num_chunk_tiles", CHUNK_TILE_WORDS),
+            ("decode_merges", "num_decode_merges", DECODE_MERGE_WORDS),
             ("chunk_merges", "num_chunk_merges", CHUNK_MERGE_WORDS))
 
 

@@ -77,11 +77,11 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
            reinterpret_cast<float*>(base + wl.chk_l)};
   }
   const int32_t* splits = d_plan;
-  const int32_t* dmerges = splits + (size_t)n.num_decode_splits * CPA_DECODE_SPLIT_WORDS;
-  const int32_t* tiles = dmerges + (size_t)n.num_decode_merges * CPA_DECODE_MERGE_WORDS;
-  const int32_t* cmerges = tiles + (size_t)n.num_chunk_tiles * CPA_CHUNK_TILE_WORDS;
+  const int32_t* tiles = splits + (size_t)n.num_decode_splits * CPA_DECODE_SPLIT_WORDS;
+  const int32_t* dmerges = tiles + (size_t)n.num_chunk_tiles * CPA_CHUNK_TILE_WORDS;
+  const int32_t* cmerges = dmerges + (size_t)n.num_decode_merges * CPA_DECODE_MERGE_WORDS;
 
-  // decode splits and chunk tiles are independent; merges follow what they merge
+  // decode splits and chunk tiles are independent; the merges (one launch) follow them
   if (n.num_decode_splits > 0) {
     st = status_of(cpa::launch_decode(q, k_cache, v_cache, d_block_table, bt_stride,
                                       d_query_start_loc, splits, n.num_decode_splits, num_q_heads,
@@ -94,14 +94,10 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
                                      num_q_heads, num_kv_heads, head_dim, sl2, out, lse, cws, s));
     if (st != CPA_OK) return st;
   }
-  if (n.num_decode_merges > 0) {
-    st = status_of(cpa::launch_merge(dmerges, n.num_decode_merges, d_query_start_loc, num_q_heads,
-                                     head_dim, dws, out, lse, s));
-    if (st != CPA_OK) return st;
-  }
-  if (n.num_chunk_merges > 0) {
-    st = status_of(cpa::launch_chunk_merge(cmerges, n.num_chunk_merges, d_query_start_loc,
-                                           num_q_heads, num_kv_heads, head_dim, cws, out, lse, s));
+  if (n.num_decode_merges > 0 || n.num_chunk_merges > 0) {
+    st = status_of(cpa::launch_merges(dmerges, n.num_decode_merges, cmerges, n.num_chunk_merges,
+                                      d_query_start_loc, num_q_heads, num_kv_heads, head_dim, dws,
+                                      cws, out, lse, s));
     if (st != CPA_OK) return st;
   }
   return CPA_OK;

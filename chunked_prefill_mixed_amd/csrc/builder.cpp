@@ -269,7 +269,7 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   if (out->plan) {
     if (words > out->plan_capacity) return CPA_ERR_CAPACITY;
     int32_t* w = out->plan;
-    for (const std::vector<int32_t>* sec : {&dsplits, &dmerges, &tiles, &cmerges}) {
+    for (const std::vector<int32_t>* sec : {&dsplits, &tiles, &dmerges, &cmerges}) {
       std::memcpy(w, sec->data(), sec->size() * sizeof(int32_t));
       w += sec->size();
     }

@@ -29,7 +29,7 @@
 // A work item may cover only a piece [kv_begin, kv_end) of its tile's keys
 // (a long, fully visible prefix is cut into pieces so small chunks still fill
 // the GPU); such a piece writes its unnormalised fp32 output, running max and
-// sum, and chunk_merge_kernel combines the pieces:
+// sum, and merge_kernel (merge.hip) combines the pieces:
 //   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
 // The running max used as the exponent reference is only moved when a tile's
 // max exceeds it by more than 2^8, so the 16-64 accumulator rescale almost
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
 
   lsum = half_sum(lsum);
   if (row_ok && slot >= 0) {
-    // one piece of a split tile: unnormalised partial for chunk_merge_kernel
+    // one piece of a split tile: unnormalised partial for merge_kernel
     const int64_t pr = ((int64_t)slot * num_kv_heads + g) * kChunkRows + r;
     float* acc = part.acc + pr * D;
 #pragma unroll
@@ -338,62 +338,6 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   }
 }
 
-// Combine the pieces of split chunk tiles.  A workgroup takes RPW rows of
-// one (merge entry, KV head); each row is handled by LPR = D/4 lanes, each
-// owning 4 consecutive d values, so a partial row is one contiguous sweep.
-// The lanes of a row read the pieces' max and sum in parallel (one piece per
-// lane), then every lane sums the pieces' fp32 partials for its 4 values
-// with up to 8 loads in flight.
-template <int D, int G>
-__global__ __launch_bounds__(256) void chunk_merge_kernel(
-    const int32_t* __restrict__ merges, const int32_t* __restrict__ qsl, int num_q_heads,
-    int num_kv_heads, Partials part, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int LPR = D / 4;             // lanes per row
-  constexpr int RPW = 256 / LPR;         // rows per workgroup
-  constexpr int RG = kChunkRows / RPW;   // workgroups per (merge entry, KV head)
-  const int rg = blockIdx.x % RG;
-  const int g = (blockIdx.x / RG) % num_kv_heads;
-  const int4* ep = reinterpret_cast<const int4*>(merges) + 2 * (blockIdx.x / (RG * num_kv_heads));
-  const int4 e0 = ep[0], e1 = ep[1];
-  const int row = e0.x, qb = e0.y, qe = e0.z, first = e0.w, n = e1.x;
-  const int li = threadIdx.x % LPR;
-  const int r = rg * RPW + threadIdx.x / LPR;
-  const int j = qb + r / G;
-  if (j >= qe) return;  // past the chunk end (no barrier below)
-  const int64_t stride = (int64_t)num_kv_heads * kChunkRows;  // rows between consecutive slots
-  const int64_t base = ((int64_t)first * num_kv_heads + g) * kChunkRows + r;
-
-  float M = neg_inf();
-  for (int i = li; i < n; i += LPR) M = fmaxf(M, part.m[base + i * stride]);
-#pragma unroll
-  for (int k = 1; k < LPR; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, LPR));
-  float L = 0.f;
-  for (int i = li; i < n; i += LPR) L += part.l[base + i * stride] * fast_exp2(part.m[base + i * stride] - M);
-#pragma unroll
-  for (int k = 1; k < LPR; k <<= 1) L += __shfl_xor(L, k, LPR);
-
-  const int d = 4 * li;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < n; i0 += LPR) {
-    const float wl = (i0 + li < n) ? fast_exp2(part.m[base + (i0 + li) * stride] - M) : 0.f;
-    const int cnt = min(LPR, n - i0);
-#pragma unroll 8
-    for (int k = 0; k < cnt; ++k) {
-      const float w = __shfl(wl, k, LPR);
-      const float4 a = *reinterpret_cast<const float4*>(part.acc + (base + (i0 + k) * stride) * D + d);
-      o.x += w * a.x; o.y += w * a.y; o.z += w * a.z; o.w += w * a.w;
-    }
-  }
-  const float inv = 1.f / L;
-  const int hq = g * G + (r % G);
-  const int t0 = qsl[row];
-  uint2 v;
-  v.x = pack_bf16x2(o.x * inv, o.y * inv);
-  v.y = pack_bf16x2(o.z * inv, o.w * inv);
-  *reinterpret_cast<uint2*>(out + ((int64_t)(t0 + j) * num_q_heads + hq) * D + d) = v;
-  if (lse && li == 0) lse[(int64_t)(t0 + j) * num_q_heads + hq] = (M + __log2f(L)) * kLn2;
-}
-
 template <int D, int G>
 static void launch_chunk_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
@@ -420,25 +364,6 @@ hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache,
   CPA_CHK(128, 1) CPA_CHK(128, 2) CPA_CHK(128, 4) CPA_CHK(128, 8)
   CPA_CHK(64, 1) CPA_CHK(64, 2) CPA_CHK(64, 4) CPA_CHK(64, 8)
 #undef CPA_CHK
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_chunk_merge(const int32_t* merges, int num_merges, const int32_t* qsl,
-                              int num_q_heads, int num_kv_heads, int head_dim, Partials part,
-                              void* out, float* lse, hipStream_t stream) {
-  const int G = num_q_heads / num_kv_heads;
-  const int groups = kChunkRows / (256 / (head_dim / 4));
-  dim3 grid(num_merges * num_kv_heads * groups), block(256);
-  auto* o = static_cast<uint16_t*>(out);
-#define CPA_CMG(DD, GG)                                                                        \
-  if (head_dim == DD && G == GG) {                                                              \
-    hipLaunchKernelGGL((chunk_merge_kernel<DD, GG>), grid, block, 0, stream, merges, qsl,       \
-                       num_q_heads, num_kv_heads, part, o, lse);                                \
-    return hipGetLastError();                                                                   \
-  }
-  CPA_CMG(128, 1) CPA_CMG(128, 2) CPA_CMG(128, 4) CPA_CMG(128, 8)
-  CPA_CMG(64, 1) CPA_CMG(64, 2) CPA_CMG(64, 4) CPA_CMG(64, 8)
-#undef CPA_CMG
   return hipErrorInvalidValue;
 }
 

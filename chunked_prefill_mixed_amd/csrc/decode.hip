@@ -1,4 +1,4 @@
-// Split-KV decode attention and the log-sum-exp merge of its pieces.
+// Split-KV decode attention (its pieces are merged by merge_kernel, merge.hip).
 //
 // A decode row's single query reads its whole cached context from HBM each
 // step ("How Chunked Prefill Stops Decode Starvation", "The stall"; tbr8.org
@@ -25,7 +25,8 @@
 // exceeds it by more than 2^8 (always on the first page), so the accumulator
 // rescale is rare; numerator and denominator share the reference.  A row
 // covered by one piece writes its bf16 output directly; otherwise each piece
-// writes unnormalised fp32 (acc, max, sum) and merge_kernel combines them:
+// writes unnormalised fp32 (acc, max, sum) and merge_kernel (merge.hip) combines
+// them:
 //   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
 
 #include "device.h"
@@ -198,62 +199,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
   }
 }
 
-// Combine the splits of a decode row: one wave per (row, query head), each
-// lane owning D/64 output dimensions.  Splits are taken kMergeBatch at a
-// time, with every load of a batch (the splits' max and sum, broadcast to all
-// lanes, and this lane's partial values) issued before any is used, so a
-// batch costs one memory round trip; batches fold into a running max, sum and
-// output with the same 2^(m_i - M) rescaling.
-constexpr int kMergeBatch = 16;
-
-template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(const int32_t* __restrict__ merges,
-                                                   const int32_t* __restrict__ qsl, int num_q_heads,
-                                                   Partials ws, uint16_t* __restrict__ out,
-                                                   float* __restrict__ lse) {
-  constexpr int PER = D / 64;
-  const int4 e = reinterpret_cast<const int4*>(merges)[blockIdx.x];
-  const int row = e.x, first = e.y, n = e.z;
-  const int h = blockIdx.y, lane = threadIdx.x;
-  float M = neg_inf(), L = 0.f;
-  float o[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
-    float mi[kMergeBatch], lv[kMergeBatch], a[kMergeBatch][PER];
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      const bool in = i0 + i < n;
-      const int64_t ph = (int64_t)(first + (in ? i0 + i : i0)) * num_q_heads + h;
-      mi[i] = in ? ws.m[ph] : neg_inf();
-      lv[i] = ws.l[ph];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) a[i][k] = ws.acc[ph * D + lane + 64 * k];
-    }
-    float Mb = M;
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, mi[i]);
-    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
-    L *= alpha;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] *= alpha;
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
-      L += w * lv[i];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] += w * a[i][k];
-    }
-    M = Mb;
-  }
-  const int t = qsl[row];
-  const float inv = 1.f / L;
-#pragma unroll
-  for (int k = 0; k < PER; ++k)
-    out[((int64_t)t * num_q_heads + h) * D + lane + 64 * k] = to_bf16(o[k] * inv);
-  if (lse && lane == 0) lse[(int64_t)t * num_q_heads + h] = (M + __log2f(L)) * kLn2;
-}
-
 template <int D, int G>
 static void launch_decode_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                             int bt_stride, const int32_t* splits, int num_splits, int hq, int hkv,
@@ -281,18 +226,6 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
   CPA_DEC(64, 1) CPA_DEC(64, 2) CPA_DEC(64, 4) CPA_DEC(64, 8)
 #undef CPA_DEC
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const int32_t* merges, int num_merges, const int32_t* qsl, int num_q_heads,
-                        int head_dim, Partials ws, void* out, float* lse, hipStream_t stream) {
-  dim3 grid(num_merges, num_q_heads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64), 0, stream, merges, qsl, num_q_heads, ws,
-                       static_cast<uint16_t*>(out), lse);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, merges, qsl, num_q_heads, ws,
-                       static_cast<uint16_t*>(out), lse);
-  return hipGetLastError();
 }
 
 }  // namespace cpa

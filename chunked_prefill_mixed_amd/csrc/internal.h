@@ -25,17 +25,16 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
                          int head_dim, float scale_log2, void* out, float* lse, Partials ws,
                          hipStream_t stream);
 
-hipError_t launch_merge(const int32_t* merges, int num_merges, const int32_t* qsl, int num_q_heads,
-                        int head_dim, Partials ws, void* out, float* lse, hipStream_t stream);
-
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
                         int head_dim, float scale_log2, void* out, float* lse, Partials part,
                         hipStream_t stream);
 
-hipError_t launch_chunk_merge(const int32_t* merges, int num_merges, const int32_t* qsl,
-                              int num_q_heads, int num_kv_heads, int head_dim, Partials part,
-                              void* out, float* lse, hipStream_t stream);
+// Both merges of a step in one launch (either count may be 0).
+hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const int32_t* cmerges,
+                         int num_chunk_merges, const int32_t* qsl, int num_q_heads,
+                         int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
+                         float* lse, hipStream_t stream);
 
 }  // namespace cpa

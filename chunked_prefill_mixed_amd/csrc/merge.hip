@@ -1,0 +1,173 @@
+// Log-sum-exp merge of split decode rows and split chunk tiles, one launch.
+//
+// A row whose keys were cut into pieces has, per piece i and query head, an
+// unnormalised fp32 output acc_i, the max m_i (log2 units of the scaled score)
+// and the sum l_i of the piece's weights relative to m_i.  The exact softmax
+// output over all the row's keys is
+//   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L,
+// the incremental-softmax identity the split relies on (tbr8.org deep dive
+// 7.2 names the incremental computation; the pieces never need correcting
+// because each covers a fixed key range).  lse = (M + log2 L) ln 2.
+//
+// Workgroups [0, chunk_blocks) merge chunk tiles, the rest decode rows, so
+// both merges of a step cost one launch.  Neither part uses a barrier.
+
+#include "device.h"
+#include "internal.h"
+#include "tiles.h"
+
+namespace cpa {
+
+// One wave per (decode row, query head), each lane owning D/64 output
+// dimensions.  Splits are taken kDecodeMergeBatch at a time, every load of a
+// batch (the splits' max and sum, broadcast to all lanes, and this lane's
+// partial values) issued before any is used, so a batch costs one memory
+// round trip; batches fold into a running max, sum and output.
+constexpr int kDecodeMergeBatch = 16;
+
+template <int D>
+__device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ merges, int entry,
+                                                  int h, const int32_t* __restrict__ qsl,
+                                                  int num_q_heads, const Partials& ws,
+                                                  uint16_t* __restrict__ out,
+                                                  float* __restrict__ lse) {
+  constexpr int PER = D / 64;
+  const int4 e = reinterpret_cast<const int4*>(merges)[entry];
+  const int row = e.x, first = e.y, n = e.z;
+  const int lane = threadIdx.x & 63;
+  float M = neg_inf(), L = 0.f;
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kDecodeMergeBatch) {
+    float mi[kDecodeMergeBatch], lv[kDecodeMergeBatch], a[kDecodeMergeBatch][PER];
+#pragma unroll
+    for (int i = 0; i < kDecodeMergeBatch; ++i) {
+      const bool in = i0 + i < n;
+      const int64_t ph = (int64_t)(first + (in ? i0 + i : i0)) * num_q_heads + h;
+      mi[i] = in ? ws.m[ph] : neg_inf();
+      lv[i] = ws.l[ph];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) a[i][k] = ws.acc[ph * D + lane + 64 * k];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kDecodeMergeBatch; ++i) Mb = fmaxf(Mb, mi[i]);
+    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
+    L *= alpha;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kDecodeMergeBatch; ++i) {
+      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
+      L += w * lv[i];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] += w * a[i][k];
+    }
+    M = Mb;
+  }
+  const int t = qsl[row];
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    out[((int64_t)t * num_q_heads + h) * D + lane + 64 * k] = to_bf16(o[k] * inv);
+  if (lse && lane == 0) lse[(int64_t)t * num_q_heads + h] = (M + __log2f(L)) * kLn2;
+}
+
+// RPW rows of one (chunk merge entry, KV head) per workgroup; each row is
+// handled by LPR = D/4 lanes, each owning 4 consecutive d values, so a partial
+// row is one contiguous sweep.  The lanes of a row read the pieces' max and
+// sum in parallel (one piece per lane), then every lane sums the pieces' fp32
+// partials for its 4 values with up to 8 loads in flight.
+template <int D, int G>
+__device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ merges, int block,
+                                                 const int32_t* __restrict__ qsl, int num_q_heads,
+                                                 int num_kv_heads, const Partials& part,
+                                                 uint16_t* __restrict__ out,
+                                                 float* __restrict__ lse) {
+  constexpr int LPR = D / 4;             // lanes per row
+  constexpr int RPW = 256 / LPR;         // rows per workgroup
+  constexpr int RG = kChunkRows / RPW;   // workgroups per (merge entry, KV head)
+  const int rg = block % RG;
+  const int g = (block / RG) % num_kv_heads;
+  const int4* ep = reinterpret_cast<const int4*>(merges) + 2 * (block / (RG * num_kv_heads));
+  const int4 e0 = ep[0], e1 = ep[1];
+  const int row = e0.x, qb = e0.y, qe = e0.z, first = e0.w, n = e1.x;
+  const int li = threadIdx.x % LPR;
+  const int r = rg * RPW + threadIdx.x / LPR;
+  const int j = qb + r / G;
+  if (j >= qe) return;  // past the chunk end
+  const int64_t stride = (int64_t)num_kv_heads * kChunkRows;  // rows between consecutive slots
+  const int64_t base = ((int64_t)first * num_kv_heads + g) * kChunkRows + r;
+
+  float M = neg_inf();
+  for (int i = li; i < n; i += LPR) M = fmaxf(M, part.m[base + i * stride]);
+#pragma unroll
+  for (int k = 1; k < LPR; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, LPR));
+  float L = 0.f;
+  for (int i = li; i < n; i += LPR)
+    L += part.l[base + i * stride] * fast_exp2(part.m[base + i * stride] - M);
+#pragma unroll
+  for (int k = 1; k < LPR; k <<= 1) L += __shfl_xor(L, k, LPR);
+
+  const int d = 4 * li;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < n; i0 += LPR) {
+    const float wl = (i0 + li < n) ? fast_exp2(part.m[base + (i0 + li) * stride] - M) : 0.f;
+    const int cnt = min(LPR, n - i0);
+#pragma unroll 8
+    for (int k = 0; k < cnt; ++k) {
+      const float w = __shfl(wl, k, LPR);
+      const float4 a =
+          *reinterpret_cast<const float4*>(part.acc + (base + (i0 + k) * stride) * D + d);
+      o.x += w * a.x; o.y += w * a.y; o.z += w * a.z; o.w += w * a.w;
+    }
+  }
+  const float inv = 1.f / L;
+  const int hq = g * G + (r % G);
+  const int t0 = qsl[row];
+  uint2 v;
+  v.x = pack_bf16x2(o.x * inv, o.y * inv);
+  v.y = pack_bf16x2(o.z * inv, o.w * inv);
+  *reinterpret_cast<uint2*>(out + ((int64_t)(t0 + j) * num_q_heads + hq) * D + d) = v;
+  if (lse && li == 0) lse[(int64_t)(t0 + j) * num_q_heads + hq] = (M + __log2f(L)) * kLn2;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void merge_kernel(
+    const int32_t* __restrict__ dmerges, int num_decode_pairs, const int32_t* __restrict__ cmerges,
+    int chunk_blocks, const int32_t* __restrict__ qsl, int num_q_heads, int num_kv_heads,
+    Partials dws, Partials cws, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  if ((int)blockIdx.x < chunk_blocks) {
+    merge_chunk_rows<D, G>(cmerges, blockIdx.x, qsl, num_q_heads, num_kv_heads, cws, out, lse);
+    return;
+  }
+  // four (decode row, query head) pairs per workgroup, one per wave
+  const int pair = ((int)blockIdx.x - chunk_blocks) * 4 + (threadIdx.x >> 6);
+  if (pair >= num_decode_pairs) return;
+  merge_decode_head<D>(dmerges, pair / num_q_heads, pair % num_q_heads, qsl, num_q_heads, dws,
+                       out, lse);
+}
+
+hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const int32_t* cmerges,
+                         int num_chunk_merges, const int32_t* qsl, int num_q_heads,
+                         int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
+                         float* lse, hipStream_t stream) {
+  const int G = num_q_heads / num_kv_heads;
+  const int chunk_blocks = num_chunk_merges * num_kv_heads * (kChunkRows / (256 / (head_dim / 4)));
+  const int pairs = num_decode_merges * num_q_heads;
+  const dim3 grid(chunk_blocks + (pairs + 3) / 4), block(256);
+  auto* o = static_cast<uint16_t*>(out);
+#define CPA_MRG(DD, GG)                                                                        \
+  if (head_dim == DD && G == GG) {                                                              \
+    hipLaunchKernelGGL((merge_kernel<DD, GG>), grid, block, 0, stream, dmerges, pairs, cmerges, \
+                       chunk_blocks, qsl, num_q_heads, num_kv_heads, dws, cws, o, lse);         \
+    return hipGetLastError();                                                                   \
+  }
+  CPA_MRG(128, 1) CPA_MRG(128, 2) CPA_MRG(128, 4) CPA_MRG(128, 8)
+  CPA_MRG(64, 1) CPA_MRG(64, 2) CPA_MRG(64, 4) CPA_MRG(64, 8)
+#undef CPA_MRG
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cpa

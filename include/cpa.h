@@ -104,10 +104,10 @@ typedef struct {
 } cpa_build_params_t;
 
 /* Counts of the device work plan built by cpa_build_metadata.  The plan is one
- * int32 array, in this order: num_decode_splits entries of
- * CPA_DECODE_SPLIT_WORDS, num_decode_merges of CPA_DECODE_MERGE_WORDS,
- * num_chunk_tiles of CPA_CHUNK_TILE_WORDS, num_chunk_merges of
- * CPA_CHUNK_MERGE_WORDS.  A chunk tile covers 128 (token, query head) rows of
+ * int32 array of four sections, in this order: num_decode_splits entries of
+ * CPA_DECODE_SPLIT_WORDS, num_chunk_tiles of CPA_CHUNK_TILE_WORDS,
+ * num_decode_merges of CPA_DECODE_MERGE_WORDS, num_chunk_merges of
+ * CPA_CHUNK_MERGE_WORDS (the two merge sections run as one launch).  A chunk tile covers 128 (token, query head) rows of
  * one KV head: 128 / (num_q_heads / num_kv_heads) tokens. */
 typedef struct {
   int32_t num_decode_splits;   /* one wave per (split, KV head) */
@@ -211,12 +211,13 @@ size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int 
  * even); lse[t][h] = log(sum_k exp(scale * <q, K[k]>)) if lse is non-NULL.
  *
  * d_plan is the plan from cpa_build_metadata copied to the device, with its
- * counts in *counts (host pointer).  Any subset of the plan's sections may be
- * run by passing counts with the other sections set to 0 and d_plan pointing
- * at the first section run.  The decode sections and the chunk sections are
- * independent (they touch different output rows), so after this step's append
- * they may run concurrently on two streams; a merge section must run after
- * the split or tile section it merges, on the same stream or after an event.  workspace must hold
+ * counts in *counts (host pointer).  A contiguous run of the plan's sections
+ * may be run alone by passing counts with the other sections set to 0 and
+ * d_plan pointing at the first section run.  The decode and the chunk
+ * sections are independent (they touch different output rows), so after this
+ * step's append they may run concurrently on two streams; a merge section must
+ * run after the split or tile section it merges, on the same stream or after
+ * an event.  Both merge sections present in one call run as one launch.  workspace must hold
  * cpa_workspace_size(counts, ...) bytes (may be NULL when nothing is split);
  * its contents need no initialisation.  The append of this step must already
  * be enqueued on the same stream.  d_seq_lens is not read (the plan carries
