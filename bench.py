@@ -277,6 +277,64 @@ def config_key(config: int) -> str:
     return workloads.CONFIG_NAMES[config]
 
 
+def measured_peaks(torch, build_lib):
+    """What this machine sustains: a streaming read of 2 GiB, a streaming copy of
+    2 GiB (bytes read + bytes written over time) and an MFMA-only loop of bf16
+    32x32x16 chains at two workgroups per CU, each timed with HIP events over 5
+    runs after 2 warm-up runs (libcpa_peaks.so)."""
+    lib = ctypes.CDLL(build_lib.PEAKS_LIB)
+    lib.cpa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_void_p]
+    lib.cpa_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.cpa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    wgs, iters = 2 * 256, 4000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    rout = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def copy():
+        if lib.cpa_peak_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                             nbytes, stream) != 0:
+            raise RuntimeError("peak copy launch failed")
+
+    def read():
+        if lib.cpa_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes,
+                             ctypes.c_void_p(rout.data_ptr()), stream) != 0:
+            raise RuntimeError("peak read launch failed")
+
+    def mfma():
+        if lib.cpa_peak_mfma(ctypes.c_void_p(out.data_ptr()), wgs, iters, stream) != 0:
+            raise RuntimeError("peak MFMA launch failed")
+
+    t_read = timed(read)
+    t_copy = timed(copy)
+    t_mfma = timed(mfma)
+    del src, dst, out, rout
+    torch.cuda.empty_cache()
+    return {"hbm_read_GB/s": nbytes / t_read / 1e9,
+            "hbm_copy_GB/s": 2 * nbytes / t_copy / 1e9,
+            "mfma_bf16_TFLOP/s": wgs * 4 * iters * 4 * 32768 / t_mfma / 1e12,
+            "method": "streaming device read of 2 GiB; streaming device copy of 2 GiB (read + "
+                      "write bytes); MFMA-only loop, "
+                      "4 independent v_mfma_f32_32x32x16_bf16 chains per wave, 2 workgroups "
+                      "of 4 waves per CU; HIP events, 5 runs after 2 warm-up"}
+
+
 def cpu_baseline(workloads_list, seconds: float):
     """The fp64 oracle (as it stands) on the host cores, whole steps of the
     same instances, round-robin until ``seconds`` of CPU work have run."""
@@ -360,7 +418,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}))
         return
-    if not os.path.exists(cpa.LIB_PATH):
+    if not (os.path.exists(cpa.LIB_PATH) and os.path.exists(build_lib.PEAKS_LIB)):
         build_lib.build()
     cpa.load()
 
@@ -439,6 +497,16 @@ def main():
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
     roofline["traffic"] = traffic_for(dominant, args.config)
+    peaks = measured_peaks(torch, build_lib)
+    for n, key, unit in (("append_kernel", "hbm_copy_GB/s", "GB/s"),
+                         ("decode_kernel", "hbm_read_GB/s", "GB/s"),
+                         ("chunk_kernel", "mfma_bf16_TFLOP/s", "TFLOP/s")):
+        v = kernels[n].get(unit)
+        kernels[n]["frac_of_measured"] = None if v is None else v / peaks[key]
+    roofline["measured_peak"] = peaks[{"mfma": "mfma_bf16_TFLOP/s", "hbm": "hbm_read_GB/s"}
+                                      [roofline["bound"]] if dominant != "append_kernel"
+                                      else "hbm_copy_GB/s"]
+    roofline["frac_of_measured"] = roofline["achieved"] / roofline["measured_peak"]
 
     result = {
         "metric": METRIC,
@@ -461,6 +529,7 @@ def main():
         "streams": ("decode and chunk on two streams, concurrently" if args.two_streams
                     else "one stream"),
         "gpu_step_us": gpu_step / K * 1e6,
+        "measured_peaks": peaks,
         "kernel_events": {"stride": stride, "sampled_steps": NS},
     }
     if not args.no_cpu_baseline:

@@ -93,9 +93,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
     const auto kr = make_page_rsrc(k_cache + page, PAGE_BYTES);
     const auto vr = make_page_rsrc(v_cache + page, PAGE_BYTES);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kd[kk] = buffer_load16(kr, kbyte + 64 * kk);
+    for (int kk = 0; kk < KK; ++kk) kd[kk] = buffer_load16<kNonTemporal>(kr, kbyte + 64 * kk);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) vd[mb] = buffer_load8(vr, vbyte + 512 * mb);
+    for (int mb = 0; mb < MB; ++mb) vd[mb] = buffer_load8<kNonTemporal>(vr, vbyte + 512 * mb);
   };
 
   float m = neg_inf(), lsum = 0.f;

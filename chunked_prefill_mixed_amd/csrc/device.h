@@ -49,13 +49,18 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_page_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
+// Cache policy of a load: 0 = default, kNonTemporal = streamed once (the nt
+// bit), which spares the caches data that no other wave will read again.
+constexpr int kNonTemporal = 2;
 // 16 bytes at byte offset off of the resource (buffer_load_dwordx4).
+template <int POLICY = 0>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
 }
 // 8 bytes at byte offset off of the resource (buffer_load_dwordx2).
+template <int POLICY = 0>
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
 }
 
 // DPP lane exchanges inside a 16-lane row.
