@@ -307,3 +307,25 @@ def test_empty_step(lib):
     m = build([], 16)
     assert m["num_seqs"] == 0 and m["num_tokens"] == 0
     assert m["counts"].num_decode_splits == 0 and m["counts"].num_chunk_tiles == 0
+
+
+def test_budget_sweep_schedule(lib):
+    """The budget sweep's steps follow the decode-first split: 32 streams plus
+    an 8192-token prompt give chunks of B - 32 tokens and ceil(8192 / (B - 32))
+    passes ("Chunked Prefill" (deepconcepts.dev): 224/480/4064-token chunks,
+    37/18/5/1 passes at budgets 256/512/2048/8224), the last chunk taking the
+    rest; the streams' contexts grow by one token per step."""
+    from chunked_prefill_mixed_amd import sweep
+    ctx = sweep.stream_contexts()
+    assert len(ctx) == 32 and ctx.min() >= 512 and ctx.max() <= 4096
+    for budget, chunk, passes in ((256, 224, 37), (512, 480, 18), (2048, 2016, 5),
+                                  (4096, 4064, 3), (8224, 8192, 1)):
+        steps = sweep.schedule(budget, ctx)
+        assert len(steps) == passes, budget
+        sizes = [int(m["num_scheduled"][32]) for _, m in steps]
+        assert sizes[:-1] == [chunk] * (passes - 1) and sum(sizes) == 8192, budget
+        for k, (reqs, m) in enumerate(steps):
+            assert m["num_decodes"] == 32 and list(m["context_lens"][:32]) == list(ctx + k)
+            assert m["context_lens"][32] == k * chunk
+    with pytest.raises(ValueError):
+        sweep.schedule(32, ctx)
