@@ -199,6 +199,7 @@ class Instance:
         # the whole plan in one call, as a caller runs a step
         self.full_args = head + (vp(plan_base), ctypes.byref(c)) + common_tail
         self.torch = torch
+        self.graph = None
         self.aux_parts = {}
         if self.aux_stream is not None:
             aux_tail = common_tail[:-1] + (vp(self.aux_stream.cuda_stream),)
@@ -209,13 +210,31 @@ class Instance:
                             ds.num_tokens, w.num_kv_heads, w.head_dim, 16, P(ds.k_cache),
                             P(ds.v_cache), self.stream)
 
+    def capture(self):
+        """Append + the whole attention call captured as one HIP graph on a
+        capture stream; unsampled steps then replay it (the metadata copy stays
+        outside the graph, before the replay on the same stream)."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()  # default priority
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=s):
+            cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            st = self.lib.cpa_append_kv(*self.append_args[:-1], cs)
+            st |= self.lib.cpa_attention(*self.full_args[:-1], cs)
+        torch.cuda.current_stream().wait_stream(s)
+        if st != 0:
+            raise RuntimeError(f"launch failed during capture with status {st}")
+        self.graph = g
+
     def step(self, events, aux=None, per_kernel=True):
         """One full step.  events: 8 torch events.  With ``aux`` (a second
-        stream) the chunk kernel and its merge run on it, concurrently with the
-        decode kernel and its merge on the main stream; both wait for the
-        append and the main stream waits for both.  Without ``per_kernel`` only
-        the step's first and last events are recorded (no markers between the
-        launches)."""
+        stream) the chunk kernel runs on it, concurrently with the decode
+        kernel on the main stream; both wait for the append, and the merge
+        follows both on the main stream.  Without ``per_kernel`` only the
+        step's first and last events are recorded (no markers between the
+        launches), and the step is one cpa_attention call, or the replay of
+        the captured graph with ``--graph``."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         self.build_host()
         self.dev.copy_(self.pinned, non_blocking=True)
@@ -225,9 +244,13 @@ class Instance:
         parts = dict((name, args) for name, _, args in self.parts)
         st = 0
         events[0].record(main)
-        st |= lib.cpa_append_kv(*self.append_args)
+        if self.graph is None or per_kernel or aux is not None:
+            st |= lib.cpa_append_kv(*self.append_args)
         if aux is None and not per_kernel:
-            st |= lib.cpa_attention(*self.full_args)
+            if self.graph is not None:
+                self.graph.replay()
+            else:
+                st |= lib.cpa_attention(*self.full_args)
             events[7].record(main)
             if st != 0:
                 raise RuntimeError(f"launch failed with status {st}")
@@ -387,6 +410,10 @@ def main():
                     help="run the chunk kernel on a second stream, concurrently with the "
                          "decode kernel; the merge follows both (default: one stream, so each "
                          "kernel's HIP-event time is its own)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each instance's append + attention as one captured HIP graph on "
+                         "the unsampled steps (the host metadata build and its copy still run "
+                         "every step, outside the graph)")
     ap.add_argument("--kernel-event-stride", type=int, default=5,
                     help="record the per-kernel HIP events on every n-th timed step only (the "
                          "others carry just the step's start and end events, since a marker "
@@ -436,6 +463,12 @@ def main():
     for s in range(W):
         insts[s % len(insts)].step(ev_w, aux)
     torch.cuda.synchronize()
+    if args.graph and aux is None:
+        for inst in insts:
+            inst.capture()
+        for s in range(len(insts)):  # one replay each before timing
+            insts[s].step(ev_w, None, per_kernel=False)
+        torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(K)]
     order = [(W + s) % len(insts) for s in range(K)]
@@ -528,6 +561,7 @@ def main():
         "kernels": kernels,
         "streams": ("decode and chunk on two streams, concurrently" if args.two_streams
                     else "one stream"),
+        "graph": bool(args.graph and aux is None),
         "gpu_step_us": gpu_step / K * 1e6,
         "measured_peaks": peaks,
         "kernel_events": {"stride": stride, "sampled_steps": NS},

@@ -78,6 +78,20 @@ class DeviceStep:
         self.append(stream)
         self.attention(stream)
 
+    def capture(self):
+        """The step (append, then attention) captured as one HIP graph (torch's
+        CUDAGraph) on a capture stream.  Replaying it re-runs both calls on
+        the same buffers; the library issues only kernel launches, so the
+        graph holds no memset or copy nodes."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()  # default priority
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=s):
+            self.run(torch.cuda.current_stream())
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
     def _section_call(self, section, stream):
         """cpa_attention over one plan section only."""
         import ctypes

@@ -262,3 +262,31 @@ def test_config_end_to_end(config):
             num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim)
         toks = sample_tokens(meta, rng)
         check_step(w, tokens=toks, label=f"{w.name}")
+
+
+def test_graph_replay_matches_eager():
+    """The step captured as one HIP graph: every replay, with eager work and
+    synchronisations between replays, gives the eager step's output and cache
+    bits (the library records only kernel launches)."""
+    import torch
+    w = workloads.make_workload(2, 1)
+    eager = DeviceStep(w, with_lse=False)
+    eager.run()
+    torch.cuda.synchronize()
+    ref_out = eager.out.clone()
+    ref_k, ref_v = eager.k_cache.clone(), eager.v_cache.clone()
+    assert eager.counts.num_decode_merges > 0 and eager.counts.num_chunk_merges > 0
+
+    ds = DeviceStep(w, with_lse=False)
+    g = ds.capture()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ds.out.fill_(0)                        # eager work between replays
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(ds.out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert torch.equal(ds.k_cache.view(torch.int16), ref_k.view(torch.int16)), rep
+        assert torch.equal(ds.v_cache.view(torch.int16), ref_v.view(torch.int16)), rep
