@@ -13,6 +13,8 @@ the worked numbers the pages print).  No function here is "parity unpinned".
 
 from .step import (  # noqa: F401
     BLOCK_SIZE,
+    POLICIES,
+    adaptive_chunk,
     BudgetError,
     Request,
     advance,

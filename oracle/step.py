@@ -64,15 +64,44 @@ class Request(NamedTuple):
 # C1: decode-first token-budget split
 # --------------------------------------------------------------------------
 
-def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: int = 0) -> dict:
+POLICIES = ("truncate", "defer", "quota")
+
+
+def adaptive_chunk(base_chunk: int, num_decodes: int) -> int:
+    """Per-request chunk size from the decode queue depth (P4 7.1): four times
+    the base chunk when no decode runs, twice under 10 decodes, the base under
+    50, half of it otherwise (at least one token)."""
+    if num_decodes == 0:
+        return base_chunk * 4
+    if num_decodes < 10:
+        return base_chunk * 2
+    if num_decodes < 50:
+        return base_chunk
+    return max(1, base_chunk // 2)
+
+
+def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: int = 0,
+             policy: str = "truncate", max_prefill_tokens: int = 0,
+             adaptive: bool = False) -> dict:
     """Split one step's token budget, decodes first (P2 section 5 hybrid
     policy; P4 3.1; P5 "The fix").
 
     * Every decode request gets one token.  More decodes than budget tokens
       is an error (P1, the budget floor).
-    * The remaining budget goes to prefill requests in queue order; each takes
-      min(remaining prompt, per-request cap, remaining budget) tokens (P1
-      "Why a chunk can be nearly free": budget 512 with 32 users gives 480).
+    * ``policy="truncate"`` (the default reading): the remaining budget goes
+      to prefill requests in queue order; each takes min(remaining prompt,
+      per-request cap, remaining budget) tokens (P1 "Why a chunk can be nearly
+      free": budget 512 with 32 users gives 480).
+    * ``policy="defer"`` (P4 3.1 as printed): a prefill's chunk is
+      min(remaining prompt, per-request cap); it is scheduled only if the
+      remaining budget holds all of it, and the first one that does not fit
+      ends the scan.
+    * ``policy="quota"`` (P4 3.2): prefills share their own budget,
+      ``max_prefill_tokens``, cut to token_budget - decodes when the decodes
+      take more than 70% of token_budget; within it, prefills are taken as in
+      "truncate".
+    * ``adaptive``: the per-request cap is adaptive_chunk(long_prefill_cap,
+      decodes) (P4 7.1); needs a positive cap.
     * Rows come out decodes first (input order), then prefills (input order);
       a request given 0 tokens is left out.
     """
@@ -80,6 +109,12 @@ def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: i
         raise ValueError("token budget must be positive")
     if long_prefill_cap < 0:
         raise ValueError("cap must be >= 0")
+    if policy not in POLICIES:
+        raise ValueError(f"unknown policy {policy}")
+    if policy == "quota" and max_prefill_tokens <= 0:
+        raise ValueError("the quota policy needs max_prefill_tokens > 0")
+    if adaptive and long_prefill_cap <= 0:
+        raise ValueError("adaptive chunking needs a base chunk (long_prefill_cap > 0)")
     for r in requests:
         if r.num_computed < 0:
             raise ValueError("negative num_computed")
@@ -90,17 +125,27 @@ def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: i
     prefills = [i for i, r in enumerate(requests) if not r.is_decode]
     if len(decodes) > token_budget:
         raise BudgetError(f"{len(decodes)} decodes exceed budget {token_budget}")
+    cap = adaptive_chunk(long_prefill_cap, len(decodes)) if adaptive else long_prefill_cap
 
     rows: list[tuple[int, int]] = [(i, 1) for i in decodes]
     remaining = token_budget - len(decodes)
+    if policy == "quota":
+        remaining = max_prefill_tokens
+        if 10 * len(decodes) > 7 * token_budget:  # decodes above 70% of the budget
+            remaining = token_budget - len(decodes)
     for i in prefills:
-        if remaining == 0:
-            break
         r = requests[i]
         want = r.target_len - r.num_computed
-        if long_prefill_cap:
-            want = min(want, long_prefill_cap)
-        n = min(want, remaining)
+        if cap:
+            want = min(want, cap)
+        if policy == "defer":
+            if want > remaining:
+                break
+            n = want
+        else:
+            if remaining == 0:
+                break
+            n = min(want, remaining)
         if n > 0:
             rows.append((i, n))
             remaining -= n

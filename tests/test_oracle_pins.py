@@ -392,6 +392,97 @@ def test_schedule_several_prefills_fcfs_and_skip():
 
 
 # ---------------------------------------------------------------------------
+# scheduler policy variants of the tbr8.org deep dive (3.1, 3.2, 7.1): outcomes
+# worked out by hand from the printed rules, and invariants that tie each
+# variant to the default (truncate) split pinned above
+# ---------------------------------------------------------------------------
+
+def _streams(n, ctx=100):
+    return [oracle.Request(i, ctx, ctx + 1, True) for i in range(n)]
+
+
+def test_policy_defer_follows_printed_rule():
+    """3.1 as printed: chunk = min(remaining prompt, chunk_size); taken only
+    if the remaining budget holds all of it, else the scan stops."""
+    reqs = _streams(32) + [oracle.Request(32, 0, 1000, False), oracle.Request(33, 0, 100, False)]
+    # no chunk size: the 1000-token prompt does not fit 512 - 32 = 480, and it
+    # blocks the 100-token one behind it (truncate gives it 480 instead)
+    d = oracle.schedule(reqs, 512, 0, policy="defer")
+    assert d["num_tokens"] == 32 and d["num_seqs"] == 32
+    assert oracle.schedule(reqs, 512, 0)["num_scheduled"][32:] == [480]
+    # chunk size 256: 256 fits (224 left), then 100 fits (124 left)
+    d = oracle.schedule(reqs, 512, 256, policy="defer")
+    assert d["order"][32:] == [32, 33] and d["num_scheduled"][32:] == [256, 100]
+    # chunk size 300 with budget 600: 300 fits (268 left), 100 fits
+    d = oracle.schedule(reqs, 600, 300, policy="defer")
+    assert d["num_scheduled"][32:] == [300, 100]
+    # the scan stops at the first misfit even if a later one would fit
+    reqs2 = _streams(2) + [oracle.Request(2, 0, 50, False), oracle.Request(3, 0, 400, False),
+                           oracle.Request(4, 0, 10, False)]
+    d = oracle.schedule(reqs2, 100, 0, policy="defer")
+    assert d["order"] == [0, 1, 2] and d["num_scheduled"] == [1, 1, 50]
+
+
+def test_policy_defer_equals_truncate_when_every_chunk_fits():
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        ndec = int(rng.integers(0, 20))
+        pre = [oracle.Request(ndec + i, int(c), int(c) + int(rng.integers(1, 300)), False)
+               for i, c in enumerate(rng.integers(0, 1000, size=int(rng.integers(1, 5))))]
+        cap = 64
+        budget = ndec + cap * len(pre) + int(rng.integers(0, 50))  # every chunk fits
+        reqs = _streams(ndec) + pre
+        assert (oracle.schedule(reqs, budget, cap, policy="defer")
+                == oracle.schedule(reqs, budget, cap))
+
+
+def test_policy_quota_follows_printed_rule():
+    """3.2: prefills get max_prefill_tokens of their own; once decodes take
+    more than 70% of the total budget it drops to total - decodes."""
+    prompt = oracle.Request(1000, 0, 8192, False)
+    q = oracle.schedule(_streams(100) + [prompt], 1000, 0, policy="quota",
+                        max_prefill_tokens=4096)
+    assert q["num_scheduled"][100:] == [4096] and q["num_tokens"] == 4196
+    q = oracle.schedule(_streams(700) + [prompt], 1000, 0, policy="quota",
+                        max_prefill_tokens=4096)  # exactly 70%: quota unchanged
+    assert q["num_scheduled"][700:] == [4096]
+    q = oracle.schedule(_streams(701) + [prompt], 1000, 0, policy="quota",
+                        max_prefill_tokens=4096)  # above 70%: 1000 - 701 left
+    assert q["num_scheduled"][701:] == [299] and q["num_tokens"] == 1000
+    # several prompts share the quota in queue order, each capped
+    reqs = _streams(10) + [oracle.Request(10 + i, 0, 3000, False) for i in range(3)]
+    q = oracle.schedule(reqs, 1000, 2048, policy="quota", max_prefill_tokens=4096)
+    assert q["num_scheduled"][10:] == [2048, 2048]
+    with pytest.raises(ValueError):
+        oracle.schedule(reqs, 1000, 0, policy="quota")
+
+
+def test_policy_quota_equals_truncate_with_matching_quota():
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        budget = int(rng.integers(100, 5000))
+        ndec = int(rng.integers(0, budget * 7 // 10))  # below 70%, so budget - ndec > 0
+        pre = [oracle.Request(ndec + i, 0, int(rng.integers(1, 4000)), False)
+               for i in range(int(rng.integers(1, 4)))]
+        reqs = _streams(ndec) + pre
+        assert (oracle.schedule(reqs, budget, 0, policy="quota", max_prefill_tokens=budget - ndec)
+                == oracle.schedule(reqs, budget, 0))
+
+
+def test_policy_adaptive_chunk_follows_queue_depth():
+    """7.1: base chunk x4 with no decode, x2 under 10, x1 under 50, /2 beyond."""
+    for ndec, want in ((0, 2048), (1, 1024), (9, 1024), (10, 512), (49, 512), (50, 256),
+                       (300, 256)):
+        reqs = _streams(ndec) + [oracle.Request(ndec, 0, 8192, False)]
+        s = oracle.schedule(reqs, 9000, 512, adaptive=True)
+        assert s["num_scheduled"][ndec:] == [want], ndec
+        assert oracle.adaptive_chunk(512, ndec) == want
+    assert oracle.adaptive_chunk(1, 60) == 1
+    with pytest.raises(ValueError):
+        oracle.schedule(_streams(3), 100, 0, adaptive=True)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by at least one pin above
 # ---------------------------------------------------------------------------
 
