@@ -129,7 +129,8 @@ class Instance:
             self.reqs[i] = cpa.cpa_req_t(r.id, r.num_computed, r.target_len, int(r.is_decode))
         self.nreq = len(w.requests)
         self.params = cpa.cpa_build_params_t(w.token_budget, w.long_prefill_cap, 16, w.num_q_heads,
-                                             w.num_kv_heads, w.head_dim, 0, 0)
+                                             w.num_kv_heads, w.head_dim, 0, 0,
+                                             cpa.CPA_POLICY_TRUNCATE, 0)
         import numpy as np
         self.scratch = {k: np.zeros(max(1, self.nreq), dtype=np.int32)
                         for k in ("order", "nsch", "newb")}

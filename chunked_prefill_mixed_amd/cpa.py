@@ -50,7 +50,15 @@ class cpa_build_params_t(ctypes.Structure):
     _fields_ = [("token_budget", ctypes.c_int32), ("long_prefill_cap", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("decode_split_tokens", ctypes.c_int32), ("chunk_split_tokens", ctypes.c_int32)]
+                ("decode_split_tokens", ctypes.c_int32), ("chunk_split_tokens", ctypes.c_int32),
+                ("policy", ctypes.c_int32), ("max_prefill_tokens", ctypes.c_int32)]
+
+
+# budget policies of cpa_build_metadata (values of include/cpa.h)
+CPA_POLICY_TRUNCATE, CPA_POLICY_DEFER, CPA_POLICY_QUOTA = 0, 1, 2
+CPA_POLICY_ADAPTIVE_CHUNK = 0x100
+POLICY_NAMES = {"truncate": CPA_POLICY_TRUNCATE, "defer": CPA_POLICY_DEFER,
+                "quota": CPA_POLICY_QUOTA}
 
 
 class cpa_plan_counts_t(ctypes.Structure):
@@ -144,13 +152,19 @@ def _i32(a):
 
 def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads, num_kv_heads,
                        head_dim, decode_split_tokens=0, chunk_split_tokens=0,
-                       host_block_table=None, num_blocks=0, block_size=BLOCK_SIZE) -> dict:
+                       host_block_table=None, num_blocks=0, block_size=BLOCK_SIZE,
+                       policy="truncate", max_prefill_tokens=0, adaptive=False) -> dict:
     """Decode-first budget split + work plan (host only, no GPU needed).
 
     ``requests``: sequence of objects with id, num_computed, target_len,
-    is_decode (queue order).  Returns numpy arrays and counts; raises
-    CpaError on a non-OK status.
+    is_decode (queue order).  ``policy`` is "truncate", "defer" or "quota"
+    (``max_prefill_tokens`` is the quota); ``adaptive`` scales
+    ``long_prefill_cap`` with the decode count.  Returns numpy arrays and
+    counts; raises CpaError on a non-OK status.
     """
+    if policy not in POLICY_NAMES:
+        raise ValueError(f"unknown policy {policy!r}")
+    pol = POLICY_NAMES[policy] | (CPA_POLICY_ADAPTIVE_CHUNK if adaptive else 0)
     lib = load()
     n = len(requests)
     reqs = (cpa_req_t * max(1, n))()
@@ -158,12 +172,13 @@ def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads,
         reqs[i] = cpa_req_t(int(r.id), int(r.num_computed), int(r.target_len), int(bool(r.is_decode)))
     params = cpa_build_params_t(int(token_budget), int(long_prefill_cap), int(block_size),
                                 int(num_q_heads), int(num_kv_heads), int(head_dim),
-                                int(decode_split_tokens), int(chunk_split_tokens))
+                                int(decode_split_tokens), int(chunk_split_tokens), pol,
+                                int(max_prefill_tokens))
     max_seqs = max(1, n)
     bufs = {k: np.zeros(max_seqs + (1 if k == "query_start_loc" else 0), dtype=np.int32)
             for k in ("order", "num_scheduled", "query_start_loc", "seq_lens", "context_lens",
                       "new_blocks")}
-    max_tokens = max(1, int(token_budget))
+    max_tokens = max(1, int(token_budget) + (int(max_prefill_tokens) if policy == "quota" else 0))
     slots = np.zeros(max_tokens, dtype=np.int64)
     bt_ptr, bt_stride = None, 0
     if host_block_table is not None:

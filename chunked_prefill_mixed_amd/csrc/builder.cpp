@@ -40,7 +40,22 @@ int check_params(const cpa_build_params_t* p) {
   if (p->decode_split_tokens % cpa::kBlock || p->decode_split_tokens > cpa::kDecodeMaxSplit)
     return CPA_ERR_INVALID;
   if (p->chunk_split_tokens % cpa::kKvTile) return CPA_ERR_INVALID;
+  const int base = p->policy & ~CPA_POLICY_ADAPTIVE_CHUNK;
+  if (base != CPA_POLICY_TRUNCATE && base != CPA_POLICY_DEFER && base != CPA_POLICY_QUOTA)
+    return CPA_ERR_INVALID;
+  if (base == CPA_POLICY_QUOTA &&
+      (p->max_prefill_tokens <= 0 || p->max_prefill_tokens > INT32_MAX - p->token_budget))
+    return CPA_ERR_INVALID;
+  if ((p->policy & CPA_POLICY_ADAPTIVE_CHUNK) && p->long_prefill_cap <= 0) return CPA_ERR_INVALID;
   return CPA_OK;
+}
+
+// Per-request chunk size from the decode queue depth (tbr8.org deep dive 7.1).
+int adaptive_cap(int base_chunk, int num_decodes) {
+  if (num_decodes == 0) return base_chunk * 4;
+  if (num_decodes < 10) return base_chunk * 2;
+  if (num_decodes < 50) return base_chunk;
+  return std::max(1, base_chunk / 2);
 }
 
 // Pages per decode piece when the caller leaves the split size to the
@@ -88,7 +103,9 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   if (bt && (bt_stride <= 0 || num_blocks <= 0)) return CPA_ERR_INVALID;
 
   const int budget = params->token_budget;
-  const int cap = params->long_prefill_cap;
+  const int policy = params->policy & ~CPA_POLICY_ADAPTIVE_CHUNK;
+  // most tokens one step can hold (the quota policy may go past the budget)
+  const int step_max = budget + (policy == CPA_POLICY_QUOTA ? params->max_prefill_tokens : 0);
   const int group = params->num_q_heads / params->num_kv_heads;
 
   // validate requests; positions must stay addressable as int32 slot indices
@@ -97,10 +114,13 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
     const cpa_req_t& r = reqs[i];
     if (r.num_computed < 0) return CPA_ERR_INVALID;
     if (!r.is_decode && r.target_len < r.num_computed) return CPA_ERR_INVALID;
-    if (r.num_computed > (INT32_MAX - budget)) return CPA_ERR_INVALID;
+    if (r.num_computed > (INT32_MAX - step_max)) return CPA_ERR_INVALID;
     n_dec += r.is_decode ? 1 : 0;
   }
   if (n_dec > budget) return CPA_ERR_BUDGET;
+  const int cap = (params->policy & CPA_POLICY_ADAPTIVE_CHUNK)
+                      ? adaptive_cap(params->long_prefill_cap, n_dec)
+                      : params->long_prefill_cap;
 
   // decode-first split of the budget
   std::vector<int32_t> order, nsched;
@@ -111,16 +131,27 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
       order.push_back(i);
       nsched.push_back(1);
     }
-  int remaining = budget - n_dec;
-  for (int i = 0; i < n_reqs && remaining > 0; ++i) {
+  // what the prefills may take: the budget left by the decodes, or the
+  // quota policy's own prefill budget (cut back once decodes take > 70%)
+  int64_t remaining = budget - n_dec;
+  if (policy == CPA_POLICY_QUOTA && 10LL * n_dec <= 7LL * budget)
+    remaining = params->max_prefill_tokens;
+  for (int i = 0; i < n_reqs; ++i) {
     const cpa_req_t& r = reqs[i];
     if (r.is_decode) continue;
-    int want = r.target_len - r.num_computed;
-    if (cap) want = std::min(want, cap);
-    int n = std::min(want, remaining);
+    int64_t want = (int64_t)r.target_len - r.num_computed;
+    if (cap) want = std::min<int64_t>(want, cap);
+    int64_t n;
+    if (policy == CPA_POLICY_DEFER) {
+      if (want > remaining) break;  // the first prefill that does not fit ends the scan
+      n = want;
+    } else {
+      if (remaining == 0) break;
+      n = std::min(want, remaining);
+    }
     if (n > 0) {
       order.push_back(i);
-      nsched.push_back(n);
+      nsched.push_back((int32_t)n);
       remaining -= n;
     }
   }

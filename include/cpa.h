@@ -101,7 +101,33 @@ typedef struct {
                                   0 = chosen by size */
   int32_t chunk_split_tokens;  /* prefix keys per chunk-tile split, multiple of 64;
                                   0 = chosen by size; a value above every context = no split */
+  int32_t policy;              /* CPA_POLICY_* below, optionally | CPA_POLICY_ADAPTIVE_CHUNK */
+  int32_t max_prefill_tokens;  /* prefill quota of CPA_POLICY_QUOTA (> 0, at most
+                                  INT32_MAX - token_budget); else ignored */
 } cpa_build_params_t;
+
+/* How the budget left after the decodes goes to prefills (tbr8.org deep dive
+ * section 3; every policy schedules all decodes first, one token each):
+ *   CPA_POLICY_TRUNCATE  prefills in queue order, each min(remaining prompt,
+ *                        long_prefill_cap, remaining budget) tokens: a prompt
+ *                        that does not fit is chunked to what remains ([P1],
+ *                        [P2] 5, [P5] "The fix").  The default.
+ *   CPA_POLICY_DEFER     3.1 as printed: a prefill's chunk is min(remaining
+ *                        prompt, long_prefill_cap); it is scheduled only if the
+ *                        remaining budget holds all of it, and the first one
+ *                        that does not fit ends the scan.
+ *   CPA_POLICY_QUOTA     3.2: prefills share max_prefill_tokens of their own
+ *                        (the step may then exceed token_budget), cut to
+ *                        token_budget - decodes when the decodes take more than
+ *                        70% of token_budget; within it as TRUNCATE.
+ *   CPA_POLICY_ADAPTIVE_CHUNK (flag) 7.1: the per-request cap is
+ *                        long_prefill_cap x4 with no decode, x2 under 10
+ *                        decodes, x1 under 50, /2 (at least 1) beyond; needs
+ *                        long_prefill_cap > 0. */
+#define CPA_POLICY_TRUNCATE 0
+#define CPA_POLICY_DEFER 1
+#define CPA_POLICY_QUOTA 2
+#define CPA_POLICY_ADAPTIVE_CHUNK 0x100
 
 /* Counts of the device work plan built by cpa_build_metadata.  The plan is one
  * int32 array of four sections, in this order: num_decode_splits entries of
@@ -145,11 +171,12 @@ typedef struct {
 /*
  * cpa_build_metadata -- host-side decode-first budget split and work plan.
  *
- * Every decode request gets one token; the remaining budget goes to prefill
- * requests in queue order, each taking min(remaining prompt, long_prefill_cap,
- * remaining budget) tokens, so a prompt that does not fit is chunked
- * ([P1] second section: budget 512 with 32 users gives 480-token chunks;
- * [P2] section 5; [P4] 3.1; [P5] "The fix").  Rows are emitted decodes first
+ * Every decode request gets one token; by default the remaining budget goes
+ * to prefill requests in queue order, each taking min(remaining prompt,
+ * long_prefill_cap, remaining budget) tokens, so a prompt that does not fit is
+ * chunked ([P1] second section: budget 512 with 32 users gives 480-token
+ * chunks; [P2] section 5; [P4] 3.1; [P5] "The fix").  params->policy selects
+ * the variants described at CPA_POLICY_TRUNCATE.  Rows are emitted decodes first
  * (queue order) then prefills (queue order); a request given no token is left
  * out.  new_blocks = ceil(seq_len/16) - ceil(context_len/16) ([P4] 4.2, for
  * chunks that start mid-page too).
@@ -162,7 +189,9 @@ typedef struct {
  * Synchronous, pure, host only (no HIP call).  Returns CPA_OK,
  * CPA_ERR_BUDGET (decodes > token_budget), CPA_ERR_INVALID (negative lengths,
  * target_len < num_computed, bad block ids, duplicate slots, split sizes that
- * are not whole pages / KV tiles), CPA_ERR_CAPACITY (an output array too small) or
+ * are not whole pages / KV tiles, an unknown policy, a quota without
+ * max_prefill_tokens, adaptive chunking without a cap), CPA_ERR_CAPACITY (an
+ * output array too small) or
  * CPA_ERR_UNSUPPORTED (shape outside the supported set).  On error the
  * outputs are unspecified.
  */

@@ -49,8 +49,9 @@ def build(reqs, budget, cap=0, Hq=32, Hkv=8, D=128, **kw):
 
 def same_as_oracle(reqs, budget, cap=0, **kw):
     got = build(reqs, budget, cap, **kw)
+    pol = {k: kw[k] for k in ("policy", "max_prefill_tokens", "adaptive") if k in kw}
     ref = oracle.schedule([oracle.Request(r.id, r.num_computed, r.target_len, bool(r.is_decode))
-                           for r in reqs], budget, cap)
+                           for r in reqs], budget, cap, **pol)
     for k in ("order", "num_scheduled", "query_start_loc", "seq_lens", "context_lens", "new_blocks"):
         assert list(got[k]) == list(ref[k]), k
     for k in ("num_seqs", "num_decodes", "num_tokens"):
@@ -204,6 +205,82 @@ def test_builder_random_mixes_match_oracle(lib):
         check_plan(m, G)
 
 
+@pytest.mark.parametrize("policy", ["truncate", "defer", "quota"])
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_builder_policies_match_oracle(lib, policy, adaptive):
+    """The library's budget policies (tbr8.org deep dive 3.1, 3.2, 7.1) give
+    the oracle's schedule on random mixes, including decode counts on both
+    sides of the quota's 70% line and of the adaptive cap's 10 / 50 steps."""
+    rng = np.random.default_rng(7000 + 2 * ["truncate", "defer", "quota"].index(policy) + adaptive)
+    for _ in range(150):
+        n = int(rng.integers(0, 80))
+        pdec = float(rng.choice([0.0, 0.3, 0.7, 0.95]))
+        reqs = []
+        for i in range(n):
+            if rng.random() < pdec:
+                c = int(rng.integers(0, 3000))
+                reqs.append(oracle.Request(i, c, c + 1, True))
+            else:
+                L = int(rng.integers(1, 3000))
+                c = int(rng.integers(0, L + 1))
+                reqs.append(oracle.Request(i, c, L, False))
+        ndec = sum(r.is_decode for r in reqs)
+        budget = int(rng.integers(max(1, ndec), max(2, ndec + int(rng.choice([8, 200, 4000])))))
+        cap = int(rng.choice([16, 100, 512])) if adaptive else int(rng.choice([0, 0, 16, 512]))
+        kw = dict(policy=policy, adaptive=adaptive)
+        if policy == "quota":
+            kw["max_prefill_tokens"] = int(rng.choice([1, 64, 1000, 6000]))
+        G = int(rng.choice([1, 4, 8]))
+        m = same_as_oracle(reqs, budget, cap, Hq=G * 2, Hkv=2, D=128, **kw)
+        check_plan(m, G)
+        if policy != "quota":
+            assert m["num_tokens"] <= budget
+        else:
+            assert m["num_tokens"] <= max(budget, ndec + kw["max_prefill_tokens"])
+
+
+def test_builder_quota_step_may_exceed_budget(lib):
+    """3.2's quota is its own prefill budget: with 10 decodes in a 64-token
+    budget (under 70%), a 200-token quota schedules 200 prefill tokens; at 50
+    decodes (over 70%) the quota falls back to the 14 the budget leaves."""
+    R = oracle.Request
+    reqs = [R(i, 30, 31, True) for i in range(10)] + [R(10, 0, 500, False)]
+    m = same_as_oracle(reqs, 64, policy="quota", max_prefill_tokens=200)
+    assert m["num_tokens"] == 210 and m["num_scheduled"][-1] == 200
+    reqs = [R(i, 30, 31, True) for i in range(50)] + [R(50, 0, 500, False)]
+    m = same_as_oracle(reqs, 64, policy="quota", max_prefill_tokens=200)
+    assert m["num_tokens"] == 64 and m["num_scheduled"][-1] == 14
+
+
+def test_builder_defer_stops_at_first_misfit(lib):
+    """3.1: a chunk that does not fit the remaining budget is not cut down;
+    the scan ends there even if a later, smaller prompt would fit."""
+    R = oracle.Request
+    reqs = [R(0, 10, 11, True), R(1, 0, 40, False), R(2, 0, 100, False), R(3, 0, 5, False)]
+    m = same_as_oracle(reqs, 64, policy="defer")
+    assert list(m["order"]) == [0, 1] and list(m["num_scheduled"]) == [1, 40]
+    m = same_as_oracle(reqs, 64, policy="truncate")
+    assert list(m["order"]) == [0, 1, 2] and list(m["num_scheduled"]) == [1, 40, 23]
+
+
+def test_builder_rejects_unknown_policy_value(lib):
+    """The C entry point itself rejects policy values it does not define."""
+    reqs = (cpa.cpa_req_t * 1)(cpa.cpa_req_t(0, 0, 10, 0))
+    bufs = [np.zeros(2, dtype=np.int32) for _ in range(6)]
+    for pol, quota, cap, ok in [(3, 0, 0, False), (0x200, 0, 0, False), (-1, 0, 0, False),
+                                (2, 0, 0, False), (2, 2**31 - 64, 0, False), (2, 8, 0, True),
+                                (0x100, 0, 0, False), (0x101, 0, 16, True), (0, 0, 0, True)]:
+        params = cpa.cpa_build_params_t(64, cap, 16, 8, 2, 128, 0, 0, pol, quota)
+        meta = cpa.cpa_meta_t()
+        meta.max_seqs = 1
+        meta.order, meta.num_scheduled, meta.query_start_loc, meta.seq_lens, meta.context_lens, \
+            meta.new_blocks = [b.ctypes.data_as(cpa.i32p) for b in bufs]
+        st = lib.cpa_build_metadata(reqs, 1, params, None, 0, 0, meta)
+        assert (st == cpa.CPA_OK) == ok, (pol, quota, cap, st)
+        if not ok:
+            assert st == cpa.CPA_ERR_INVALID
+
+
 @pytest.mark.parametrize("case,status", [
     ("budget_zero", cpa.CPA_ERR_INVALID),
     ("negative_computed", cpa.CPA_ERR_INVALID),
@@ -220,6 +297,8 @@ def test_builder_random_mixes_match_oracle(lib):
     ("block_id_out_of_range", cpa.CPA_ERR_INVALID),
     ("duplicate_slot", cpa.CPA_ERR_INVALID),
     ("fresh_slot_is_cached_elsewhere", cpa.CPA_ERR_INVALID),
+    ("quota_without_max_prefill", cpa.CPA_ERR_INVALID),
+    ("adaptive_without_cap", cpa.CPA_ERR_INVALID),
 ])
 def test_builder_error_paths(lib, case, status):
     R = oracle.Request
@@ -263,6 +342,10 @@ def test_builder_error_paths(lib, case, status):
         bt2 = bt.copy()
         bt2[1, 0] = 0  # row 1 would overwrite positions row 0 reads as context
         kw.update(host_block_table=bt2, num_blocks=10)
+    elif case == "quota_without_max_prefill":
+        kw["policy"] = "quota"
+    elif case == "adaptive_without_cap":
+        kw["adaptive"] = True
     budget = kw.pop("budget")
     with pytest.raises(cpa.CpaError) as e:
         cpa.cpa_build_metadata(reqs, token_budget=budget, long_prefill_cap=0,
