@@ -21,8 +21,15 @@
 // is exactly the B-operand layout of the PV MFMA, so P never goes through
 // LDS.  V is stored transposed inside each cache page ([D][16]), so the PV
 // A operand is one 16-byte read per lane, with no transpose.
-// K/V tiles of 64 keys (4 pages) are staged in LDS by all 256 threads; the
-// next tile's global loads are in flight while the current one is computed.
+// K/V tiles of 64 keys (4 pages) are staged in LDS by all 256 threads with
+// global_load_lds_dwordx4 (straight from memory into LDS, no register
+// staging); the next tile's loads are in flight while the current one is
+// computed.  The lane-to-LDS-slot order of those loads is fixed, so the LDS
+// layout is chosen by which 16 bytes each lane fetches: K row r keeps its
+// 16-byte d pieces XOR-permuted by swz(r), V^T rows keep their two 8-key
+// halves swapped when bit 3 of d is set (conflict-free fragment reads for
+// both).  A tile that reaches past the piece's last key goes through
+// registers instead, so the V slots past the end can be zeroed.
 // Only tiles that reach past the first query's last visible key apply the
 // causal mask.
 //
@@ -53,15 +60,18 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials part) {
   constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;               // 32-row d blocks of O^T
-  constexpr int KSTR = D + 8;              // padded K row in LDS (elements)
+  constexpr int CPR = D / 8;               // 16-byte pieces per K row
   constexpr int PAGE = kBlock * D;         // elements of one (page, KV head)
   constexpr int CHUNKS = 4 * PAGE / 8;     // 16-byte pieces per 64-key tile (K or V)
   constexpr int PER_THREAD = CHUNKS / 256;
   static_assert(CHUNKS % 256 == 0, "tile must split evenly over 256 threads");
 
   // two stages: one tile is read while the next is written
-  __shared__ __align__(16) uint16_t k_lds_buf[2][kKvTile * KSTR];
+  __shared__ __align__(16) uint16_t k_lds_buf[2][kKvTile * D];
   __shared__ __align__(16) uint16_t v_lds_buf[2][4 * PAGE];
+  // K row r's d piece c sits in 16-byte slot c ^ swz(r) of the row: the 16
+  // rows one 16-lane group reads at the same c then cover all 64 banks
+  auto swz = [](int r) { return (r / (128 / D)) % CPR; };
 
   const int item = xcd_remap(blockIdx.x, num_tiles * num_kv_heads);
   const int g = item / num_tiles;
@@ -73,6 +83,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   const int t0 = qsl[row];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ncol = lane & 31, half = lane >> 5;
   const int r = wave * 32 + ncol;
   int j = qb + r / G;
@@ -115,17 +126,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       ids[i] = pg * kBlock < kv_end ? btrow[pg] : 0;
     }
   };
+  // the ragged last tile of a piece, through registers: pages at or past
+  // kv_end are not read, V slots past it are zeroed
   auto load_tile = [&](int kt, const int (&ids)[PER_THREAD]) {
-    if ((kt + 1) * kKvTile <= kv_end) {  // whole tile below the end: no checks
-#pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        const int cidx = tid + 256 * i;
-        const int64_t base = ((int64_t)ids[i] * num_kv_heads + g) * PAGE + (cidx % (PAGE / 8)) * 8;
-        kreg[i] = *reinterpret_cast<const uint4*>(k_cache + base);
-        vreg[i] = *reinterpret_cast<const uint4*>(v_cache + base);
-      }
-      return;
-    }
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int cidx = tid + 256 * i;
@@ -157,6 +160,32 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       }
     }
   };
+  // a whole tile below kv_end: thread tid fills 16-byte LDS slot p = tid +
+  // 256 i of the K and of the V stage.  Slot p lies in page p / (PAGE / 8) of
+  // the tile (the same page for the whole wave) and at the same place inside
+  // it for every i: K slot p holds key p / CPR, piece (p % CPR) ^ swz(key);
+  // V slot s = p % (PAGE / 8) holds row d = s / 2, half (s & 1) ^ bit 3 of d.
+  const uint32_t k_lane_bytes =
+      2u * (((tid / CPR) % kBlock) * D + 8 * ((tid % CPR) ^ swz(tid / CPR)));
+  const int v_s = tid % (PAGE / 8), v_d = v_s >> 1;
+  const uint32_t v_lane_bytes = 2u * (v_d * kBlock + 8 * ((v_s & 1) ^ ((v_d >> 3) & 1)));
+  auto issue_direct = [&](int stage, const int (&ids)[PER_THREAD]) {
+    // page ids are wave-uniform: take them into scalar registers before the
+    // first load, so no load of this tile waits on another
+    int sid[PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) sid[i] = __builtin_amdgcn_readfirstlane(ids[i]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int64_t base = ((int64_t)sid[i] * num_kv_heads + g) * PAGE * 2;  // bytes
+      const int lds_off = (wave_u * 64 + 256 * i) * 8;
+      load_lds16(reinterpret_cast<const char*>(k_cache) + base + k_lane_bytes,
+                 &k_lds_buf[stage][lds_off]);
+      load_lds16(reinterpret_cast<const char*>(v_cache) + base + v_lane_bytes,
+                 &v_lds_buf[stage][lds_off]);
+    }
+  };
   auto store_tile = [&](int stage) {
     uint16_t* k_lds = k_lds_buf[stage];
     uint16_t* v_lds = v_lds_buf[stage];
@@ -167,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       const int w = cidx % (PAGE / 8);
       const int key = kp * kBlock + w / (D / 8);
       const int dpiece = w % (D / 8);
-      *reinterpret_cast<uint4*>(&k_lds[key * KSTR + dpiece * 8]) = kreg[i];
+      *reinterpret_cast<uint4*>(&k_lds[key * D + 8 * (dpiece ^ swz(key))]) = kreg[i];
       // V^T row d = w/2 keeps its two 8-key halves swapped when bit 3 of d is
       // set, so 16 lanes reading half 0 of rows d..d+15 hit distinct banks
       const int d = w >> 1, hh = (w & 1) ^ ((d >> 3) & 1);
@@ -175,23 +204,39 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     }
   };
 
+  // tile kt is whole (all 64 keys below kv_end) or the ragged last one
+  auto whole = [&](int kt) { return (kt + 1) * kKvTile <= kv_end; };
   int ids[PER_THREAD];
   load_ids(kt0, ids);
-  load_tile(kt0, ids);
+  if (whole(kt0)) {
+    issue_direct(0, ids);
+  } else {
+    load_tile(kt0, ids);
+    store_tile(0);
+  }
   load_ids(min(kt0 + 1, n_kv - 1), ids);
-  store_tile(0);
+  wait_vmem();
   __syncthreads();
-  load_tile(min(kt0 + 1, n_kv - 1), ids);
-  load_ids(min(kt0 + 2, n_kv - 1), ids);
 
   // one 64-key tile; MASK is a compile-time switch so tiles wholly visible to
   // every row of the tile carry no masking code at all.  On entry the tile is
-  // in LDS stage (kt - kt0) & 1 and the next tile's K/V are in registers.
+  // in LDS stage (kt - kt0) & 1 and ids holds the next tile's page ids.
   auto tile = [&](auto mask_tag, int kt) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int stage = (kt - kt0) & 1;
     const uint16_t* k_lds = k_lds_buf[stage];
     const uint16_t* v_lds = v_lds_buf[stage];
+    // start the next tile into the other stage (last read in tile kt - 1,
+    // before the barrier that ended it)
+    const bool more = kt + 1 < n_kv;
+    const bool next_whole = whole(kt + 1);
+    if (more) {
+      if (next_whole)
+        issue_direct(stage ^ 1, ids);
+      else
+        load_tile(kt + 1, ids);
+      load_ids(min(kt + 2, n_kv - 1), ids);
+    }
 
     // S^T = K Q^T for two 32-key blocks, the two accumulator chains interleaved
     f32x16_t s[2];
@@ -204,9 +249,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     constexpr int kAhead = 4;
     uint4 ka[2 * KS];
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i)
-      ka[i] = *reinterpret_cast<const uint4*>(
-          &k_lds[(32 * (i & 1) + krow) * KSTR + 8 * half + 16 * (i >> 1)]);
+    for (int i = 0; i < 2 * KS; ++i) {
+      const int kr = 32 * (i & 1) + krow;
+      ka[i] = *reinterpret_cast<const uint4*>(&k_lds[kr * D + 8 * ((2 * (i >> 1) + half) ^ swz(kr))]);
+    }
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i)
       s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
@@ -286,14 +332,11 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
                                                         o[db], 0, 0, 0);
       }
 
-    // stage the next tile into the other buffer (its previous contents, tile
-    // kt - 1, were last read before the barrier that ended that tile), then
-    // start loading the one after it
-    if (kt + 1 < n_kv) {
-      store_tile(stage ^ 1);
+    // the next tile must be in LDS before any wave reads it
+    if (more) {
+      if (!next_whole) store_tile(stage ^ 1);
+      wait_vmem();
       __syncthreads();
-      load_tile(min(kt + 2, n_kv - 1), ids);
-      load_ids(min(kt + 3, n_kv - 1), ids);
     }
   };
 

@@ -63,6 +63,17 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
 }
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes land at lds_wave_base + 16 * l,
+// and lds_wave_base must be the same for every lane of the wave.  Completion
+// is counted by vmcnt, so the data may be read after s_waitcnt vmcnt(0) and a
+// barrier.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // DPP lane exchanges inside a 16-lane row.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
