@@ -118,12 +118,25 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   const int n_kv = (kv_end + kKvTile - 1) / kKvTile;
 
   uint4 kreg[PER_THREAD], vreg[PER_THREAD];
-  // page ids of the pages this thread stages, read one tile ahead of their use
-  auto load_ids = [&](int kt, int (&ids)[PER_THREAD]) {
+  // Page ids come in windows of 64 pages (16 tiles), one id per lane, read a
+  // window ahead of their use; a tile's ids are taken with v_readlane.  The
+  // pages slot i of a wave stages is the same for all its lanes.
+  auto load_window = [&](int w) {
+    const int pg = 64 * w + lane;
+    return pg * kBlock < kv_end ? btrow[pg] : 0;
+  };
+  int win = kt0 / 16;  // window held in id_cur
+  int id_cur = load_window(win), id_next = load_window(win + 1);
+  auto tile_ids = [&](int kt, int (&ids)[PER_THREAD]) {
+    if (kt / 16 != win) {  // first tile of the next window
+      id_cur = id_next;
+      ++win;
+      id_next = load_window(win + 1);
+    }
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      const int pg = kt * 4 + (tid + 256 * i) / (PAGE / 8);
-      ids[i] = pg * kBlock < kv_end ? btrow[pg] : 0;
+      const int pg = kt * 4 + (wave_u * 64 + 256 * i) / (PAGE / 8);
+      ids[i] = __builtin_amdgcn_readlane(id_cur, pg - 64 * win);
     }
   };
   // the ragged last tile of a piece, through registers: pages at or past
@@ -170,15 +183,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   const int v_s = tid % (PAGE / 8), v_d = v_s >> 1;
   const uint32_t v_lane_bytes = 2u * (v_d * kBlock + 8 * ((v_s & 1) ^ ((v_d >> 3) & 1)));
   auto issue_direct = [&](int stage, const int (&ids)[PER_THREAD]) {
-    // page ids are wave-uniform: take them into scalar registers before the
-    // first load, so no load of this tile waits on another
-    int sid[PER_THREAD];
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) sid[i] = __builtin_amdgcn_readfirstlane(ids[i]);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      const int64_t base = ((int64_t)sid[i] * num_kv_heads + g) * PAGE * 2;  // bytes
+      const int64_t base = ((int64_t)ids[i] * num_kv_heads + g) * PAGE * 2;  // bytes
       const int lds_off = (wave_u * 64 + 256 * i) * 8;
       load_lds16(reinterpret_cast<const char*>(k_cache) + base + k_lane_bytes,
                  &k_lds_buf[stage][lds_off]);
@@ -206,21 +213,22 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
 
   // tile kt is whole (all 64 keys below kv_end) or the ragged last one
   auto whole = [&](int kt) { return (kt + 1) * kKvTile <= kv_end; };
-  int ids[PER_THREAD];
-  load_ids(kt0, ids);
-  if (whole(kt0)) {
-    issue_direct(0, ids);
-  } else {
-    load_tile(kt0, ids);
-    store_tile(0);
+  {
+    int ids[PER_THREAD];
+    tile_ids(kt0, ids);
+    if (whole(kt0)) {
+      issue_direct(0, ids);
+    } else {
+      load_tile(kt0, ids);
+      store_tile(0);
+    }
   }
-  load_ids(min(kt0 + 1, n_kv - 1), ids);
   wait_vmem();
   __syncthreads();
 
   // one 64-key tile; MASK is a compile-time switch so tiles wholly visible to
   // every row of the tile carry no masking code at all.  On entry the tile is
-  // in LDS stage (kt - kt0) & 1 and ids holds the next tile's page ids.
+  // in LDS stage (kt - kt0) & 1.
   auto tile = [&](auto mask_tag, int kt) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int stage = (kt - kt0) & 1;
@@ -231,11 +239,12 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     const bool more = kt + 1 < n_kv;
     const bool next_whole = whole(kt + 1);
     if (more) {
+      int ids[PER_THREAD];
+      tile_ids(kt + 1, ids);
       if (next_whole)
         issue_direct(stage ^ 1, ids);
       else
         load_tile(kt + 1, ids);
-      load_ids(min(kt + 2, n_kv - 1), ids);
     }
 
     // S^T = K Q^T for two 32-key blocks, the two accumulator chains interleaved
@@ -277,16 +286,38 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
         }
     }
 
-    float mx = neg_inf();
+    // tile max per row (four independent chains, then across the half-waves)
+    float pm[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = half_max(mx);
+      for (int rr = 0; rr < 16; ++rr) pm[rr & 3] = fmaxf(pm[rr & 3], s[kb][rr]);
+    const float mx = half_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
+
+    // probabilities against the current reference max, bf16-rounded as the
+    // PV product uses them, and their row sum (two per v_dot2, four partial
+    // sums).  They are computed before the tile max is known, and computed
+    // again in the rare case the reference has to move.
+    uint4 pb[4];
+    float ps[4];
+    auto probs = [&](float msc) {
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pv[i] = fast_exp2(__builtin_fmaf(s[kp >> 1][8 * (kp & 1) + i], scale_log2, -msc));
+        pb[kp] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+        ps[kp] = sum2_bf16(pb[kp].w,
+                           sum2_bf16(pb[kp].z, sum2_bf16(pb[kp].y, sum2_bf16(pb[kp].x, 0.f))));
+      }
+    };
+    probs(m * scale_log2);
     // move the reference max only when this tile exceeds it by more than 2^8
     // (always on a row's first tile, where m is -inf)
     const bool grow = (mx - m) * scale_log2 > 8.f;
-    if (__any(grow)) {
+    if (__builtin_expect(__any(grow), 0)) {
       // rare: rescale the running sums; the empty asm keeps the compiler from
       // hoisting this out of the branch and running it on every tile
       asm volatile("" ::: "memory");
@@ -298,23 +329,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
-    const float msc = m * scale_log2;
-
-    uint4 pb[4];
-    // row sum of the bf16-rounded probabilities the PV product uses, two per
-    // v_dot2, four independent partial sums
-    float ps[4];
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pv[i] = fast_exp2(__builtin_fmaf(s[kp >> 1][8 * (kp & 1) + i], scale_log2, -msc));
-      pb[kp] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                          pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
-      ps[kp] = sum2_bf16(pb[kp].w,
-                         sum2_bf16(pb[kp].z, sum2_bf16(pb[kp].y, sum2_bf16(pb[kp].x, 0.f))));
+      probs(m * scale_log2);
     }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
