@@ -352,11 +352,11 @@ def measured_peaks(torch, build_lib):
     torch.cuda.empty_cache()
     return {"hbm_read_GB/s": nbytes / t_read / 1e9,
             "hbm_copy_GB/s": 2 * nbytes / t_copy / 1e9,
-            "mfma_bf16_TFLOP/s": wgs * 4 * iters * 4 * 32768 / t_mfma / 1e12,
+            "mfma_bf16_TFLOP/s": wgs * 4 * iters * 8 * 32768 / t_mfma / 1e12,
             "method": "streaming non-temporal read of 2 GiB and copy of 2 GiB (read + write bytes), "
-                      "one contiguous range per workgroup; MFMA-only loop, "
-                      "4 independent v_mfma_f32_32x32x16_bf16 chains per wave, 2 workgroups "
-                      "of 4 waves per CU; HIP events, 5 runs after 2 warm-up"}
+                      "one contiguous range per workgroup; MFMA-only loop on random bf16 operands "
+                      "(8 operand sets rotated, 4 v_mfma_f32_32x32x16_bf16 chains per wave, 2 "
+                      "workgroups of 4 waves per CU); HIP events, 5 runs after 2 warm-up"}
 
 
 def cpu_baseline(workloads_list, seconds: float):

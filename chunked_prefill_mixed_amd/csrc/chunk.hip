@@ -286,6 +286,19 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
         }
     }
 
+    // the first PV A operands (V^T fragments, independent of P) are read
+    // now, so their LDS latency hides behind the softmax below
+    const int vh = half ^ ((ncol >> 3) & 1);  // the swizzled half holding keys 8*half..
+    auto vfrag = [&](int i) {  // i = kp * DB + db
+      return *reinterpret_cast<const uint4*>(
+          &v_lds[(i / DB) * PAGE + (32 * (i % DB) + ncol) * kBlock + 8 * vh]);
+    };
+    constexpr int kVAhead = 4;
+    uint4 va[kVAhead];
+#pragma unroll
+    for (int i = 0; i < kVAhead; ++i) va[i] = vfrag(i);
+    __builtin_amdgcn_sched_barrier(0);
+
     // tile max per row (four independent chains, then across the half-waves)
     float pm[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
 #pragma unroll
@@ -334,18 +347,15 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // O^T += V^T P^T, one page (16 keys) per MFMA, the DB accumulator chains
-    // interleaved
-    const int vh = half ^ ((ncol >> 3) & 1);  // the swizzled half holding keys 8*half..
+    // interleaved; V fragments read kVAhead MFMAs before their use
 #pragma unroll
-    for (int kp = 0; kp < 4; ++kp)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint4 a =
-            *reinterpret_cast<const uint4*>(&v_lds[kp * PAGE + (32 * db + ncol) * kBlock + 8 * vh]);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, pb[kp]),
-                                                        o[db], 0, 0, 0);
-      }
+    for (int i = 0; i < 4 * DB; ++i) {
+      const uint4 a = va[i % kVAhead];
+      if (i + kVAhead < 4 * DB) va[i % kVAhead] = vfrag(i + kVAhead);
+      o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, pb[i / DB]),
+                                                          o[i % DB], 0, 0, 0);
+    }
 
     // the next tile must be in LDS before any wave reads it
     if (more) {

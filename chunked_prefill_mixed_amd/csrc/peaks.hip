@@ -1,6 +1,7 @@
 // Measured ceilings for the bench's roofline report (libcpa_peaks.so; not part
 // of the attention path): a streaming device read and a streaming copy for
-// HBM bandwidth and an MFMA-only loop for dense bf16 matrix throughput.  The published MI355X
+// HBM bandwidth and an MFMA-only loop on random operands for dense bf16
+// matrix throughput.  The published MI355X
 // figures (8 TB/s, 2.5 PFLOP/s dense bf16) are the roofline peaks; these are
 // what the box sustains under the same clocks and power limits.
 
@@ -54,21 +55,48 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4_t* __restric
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
 }
 
-// kChains independent v_mfma_f32_32x32x16_bf16 accumulation chains per wave on
-// register operands; one float per thread is written so nothing is dead code
+// MFMA-only loop: kChains independent v_mfma_f32_32x32x16_bf16 accumulation
+// chains per wave, kSets register operand sets with random bf16 values in
+// (-2, 2) rotated so consecutive MFMAs see different bits.  Matrix-core
+// throughput on this chip depends on the operand bits (power): constant
+// operands run ~40% faster than random ones, and the attention kernels
+// multiply random data, so the ceiling is taken with random operands.  One
+// float per thread is written so nothing is dead code.
 constexpr int kChains = 4;
+constexpr int kSets = 8;
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// two bf16 values uniform in (-2, 2) from the hash of i
+__device__ __forceinline__ uint32_t random_bf16x2(uint32_t i) {
+  const uint32_t h = mix32(i);
+  const __bf16 lo = (__bf16)(((int)(h & 0xFFFF) - 32768) * (2.f / 32768.f));
+  const __bf16 hi = (__bf16)(((int)(h >> 16) - 32768) * (2.f / 32768.f));
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
 __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int iters) {
-  bf16x8_t a, b;
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(1e-3f * (threadIdx.x + i));
-    b[i] = (__bf16)(1e-3f * (i - (int)threadIdx.x));
-  }
+  u32x4_t a[kSets], b[kSets];
+  const uint32_t t = (uint32_t)(blockIdx.x * blockDim.x + threadIdx.x) * (8 * kSets);
+  for (int s = 0; s < kSets; ++s)
+    for (int e = 0; e < 4; ++e) {
+      a[s][e] = random_bf16x2(t + 8 * s + e);
+      b[s][e] = random_bf16x2(t + 8 * s + e + 4);
+    }
   f32x16_t acc[kChains];
   for (int c = 0; c < kChains; ++c) acc[c] = f32x16_t{};
   for (int it = 0; it < iters; ++it)
 #pragma unroll
-    for (int c = 0; c < kChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    for (int s = 0; s < kSets; ++s)
+      acc[s % kChains] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, a[s]), __builtin_bit_cast(bf16x8_t, b[(s + it) % kSets]),
+          acc[s % kChains], 0, 0, 0);
   float s = 0.f;
   for (int c = 0; c < kChains; ++c)
     for (int i = 0; i < 16; ++i) s += acc[c][i];
@@ -101,7 +129,7 @@ int cpa_peak_read(const void* src, int64_t bytes, uint32_t* out, void* stream) {
 }
 
 // Runs workgroups x 256 threads of the MFMA loop for iters iterations; out must
-// hold workgroups * 256 floats.  Flops = workgroups * 4 waves * iters * 4 chains
+// hold workgroups * 256 floats.  Flops = workgroups * 4 waves * iters * 8 MFMAs
 // * 32768.  0 or -5.
 int cpa_peak_mfma(float* out, int workgroups, int iters, void* stream) {
   if (!out || workgroups <= 0 || iters <= 0) return -1;
