@@ -18,8 +18,9 @@ last-level cache from the previous step.
 
 Prints ONE JSON line on stdout.  Per-kernel durations come from HIP events
 recorded on the launch stream around each launch inside the timed region, on
-every fifth timed step (``--kernel-event-stride``); the other steps carry only
-a start and an end event, so the markers do not serialise the whole run.
+every fifth timed step (``--kernel-event-stride``); the other steps carry no
+events at all (each marker costs a few microseconds of GPU time between two
+launches), and the step rate is the wall clock over all timed steps.
 """
 
 from __future__ import annotations
@@ -229,7 +230,7 @@ class Instance:
         self.graph = g
 
     def step(self, events, aux=None, per_kernel=True):
-        """One full step.  events: 8 torch events.  With ``aux`` (a second
+        """One full step.  events: 9 torch events.  With ``aux`` (a second
         stream) the chunk kernel runs on it, concurrently with the decode
         kernel on the main stream; both wait for the append, and the merge
         follows both on the main stream.  Without ``per_kernel`` only the
@@ -238,13 +239,16 @@ class Instance:
         the captured graph with ``--graph``."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         self.build_host()
+        main = self.torch.cuda.current_stream()
+        if per_kernel:
+            events[8].record(main)  # before the metadata copy
         self.dev.copy_(self.pinned, non_blocking=True)
         self.copy_done.record()
         lib = self.lib
-        main = self.torch.cuda.current_stream()
         parts = dict((name, args) for name, _, args in self.parts)
         st = 0
-        events[0].record(main)
+        if per_kernel:
+            events[0].record(main)
         if self.graph is None or per_kernel or aux is not None:
             st |= lib.cpa_append_kv(*self.append_args)
         if aux is None and not per_kernel:
@@ -252,7 +256,6 @@ class Instance:
                 self.graph.replay()
             else:
                 st |= lib.cpa_attention(*self.full_args)
-            events[7].record(main)
             if st != 0:
                 raise RuntimeError(f"launch failed with status {st}")
             return
@@ -459,7 +462,7 @@ def main():
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
 
     K, W = args.steps, args.warmup
-    NEV = 8
+    NEV = 9
     ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
     for s in range(W):
         insts[s % len(insts)].step(ev_w, aux)
@@ -490,9 +493,12 @@ def main():
     gpu_step = 0.0
     work = {"decode_bytes": 0, "chunk_flops": 0, "append_bytes": 0, "tokens": 0}
     tokens = 0
+    copy_us = 0.0
     for s in range(K):
-        gpu_step += events[s][0].elapsed_time(events[s][7]) * 1e-3
         tokens += insts[order[s]].work["tokens"]
+    for s in sampled:
+        gpu_step += events[s][0].elapsed_time(events[s][7]) * 1e-3
+        copy_us += events[s][8].elapsed_time(events[s][0]) * 1e3
     for s in sampled:  # per-kernel durations and work over the sampled steps
         ev = events[s]
         for n, (a, b) in spans.items():
@@ -563,7 +569,10 @@ def main():
         "streams": ("decode and chunk on two streams, concurrently" if args.two_streams
                     else "one stream"),
         "graph": bool(args.graph and aux is None),
-        "gpu_step_us": gpu_step / K * 1e6,
+        # GPU time of a sampled step (append through merge, with the markers
+        # between its launches) and of its metadata upload before it
+        "gpu_step_us": gpu_step / NS * 1e6,
+        "metadata_upload_us": copy_us / NS,
         "measured_peaks": peaks,
         "kernel_events": {"stride": stride, "sampled_steps": NS},
     }
