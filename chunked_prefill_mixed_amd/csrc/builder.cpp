@@ -84,13 +84,27 @@ int pick_piece_pages(const std::vector<int64_t>& row_pages, int num_kv_heads, in
   return (int)lo;
 }
 
-// Prefix keys per chunk piece: none split when the tiles alone give enough
-// workgroups; otherwise about kChunkWgTarget pieces (x KV heads) overall.
-int64_t pick_chunk_split(int64_t tiles, int64_t total_keys, int num_kv_heads) {
-  if (tiles * num_kv_heads >= cpa::kChunkWgTarget) return INT64_MAX;
-  int64_t per = ceil_div(total_keys * num_kv_heads, cpa::kChunkWgTarget);
-  per = ceil_div(per, cpa::kKvTile) * cpa::kKvTile;
-  return std::max<int64_t>(per, cpa::kChunkMinSplit);
+// Pieces per chunk tile when the caller leaves the split size to the library:
+// none split when the tiles alone give a resident round of workgroups;
+// otherwise each tile's keys are cut into ceil(L / S) equal pieces, with S
+// the smallest size (at least kChunkMinSplit) for which all pieces of all KV
+// heads fit one round, so no short tail pieces spill into a second round.
+std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, int num_kv_heads) {
+  std::vector<int32_t> n(tile_keys.size(), 1);
+  if ((int64_t)tile_keys.size() * num_kv_heads >= cpa::kChunkWgTarget) return n;
+  int64_t total_keys = 0;
+  for (int64_t L : tile_keys) total_keys += L;
+  int64_t S = ceil_div(total_keys * num_kv_heads, cpa::kChunkWgTarget);
+  S = std::max<int64_t>(ceil_div(S, cpa::kKvTile) * cpa::kKvTile, cpa::kChunkMinSplit);
+  for (;;) {
+    int64_t pieces = 0;
+    for (size_t t = 0; t < tile_keys.size(); ++t) {
+      n[t] = (int32_t)std::max<int64_t>(1, ceil_div(tile_keys[t], S));
+      pieces += n[t];
+    }
+    if (pieces * num_kv_heads <= cpa::kChunkWgTarget) return n;
+    S += std::max<int64_t>(cpa::kKvTile, S / 16);
+  }
 }
 
 }  // namespace
@@ -248,40 +262,59 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
 
   // chunk tiles: 128 (token, head) rows of one KV head each.  Keys below
   // context + q_begin are visible to every row of the tile, so a long prefix
-  // may be cut into pieces at multiples of the split size; the last piece
-  // holds the rest, including the causal diagonal.
+  // may be cut into pieces there; the last piece holds the rest, including
+  // the causal diagonal.
   const int tile_tokens = cpa::chunk_tile_tokens(group);
   struct Tile { int32_t row, qb, qe; int64_t prefix, keys; };
   std::vector<Tile> tl;
-  int64_t chunk_keys = 0;
   for (int s = n_dec; s < nseq; ++s) {
     const int n = out->num_scheduled[s];
     for (int qb = 0; qb < n; qb += tile_tokens) {
       const int qe = std::min(n, qb + tile_tokens);
       const int64_t c = out->context_lens[s];
       tl.push_back({s, qb, qe, c + qb, c + qe});
-      chunk_keys += c + qe;
     }
   }
-  const int64_t csplit = params->chunk_split_tokens
-                             ? (int64_t)params->chunk_split_tokens
-                             : pick_chunk_split((int64_t)tl.size(), chunk_keys, params->num_kv_heads);
+  // Inner cut points of each tile's keys [0, keys): multiples of the KV tile,
+  // at or before the tile's first query's limit (prefix), so every row of the
+  // tile sees at least one key of every piece.  A caller's split size cuts at
+  // its multiples; by default the cuts divide the keys into equal pieces.
+  std::vector<int32_t> auto_n;
+  if (!params->chunk_split_tokens) {
+    std::vector<int64_t> keys(tl.size());
+    for (size_t i = 0; i < tl.size(); ++i) keys[i] = tl[i].keys;
+    auto_n = pick_chunk_pieces(keys, params->num_kv_heads);
+  }
   struct Piece { int32_t row, qb, qe, kb, ke, slot; };
   std::vector<Piece> pieces;
   std::vector<int32_t> cmerges;
+  std::vector<int64_t> cuts;
   int cpartials = 0;
-  for (const Tile& t : tl) {
-    const int64_t n = t.prefix / csplit + 1;  // last piece starts at or before the prefix end
+  for (size_t i = 0; i < tl.size(); ++i) {
+    const Tile& t = tl[i];
+    const int64_t last = t.prefix / cpa::kKvTile * cpa::kKvTile;  // latest allowed cut
+    cuts.clear();
+    if (params->chunk_split_tokens) {
+      const int64_t S = params->chunk_split_tokens;
+      for (int64_t c = S; c <= t.prefix; c += S) cuts.push_back(c);
+    } else {
+      const int64_t n = auto_n[i];
+      for (int64_t k = 1; k < n; ++k) {
+        const int64_t c = std::min(k * t.keys / n / cpa::kKvTile * cpa::kKvTile, last);
+        if (c > 0 && (cuts.empty() || c > cuts.back())) cuts.push_back(c);
+      }
+    }
+    const int32_t n = (int32_t)cuts.size() + 1;
     if (n == 1) {
       pieces.push_back({t.row, t.qb, t.qe, 0, (int32_t)t.keys, -1});
       continue;
     }
-    cmerges.insert(cmerges.end(), {t.row, t.qb, t.qe, cpartials, (int32_t)n, 0, 0, 0});
-    for (int64_t k = 0; k < n; ++k) {
-      const int64_t kb = k * csplit, ke = (k + 1 < n) ? (k + 1) * csplit : t.keys;
-      pieces.push_back({t.row, t.qb, t.qe, (int32_t)kb, (int32_t)ke, cpartials + (int32_t)k});
+    cmerges.insert(cmerges.end(), {t.row, t.qb, t.qe, cpartials, n, 0, 0, 0});
+    for (int32_t k = 0; k < n; ++k) {
+      const int64_t kb = k ? cuts[k - 1] : 0, ke = k + 1 < n ? cuts[k] : t.keys;
+      pieces.push_back({t.row, t.qb, t.qe, (int32_t)kb, (int32_t)ke, cpartials + k});
     }
-    cpartials += (int)n;
+    cpartials += n;
   }
   // longest key range first, so the last workgroups to start are short ones
   std::stable_sort(pieces.begin(), pieces.end(),
