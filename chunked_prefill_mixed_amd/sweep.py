@@ -1,93 +1,153 @@
-"""Token-budget sweep of the attention step on one MI355X.
+"""Multi-step replay of a long prompt arriving among streaming requests, on
+one MI355X, attention part only.
 
-The scenario of "Chunked Prefill" (deepconcepts.dev), "Why a chunk can be
-nearly free" and "The budget points in two directions": 32 running decode
-streams and one 8192-token prompt that arrives at step 0.  With token budget
-B the decode-first split gives every stream one token per step and the prompt
-B - 32 tokens per step until it is prefilled (the pages' 224-, 480- and
-4064-token chunks at budgets 256, 512 and 4096).  For each budget this runs
-the whole sequence of steps through the library (cpa_build_metadata,
-cpa_append_kv, cpa_attention on one stream; the streams' contexts grow by one
-token per step, the prompt's by its chunk) and times each step's append +
-attention with HIP events.  Attention only: no model layers, so the numbers
-are the attention part of the pages' pass times, not their whole passes.
+Two scenarios from the pages, each run over its own knob:
 
-Reported per budget: chunk tokens per step, steps to finish the prompt, mean
-and max step time, the decode-only step time at the same contexts (the same
-32 streams with no prompt), the mean extra time a chunk adds to a step, the
-prompt's prefill time (sum of its steps) and the rate at which the streams
-and the prompt advance.
+* ``budget`` -- "Chunked Prefill" (deepconcepts.dev), "Why a chunk can be
+  nearly free" and "The budget points in two directions": 32 running decode
+  streams and one 8192-token prompt that arrives at step 0, swept over the
+  token budget B.  Decode-first gives every stream one token per step and the
+  prompt B - 32 tokens per step (the page's 224-, 480- and 4064-token chunks
+  at budgets 256, 512 and 4096; one pass at 8224).
+* ``chunk`` -- "Chunked prefill" test on an M5 Max (the page's table of chunk
+  size against time to first token and worst streaming pause): three
+  streaming requests and one 8000-token prompt, swept over the chunk size C
+  (budget 3 + C, so the prompt gets C tokens a step; 8003 = unchunked).
 
-    python -m chunked_prefill_mixed_amd.sweep [--budgets 64 128 ...] [--out FILE]
+For every knob value the whole sequence of steps runs through the library
+(cpa_build_metadata, cpa_append_kv, cpa_attention on one stream; the
+streams' contexts grow by one token per step, the prompt's by its chunk) and
+each step's append + attention is timed with HIP events.  Attention only: no
+model layers, so the figures are the attention part of the pages' pass
+times, not their whole passes.
 
-Inputs are seeded and synthetic (workloads.py recipe): contexts uniform in
-[512, 4096], Hq=32, Hkv=8, D=128, bf16, 16-token pages.
+Reported per knob value: chunk tokens, steps to finish the prompt, mean and
+max step time, the decode-only step time at the same contexts (the streams
+alone), and the replay's figures: time to first token of the prompt (the sum
+of its steps: its first token comes from the last chunk's step), the worst
+gap between two tokens of a stream while the prompt is prefilled (the longest
+step), the stall above the undisturbed gap (longest step minus the
+decode-only step), the tokens the streams receive meanwhile (streams x
+steps) and the time to first token against the unchunked run.
+
+    python -m chunked_prefill_mixed_amd.sweep [--scenario budget|chunk]
+                                              [--values ...] [--out FILE]
+
+Inputs are seeded and synthetic (workloads.py recipe): stream contexts
+uniform in [512, 4096] (budget scenario) or [128, 1024] (chunk scenario),
+Hq=32, Hkv=8, D=128, bf16, 16-token pages.
 """
 
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import sys
+from dataclasses import dataclass
 
 import numpy as np
 
 from . import cpa, workloads
 
-NUM_STREAMS = 32
-PROMPT = 8192
 HQ, HKV, D = 32, 8, 128
-DEFAULT_BUDGETS = (64, 128, 256, 512, 1024, 2048, 4096, NUM_STREAMS + PROMPT)
+NUM_STREAMS = 32   # budget scenario
+PROMPT = 8192
 
 
-def stream_contexts(seed: int = 1002) -> np.ndarray:
-    """Initial cached lengths of the 32 streams: uniform in [512, 4096]."""
+@dataclass(frozen=True)
+class Scenario:
+    name: str
+    streams: int
+    prompt: int
+    ctx_lo: int
+    ctx_hi: int
+    seed: int
+    values: tuple    # knob values: budgets, or chunk sizes
+    knob: str        # "budget" or "chunk"
+
+    def budget(self, value: int) -> int:
+        return value if self.knob == "budget" else self.streams + value
+
+
+SCENARIOS = {
+    "budget": Scenario("budget", NUM_STREAMS, PROMPT, 512, 4096, 1002,
+                       (64, 128, 256, 512, 1024, 2048, 4096, NUM_STREAMS + PROMPT), "budget"),
+    "chunk": Scenario("chunk", 3, 8000, 128, 1024, 1003, (256, 512, 1024, 2048, 8000), "chunk"),
+}
+DEFAULT_BUDGETS = SCENARIOS["budget"].values
+
+
+def stream_contexts(seed: int = 1002, n: int = NUM_STREAMS, lo: int = 512, hi: int = 4096) -> np.ndarray:
+    """Initial cached lengths of the streams: uniform in [lo, hi]."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99]).spawn(1)[0]))
-    return rng.integers(512, 4096, size=NUM_STREAMS, endpoint=True)
+    return rng.integers(lo, hi, size=n, endpoint=True)
 
 
-def schedule(budget: int, contexts) -> list:
+def _requests(contexts, k, done, prompt):
+    n = len(contexts)
+    reqs = [workloads.Req(i, int(c) + k, int(c) + k + 1, True) for i, c in enumerate(contexts)]
+    reqs.append(workloads.Req(n, done, prompt, False))
+    return reqs
+
+
+def schedule(budget: int, contexts, prompt: int = PROMPT) -> list:
     """The steps of one run at this budget, host only: for each step the
     request list (queue order: streams, then the prompt) and the metadata
     cpa_build_metadata returns for it."""
+    n = len(contexts)
     steps = []
     done = 0
     k = 0
-    while done < PROMPT:
-        reqs = [workloads.Req(i, int(c) + k, int(c) + k + 1, True) for i, c in enumerate(contexts)]
-        reqs.append(workloads.Req(NUM_STREAMS, done, PROMPT, False))
+    while done < prompt:
+        reqs = _requests(contexts, k, done, prompt)
         meta = cpa.cpa_build_metadata(reqs, token_budget=budget, long_prefill_cap=0,
                                       num_q_heads=HQ, num_kv_heads=HKV, head_dim=D)
-        if meta["num_seqs"] <= NUM_STREAMS:  # budget leaves nothing for the prompt
+        if meta["num_seqs"] <= n:  # budget leaves nothing for the prompt
             raise ValueError(f"budget {budget} cannot finish the prompt")
         steps.append((reqs, meta))
-        done += int(meta["num_scheduled"][NUM_STREAMS])
+        done += int(meta["num_scheduled"][n])
         k += 1
     return steps
 
 
 def _decode_only(contexts, k):
     reqs = [workloads.Req(i, int(c) + k, int(c) + k + 1, True) for i, c in enumerate(contexts)]
-    meta = cpa.cpa_build_metadata(reqs, token_budget=NUM_STREAMS, long_prefill_cap=0,
+    meta = cpa.cpa_build_metadata(reqs, token_budget=len(contexts), long_prefill_cap=0,
                                   num_q_heads=HQ, num_kv_heads=HKV, head_dim=D)
     return reqs, meta
+
+
+def replay_figures(times, decode_only, streams, ttft_unchunked=None) -> dict:
+    """The replay's figures from one run's step times (seconds) and the
+    decode-only step time at the same contexts (seconds)."""
+    t = np.asarray(times, dtype=np.float64)
+    ttft = float(t.sum())
+    fig = {"steps": int(t.size), "mean_step_us": float(t.mean() * 1e6),
+           "max_step_us": float(t.max() * 1e6), "decode_only_step_us": float(decode_only * 1e6),
+           "ttft_ms": ttft * 1e3, "worst_gap_us": float(t.max() * 1e6),
+           "stall_us": float((t.max() - decode_only) * 1e6),
+           "stream_tokens_during_prefill": int(streams * t.size),
+           "mean_extra_us": float((t.mean() - decode_only) * 1e6)}
+    if ttft_unchunked:
+        fig["ttft_vs_unchunked"] = ttft / ttft_unchunked
+    return fig
 
 
 class _Gpu:
     """The run's pool and packed inputs in HBM, and one timed step."""
 
-    def __init__(self, contexts, max_steps: int, max_budget: int):
+    def __init__(self, scn: Scenario, contexts, max_steps: int, max_budget: int):
         import torch
         self.torch = torch
-        reach = [int(c) + max_steps + 1 for c in contexts] + [PROMPT]
-        reqs = [workloads.Req(i, int(c), int(c) + 1, True) for i, c in enumerate(contexts)]
-        reqs.append(workloads.Req(NUM_STREAMS, 0, PROMPT, False))
-        st = workloads._streams(1002, 99)
-        w = workloads.build("budget_sweep", 1002, 99, num_q_heads=HQ, num_kv_heads=HKV,
+        n = len(contexts)
+        reach = [int(c) + max_steps + 1 for c in contexts] + [scn.prompt]
+        reqs = _requests(contexts, 0, 0, scn.prompt)
+        st = workloads._streams(scn.seed, 99)
+        w = workloads.build(f"replay_{scn.name}", scn.seed, 99, num_q_heads=HQ, num_kv_heads=HKV,
                             head_dim=D, token_budget=max_budget, long_prefill_cap=0,
                             requests=reqs, reach=reach, pool_blocks=None, streams=st)
         self.w = w
+        self.n = n
         dev = "cuda"
         bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
             torch.bfloat16)
@@ -128,51 +188,58 @@ class _Gpu:
         return e0.elapsed_time(e1) * 1e-3
 
 
-def run(budgets, out_path=None) -> list:
+def run(scenario: str = "budget", values=None, out_path=None) -> list:
     import torch
     if not torch.cuda.is_available():
-        raise SystemExit("the sweep needs a GPU (the HIP library has no CPU path)")
+        raise SystemExit("the replay needs a GPU (the HIP library has no CPU path)")
     cpa.load()
-    contexts = stream_contexts()
-    plans = {b: schedule(b, contexts) for b in budgets}
+    scn = SCENARIOS[scenario]
+    values = sorted(values or scn.values)
+    contexts = stream_contexts(scn.seed, scn.streams, scn.ctx_lo, scn.ctx_hi)
+    plans = {v: schedule(scn.budget(v), contexts, scn.prompt) for v in values}
     max_steps = max(len(p) for p in plans.values())
-    gpu = _Gpu(contexts, max_steps, max(budgets))
-    # warm-up: a few steps of the first budget, then reset the pool
-    for _, meta in plans[budgets[0]][:3]:
+    gpu = _Gpu(scn, contexts, max_steps, max(scn.budget(v) for v in values))
+    n = scn.streams
+    for _, meta in plans[values[0]][:3]:  # warm-up, then reset the pool
         gpu.step(meta)
-    rows = []
-    for b in budgets:
+    runs = {}
+    for v in values:
         gpu.reset()
-        times, decode_only, chunks = [], [], []
-        for k, (_, meta) in enumerate(plans[b]):
+        times, chunks = [], []
+        for _, meta in plans[v]:
             times.append(gpu.step(meta))
-            chunks.append(int(meta["num_scheduled"][NUM_STREAMS]))
+            chunks.append(int(meta["num_scheduled"][n]))
         # decode-only steps at the first, middle and last contexts of the run
         # (own pool copy, so the run's cache contents are not disturbed)
         saved = gpu.k_cache.clone(), gpu.v_cache.clone()
-        for k in sorted({0, len(times) // 2, len(times) - 1}):
-            decode_only.append(gpu.step(_decode_only(contexts, k)[1]))
+        dec = [gpu.step(_decode_only(contexts, k)[1])
+               for k in sorted({0, len(times) // 2, len(times) - 1})]
         gpu.k_cache.copy_(saved[0])
         gpu.v_cache.copy_(saved[1])
-        t = np.asarray(times)
-        d = float(np.mean(decode_only))
-        row = {"budget": b, "chunk_tokens": chunks[0], "steps": len(times),
-               "mean_step_us": float(t.mean() * 1e6), "max_step_us": float(t.max() * 1e6),
-               "decode_only_step_us": d * 1e6,
-               "mean_extra_us": float((t.mean() - d) * 1e6),
-               "prefill_ms": float(t.sum() * 1e3),
-               "prompt_tokens_per_s": PROMPT / float(t.sum()),
-               "stream_tokens_per_s": NUM_STREAMS / float(t.mean())}
+        runs[v] = (times, chunks, float(np.mean(dec)))
+    unchunked = max(values, key=lambda v: scn.budget(v))
+    ttft_unchunked = float(np.sum(runs[unchunked][0])) if len(plans[unchunked]) == 1 else None
+    rows = []
+    for v in values:
+        times, chunks, d = runs[v]
+        row = {"scenario": scn.name, scn.knob: v, "budget": scn.budget(v),
+               "chunk_tokens": chunks[0]}
+        row.update(replay_figures(times, d, n, ttft_unchunked))
+        row["prompt_tokens_per_s"] = scn.prompt / (row["ttft_ms"] * 1e-3)
+        row["stream_tokens_per_s"] = n / (row["mean_step_us"] * 1e-6)
         rows.append(row)
         print(json.dumps(row), flush=True)
-    lines = ["budget  chunk  steps  mean_us   max_us  decode_only_us  extra_us  prefill_ms"
-             "  prompt_tok/s  stream_tok/s"]
+    head = (f"{scn.knob:>6} chunk  steps  mean_us   max_us  decode_only_us  stall_us  ttft_ms"
+            "  vs_unchunked  stream_tokens")
+    lines = [f"scenario {scn.name}: {n} streams (contexts U[{scn.ctx_lo}, {scn.ctx_hi}]) + a "
+             f"{scn.prompt}-token prompt; Hq={HQ} Hkv={HKV} D={D} bf16; append + attention per step",
+             head]
     for r in rows:
-        lines.append(f"{r['budget']:6d} {r['chunk_tokens']:6d} {r['steps']:6d} "
+        vs = f"{r['ttft_vs_unchunked']:12.2f}x" if "ttft_vs_unchunked" in r else f"{'-':>13}"
+        lines.append(f"{r[scn.knob]:6d} {r['chunk_tokens']:5d} {r['steps']:6d} "
                      f"{r['mean_step_us']:8.1f} {r['max_step_us']:8.1f} "
-                     f"{r['decode_only_step_us']:15.1f} {r['mean_extra_us']:9.1f} "
-                     f"{r['prefill_ms']:11.2f} {r['prompt_tokens_per_s']:13.0f} "
-                     f"{r['stream_tokens_per_s']:13.0f}")
+                     f"{r['decode_only_step_us']:15.1f} {r['stall_us']:9.1f} {r['ttft_ms']:8.2f} "
+                     f"{vs} {r['stream_tokens_during_prefill']:14d}")
     text = "\n".join(lines)
     print(text, file=sys.stderr)
     if out_path:
@@ -183,10 +250,13 @@ def run(budgets, out_path=None) -> list:
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--budgets", type=int, nargs="+", default=list(DEFAULT_BUDGETS))
+    ap.add_argument("--scenario", choices=sorted(SCENARIOS), default="budget")
+    ap.add_argument("--values", type=int, nargs="+", default=None,
+                    help="budgets (budget scenario) or chunk sizes (chunk scenario)")
+    ap.add_argument("--budgets", type=int, nargs="+", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--out", default=None, help="also write the table to this file")
     args = ap.parse_args()
-    run(sorted(args.budgets), args.out)
+    run(args.scenario, args.values or args.budgets, args.out)
 
 
 if __name__ == "__main__":

@@ -412,3 +412,33 @@ def test_budget_sweep_schedule(lib):
             assert m["context_lens"][32] == k * chunk
     with pytest.raises(ValueError):
         sweep.schedule(32, ctx)
+
+
+def test_replay_chunk_scenario_schedule(lib):
+    """The chunk-size replay: three streams and an 8000-token prompt with
+    budget 3 + C give chunks of C tokens and ceil(8000 / C) passes (32/16/8/4
+    at C = 256/512/1024/2048, one pass unchunked), the streams one token a
+    step."""
+    from chunked_prefill_mixed_amd import sweep
+    scn = sweep.SCENARIOS["chunk"]
+    ctx = sweep.stream_contexts(scn.seed, scn.streams, scn.ctx_lo, scn.ctx_hi)
+    assert len(ctx) == 3 and ctx.min() >= 128 and ctx.max() <= 1024
+    for C, passes in ((256, 32), (512, 16), (1024, 8), (2048, 4), (8000, 1)):
+        steps = sweep.schedule(scn.budget(C), ctx, scn.prompt)
+        assert len(steps) == passes, C
+        sizes = [int(m["num_scheduled"][3]) for _, m in steps]
+        assert sizes[:-1] == [C] * (passes - 1) and sum(sizes) == 8000, C
+        for k, (_, m) in enumerate(steps):
+            assert m["num_decodes"] == 3 and list(m["context_lens"][:3]) == list(ctx + k)
+
+
+def test_replay_figures_arithmetic():
+    """Replay figures from given step times: time to first token is the sum
+    of the prompt's steps, the worst gap the longest step, the stall that
+    minus the decode-only step, the streams' tokens streams x steps."""
+    from chunked_prefill_mixed_amd import sweep
+    f = sweep.replay_figures([100e-6, 250e-6, 150e-6], 80e-6, 32, ttft_unchunked=400e-6)
+    assert f["steps"] == 3 and f["stream_tokens_during_prefill"] == 96
+    assert math.isclose(f["ttft_ms"], 0.5) and math.isclose(f["worst_gap_us"], 250.0)
+    assert math.isclose(f["stall_us"], 170.0) and math.isclose(f["mean_step_us"], 500 / 3)
+    assert math.isclose(f["ttft_vs_unchunked"], 1.25)
