@@ -82,7 +82,7 @@ def adaptive_chunk(base_chunk: int, num_decodes: int) -> int:
 
 def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: int = 0,
              policy: str = "truncate", max_prefill_tokens: int = 0,
-             adaptive: bool = False) -> dict:
+             adaptive: bool = False, block_aligned: bool = False) -> dict:
     """Split one step's token budget, decodes first (P2 section 5 hybrid
     policy; P4 3.1; P5 "The fix").
 
@@ -102,6 +102,13 @@ def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: i
       "truncate".
     * ``adaptive``: the per-request cap is adaptive_chunk(long_prefill_cap,
       decodes) (P4 7.1); needs a positive cap.
+    * ``block_aligned``: a chunk that stops before the end of its prompt
+      stops on a page boundary instead, (c + n) rounded down to a multiple of
+      BLOCK_SIZE, when that leaves it at least one token; the tokens given
+      back stay in the budget for the prompts behind it.  Every page such a
+      chunk writes is then complete, so a prefix cache can reuse it: P1's
+      closing notes say a chunked prefill only reuses cached pages that sit on
+      page boundaries, P4 6.1 that prefix caching and chunked prefill combine.
     * Rows come out decodes first (input order), then prefills (input order);
       a request given 0 tokens is left out.
     """
@@ -146,6 +153,10 @@ def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: i
             if remaining == 0:
                 break
             n = min(want, remaining)
+        if block_aligned and 0 < n < r.target_len - r.num_computed:
+            end = (r.num_computed + n) // BLOCK_SIZE * BLOCK_SIZE
+            if end > r.num_computed:
+                n = end - r.num_computed
         if n > 0:
             rows.append((i, n))
             remaining -= n

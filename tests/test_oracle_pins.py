@@ -482,6 +482,57 @@ def test_policy_adaptive_chunk_follows_queue_depth():
         oracle.schedule(_streams(3), 100, 0, adaptive=True)
 
 
+def test_block_aligned_chunks_follow_the_rule():
+    """A chunk cut short ends on a page boundary when that leaves it a token;
+    the tokens it gives back go to the next prompt; a prompt's last chunk and
+    a cut that would leave nothing are unchanged (hand-worked cases)."""
+    R = oracle.Request
+    reqs = _streams(32) + [R(32, 100, 8192, False), R(33, 0, 100, False)]
+    assert oracle.schedule(reqs, 512)["num_scheduled"][32:] == [480]
+    s = oracle.schedule(reqs, 512, block_aligned=True)
+    assert s["num_scheduled"][32:] == [476, 4] and s["seq_lens"][32] == 576
+    # the prompt's last chunk is not cut
+    reqs = _streams(32) + [R(32, 100, 300, False)]
+    assert oracle.schedule(reqs, 512, block_aligned=True)["num_scheduled"][32:] == [200]
+    # 10 + 3 tokens cannot reach page boundary 16: the chunk keeps its 3
+    reqs = _streams(32) + [R(32, 10, 500, False)]
+    assert oracle.schedule(reqs, 35, block_aligned=True)["num_scheduled"][32:] == [3]
+    # the page-2 step table (budget 8192, cap 2048) is already aligned
+    reqs = _streams(2) + [R(2, 2048, 8192, False)]
+    assert oracle.schedule(reqs, 8192, 2048, block_aligned=True)["num_scheduled"] == [1, 1, 2048]
+
+
+def test_block_aligned_invariants_on_random_mixes():
+    """Random mixes: every chunk that stops short of its prompt's end and
+    could reach a page boundary ends on one; the step stays within the
+    budget; with the flag off the split is the default one."""
+    rng = np.random.default_rng(31)
+    R = oracle.Request
+    for _ in range(300):
+        n = int(rng.integers(1, 30))
+        reqs = []
+        for i in range(n):
+            if rng.random() < 0.5:
+                c = int(rng.integers(0, 3000))
+                reqs.append(R(i, c, c + 1, True))
+            else:
+                L = int(rng.integers(1, 3000))
+                reqs.append(R(i, int(rng.integers(0, L + 1)), L, False))
+        ndec = sum(r.is_decode for r in reqs)
+        budget = int(rng.integers(max(1, ndec), ndec + 2000))
+        cap = int(rng.choice([0, 0, 100, 512]))
+        s = oracle.schedule(reqs, budget, cap, block_aligned=True)
+        assert sum(s["num_scheduled"]) <= budget
+        for i, nn, c in zip(s["order"], s["num_scheduled"], s["context_lens"]):
+            r = reqs[i]
+            if r.is_decode or nn == r.target_len - r.num_computed:
+                continue
+            if (c + nn) // oracle.BLOCK_SIZE * oracle.BLOCK_SIZE > c:
+                assert (c + nn) % oracle.BLOCK_SIZE == 0, (c, nn)
+        assert oracle.schedule(reqs, budget, cap, block_aligned=False) == oracle.schedule(
+            reqs, budget, cap)
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by at least one pin above
 # ---------------------------------------------------------------------------
