@@ -57,6 +57,7 @@ class cpa_build_params_t(ctypes.Structure):
 # budget policies of cpa_build_metadata (values of include/cpa.h)
 CPA_POLICY_TRUNCATE, CPA_POLICY_DEFER, CPA_POLICY_QUOTA = 0, 1, 2
 CPA_POLICY_ADAPTIVE_CHUNK = 0x100
+CPA_POLICY_BLOCK_ALIGNED = 0x200
 POLICY_NAMES = {"truncate": CPA_POLICY_TRUNCATE, "defer": CPA_POLICY_DEFER,
                 "quota": CPA_POLICY_QUOTA}
 
@@ -153,18 +154,21 @@ def _i32(a):
 def cpa_build_metadata(requests, *, token_budget, long_prefill_cap, num_q_heads, num_kv_heads,
                        head_dim, decode_split_tokens=0, chunk_split_tokens=0,
                        host_block_table=None, num_blocks=0, block_size=BLOCK_SIZE,
-                       policy="truncate", max_prefill_tokens=0, adaptive=False) -> dict:
+                       policy="truncate", max_prefill_tokens=0, adaptive=False,
+                       block_aligned=False) -> dict:
     """Decode-first budget split + work plan (host only, no GPU needed).
 
     ``requests``: sequence of objects with id, num_computed, target_len,
     is_decode (queue order).  ``policy`` is "truncate", "defer" or "quota"
     (``max_prefill_tokens`` is the quota); ``adaptive`` scales
-    ``long_prefill_cap`` with the decode count.  Returns numpy arrays and
+    ``long_prefill_cap`` with the decode count; ``block_aligned`` ends chunks
+    cut short on page boundaries.  Returns numpy arrays and
     counts; raises CpaError on a non-OK status.
     """
     if policy not in POLICY_NAMES:
         raise ValueError(f"unknown policy {policy!r}")
-    pol = POLICY_NAMES[policy] | (CPA_POLICY_ADAPTIVE_CHUNK if adaptive else 0)
+    pol = (POLICY_NAMES[policy] | (CPA_POLICY_ADAPTIVE_CHUNK if adaptive else 0)
+           | (CPA_POLICY_BLOCK_ALIGNED if block_aligned else 0))
     lib = load()
     n = len(requests)
     reqs = (cpa_req_t * max(1, n))()

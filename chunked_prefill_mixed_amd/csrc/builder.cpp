@@ -40,7 +40,7 @@ int check_params(const cpa_build_params_t* p) {
   if (p->decode_split_tokens % cpa::kBlock || p->decode_split_tokens > cpa::kDecodeMaxSplit)
     return CPA_ERR_INVALID;
   if (p->chunk_split_tokens % cpa::kKvTile) return CPA_ERR_INVALID;
-  const int base = p->policy & ~CPA_POLICY_ADAPTIVE_CHUNK;
+  const int base = p->policy & ~(CPA_POLICY_ADAPTIVE_CHUNK | CPA_POLICY_BLOCK_ALIGNED);
   if (base != CPA_POLICY_TRUNCATE && base != CPA_POLICY_DEFER && base != CPA_POLICY_QUOTA)
     return CPA_ERR_INVALID;
   if (base == CPA_POLICY_QUOTA &&
@@ -117,7 +117,8 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   if (bt && (bt_stride <= 0 || num_blocks <= 0)) return CPA_ERR_INVALID;
 
   const int budget = params->token_budget;
-  const int policy = params->policy & ~CPA_POLICY_ADAPTIVE_CHUNK;
+  const int policy = params->policy & ~(CPA_POLICY_ADAPTIVE_CHUNK | CPA_POLICY_BLOCK_ALIGNED);
+  const bool aligned = params->policy & CPA_POLICY_BLOCK_ALIGNED;
   // most tokens one step can hold (the quota policy may go past the budget)
   const int step_max = budget + (policy == CPA_POLICY_QUOTA ? params->max_prefill_tokens : 0);
   const int group = params->num_q_heads / params->num_kv_heads;
@@ -162,6 +163,11 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
     } else {
       if (remaining == 0) break;
       n = std::min(want, remaining);
+    }
+    // a chunk that stops short of its prompt's end may stop on a page boundary
+    if (aligned && n > 0 && n < (int64_t)r.target_len - r.num_computed) {
+      const int64_t end = (r.num_computed + n) / cpa::kBlock * cpa::kBlock;
+      if (end > r.num_computed) n = end - r.num_computed;
     }
     if (n > 0) {
       order.push_back(i);

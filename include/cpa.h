@@ -101,7 +101,8 @@ typedef struct {
                                   0 = chosen by size */
   int32_t chunk_split_tokens;  /* prefix keys per chunk-tile split, multiple of 64;
                                   0 = chosen by size; a value above every context = no split */
-  int32_t policy;              /* CPA_POLICY_* below, optionally | CPA_POLICY_ADAPTIVE_CHUNK */
+  int32_t policy;              /* CPA_POLICY_* below, optionally | the flags
+                                  CPA_POLICY_ADAPTIVE_CHUNK, CPA_POLICY_BLOCK_ALIGNED */
   int32_t max_prefill_tokens;  /* prefill quota of CPA_POLICY_QUOTA (> 0, at most
                                   INT32_MAX - token_budget); else ignored */
 } cpa_build_params_t;
@@ -123,11 +124,21 @@ typedef struct {
  *   CPA_POLICY_ADAPTIVE_CHUNK (flag) 7.1: the per-request cap is
  *                        long_prefill_cap x4 with no decode, x2 under 10
  *                        decodes, x1 under 50, /2 (at least 1) beyond; needs
- *                        long_prefill_cap > 0. */
+ *                        long_prefill_cap > 0.
+ *   CPA_POLICY_BLOCK_ALIGNED (flag): a chunk that stops before the end of
+ *                        its prompt stops on a page boundary instead
+ *                        (context + n rounded down to a multiple of 16) when
+ *                        that leaves it at least one token; the tokens given
+ *                        back stay in the budget for the prompts behind it.
+ *                        Every page such a chunk writes is complete, so a
+ *                        prefix cache can reuse it ([P1] closing notes: a
+ *                        chunked prefill reuses only cached pages on page
+ *                        boundaries; [P4] 6.1). */
 #define CPA_POLICY_TRUNCATE 0
 #define CPA_POLICY_DEFER 1
 #define CPA_POLICY_QUOTA 2
 #define CPA_POLICY_ADAPTIVE_CHUNK 0x100
+#define CPA_POLICY_BLOCK_ALIGNED 0x200
 
 /* Counts of the device work plan built by cpa_build_metadata.  The plan is one
  * int32 array of four sections, in this order: num_decode_splits entries of

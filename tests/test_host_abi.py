@@ -49,7 +49,8 @@ def build(reqs, budget, cap=0, Hq=32, Hkv=8, D=128, **kw):
 
 def same_as_oracle(reqs, budget, cap=0, **kw):
     got = build(reqs, budget, cap, **kw)
-    pol = {k: kw[k] for k in ("policy", "max_prefill_tokens", "adaptive") if k in kw}
+    pol = {k: kw[k] for k in ("policy", "max_prefill_tokens", "adaptive", "block_aligned")
+           if k in kw}
     ref = oracle.schedule([oracle.Request(r.id, r.num_computed, r.target_len, bool(r.is_decode))
                            for r in reqs], budget, cap, **pol)
     for k in ("order", "num_scheduled", "query_start_loc", "seq_lens", "context_lens", "new_blocks"):
@@ -207,11 +208,13 @@ def test_builder_random_mixes_match_oracle(lib):
 
 @pytest.mark.parametrize("policy", ["truncate", "defer", "quota"])
 @pytest.mark.parametrize("adaptive", [False, True])
-def test_builder_policies_match_oracle(lib, policy, adaptive):
+@pytest.mark.parametrize("block_aligned", [False, True])
+def test_builder_policies_match_oracle(lib, policy, adaptive, block_aligned):
     """The library's budget policies (tbr8.org deep dive 3.1, 3.2, 7.1) give
     the oracle's schedule on random mixes, including decode counts on both
     sides of the quota's 70% line and of the adaptive cap's 10 / 50 steps."""
-    rng = np.random.default_rng(7000 + 2 * ["truncate", "defer", "quota"].index(policy) + adaptive)
+    rng = np.random.default_rng(7000 + 4 * ["truncate", "defer", "quota"].index(policy)
+                                + 2 * adaptive + block_aligned)
     for _ in range(150):
         n = int(rng.integers(0, 80))
         pdec = float(rng.choice([0.0, 0.3, 0.7, 0.95]))
@@ -227,7 +230,7 @@ def test_builder_policies_match_oracle(lib, policy, adaptive):
         ndec = sum(r.is_decode for r in reqs)
         budget = int(rng.integers(max(1, ndec), max(2, ndec + int(rng.choice([8, 200, 4000])))))
         cap = int(rng.choice([16, 100, 512])) if adaptive else int(rng.choice([0, 0, 16, 512]))
-        kw = dict(policy=policy, adaptive=adaptive)
+        kw = dict(policy=policy, adaptive=adaptive, block_aligned=block_aligned)
         if policy == "quota":
             kw["max_prefill_tokens"] = int(rng.choice([1, 64, 1000, 6000]))
         G = int(rng.choice([1, 4, 8]))
@@ -263,13 +266,24 @@ def test_builder_defer_stops_at_first_misfit(lib):
     assert list(m["order"]) == [0, 1, 2] and list(m["num_scheduled"]) == [1, 40, 23]
 
 
+def test_builder_block_aligned_case(lib):
+    """The page-boundary rule on the oracle's hand-worked case: 32 streams,
+    budget 512, a prompt at 100 gets 476 tokens (ends at page boundary 576)
+    and the 4 left go to the next prompt."""
+    R = oracle.Request
+    reqs = [R(i, 30, 31, True) for i in range(32)] + [R(32, 100, 8192, False), R(33, 0, 100, False)]
+    m = same_as_oracle(reqs, 512, block_aligned=True)
+    assert list(m["num_scheduled"][32:]) == [476, 4] and m["seq_lens"][32] == 576
+
+
 def test_builder_rejects_unknown_policy_value(lib):
     """The C entry point itself rejects policy values it does not define."""
     reqs = (cpa.cpa_req_t * 1)(cpa.cpa_req_t(0, 0, 10, 0))
     bufs = [np.zeros(2, dtype=np.int32) for _ in range(6)]
-    for pol, quota, cap, ok in [(3, 0, 0, False), (0x200, 0, 0, False), (-1, 0, 0, False),
+    for pol, quota, cap, ok in [(3, 0, 0, False), (0x800, 0, 0, False), (-1, 0, 0, False),
                                 (2, 0, 0, False), (2, 2**31 - 64, 0, False), (2, 8, 0, True),
-                                (0x100, 0, 0, False), (0x101, 0, 16, True), (0, 0, 0, True)]:
+                                (0x100, 0, 0, False), (0x101, 0, 16, True), (0, 0, 0, True),
+                                (0x200, 0, 0, True), (0x302, 8, 16, True), (0x400, 0, 0, False)]:
         params = cpa.cpa_build_params_t(64, cap, 16, 8, 2, 128, 0, 0, pol, quota)
         meta = cpa.cpa_meta_t()
         meta.max_seqs = 1
