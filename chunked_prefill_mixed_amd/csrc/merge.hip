@@ -76,9 +76,13 @@ __device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ me
 
 // RPW rows of one (chunk merge entry, KV head) per workgroup; each row is
 // handled by LPR = D/4 lanes, each owning 4 consecutive d values, so a partial
-// row is one contiguous sweep.  The lanes of a row read the pieces' max and
-// sum in parallel (one piece per lane), then every lane sums the pieces' fp32
-// partials for its 4 values with up to 8 loads in flight.
+// row is one contiguous sweep.  Pieces are taken kChunkMergeBatch at a time:
+// every lane issues all loads of a batch (each piece's max and sum, the same
+// address for the row's lanes, and its 16 bytes of the piece's partial)
+// before using any, so a batch costs one memory round trip; batches fold into
+// a running max, sum and output as in the decode merge.
+constexpr int kChunkMergeBatch = 8;
+
 template <int D, int G>
 __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ merges, int block,
                                                  const int32_t* __restrict__ qsl, int num_q_heads,
@@ -99,29 +103,34 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
   if (j >= qe) return;  // past the chunk end
   const int64_t stride = (int64_t)num_kv_heads * kChunkRows;  // rows between consecutive slots
   const int64_t base = ((int64_t)first * num_kv_heads + g) * kChunkRows + r;
-
-  float M = neg_inf();
-  for (int i = li; i < n; i += LPR) M = fmaxf(M, part.m[base + i * stride]);
-#pragma unroll
-  for (int k = 1; k < LPR; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, LPR));
-  float L = 0.f;
-  for (int i = li; i < n; i += LPR)
-    L += part.l[base + i * stride] * fast_exp2(part.m[base + i * stride] - M);
-#pragma unroll
-  for (int k = 1; k < LPR; k <<= 1) L += __shfl_xor(L, k, LPR);
-
   const int d = 4 * li;
+
+  float M = neg_inf(), L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < n; i0 += LPR) {
-    const float wl = (i0 + li < n) ? fast_exp2(part.m[base + (i0 + li) * stride] - M) : 0.f;
-    const int cnt = min(LPR, n - i0);
-#pragma unroll 8
-    for (int k = 0; k < cnt; ++k) {
-      const float w = __shfl(wl, k, LPR);
-      const float4 a =
-          *reinterpret_cast<const float4*>(part.acc + (base + (i0 + k) * stride) * D + d);
-      o.x += w * a.x; o.y += w * a.y; o.z += w * a.z; o.w += w * a.w;
+  for (int i0 = 0; i0 < n; i0 += kChunkMergeBatch) {
+    float mi[kChunkMergeBatch], lv[kChunkMergeBatch];
+    float4 a[kChunkMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kChunkMergeBatch; ++i) {
+      const bool in = i0 + i < n;
+      const int64_t pr = base + (int64_t)(in ? i0 + i : i0) * stride;
+      mi[i] = in ? part.m[pr] : neg_inf();
+      lv[i] = part.l[pr];
+      a[i] = *reinterpret_cast<const float4*>(part.acc + pr * D + d);
     }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kChunkMergeBatch; ++i) Mb = fmaxf(Mb, mi[i]);
+    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
+    L *= alpha;
+    o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
+#pragma unroll
+    for (int i = 0; i < kChunkMergeBatch; ++i) {
+      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
+      L += w * lv[i];
+      o.x += w * a[i].x; o.y += w * a[i].y; o.z += w * a[i].z; o.w += w * a[i].w;
+    }
+    M = Mb;
   }
   const float inv = 1.f / L;
   const int hq = g * G + (r % G);
