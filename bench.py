@@ -430,7 +430,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: the attention step runs on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the path has no collectives or sharding.", file=sys.stderr)
         sys.exit(2)
 

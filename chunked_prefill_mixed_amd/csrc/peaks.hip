@@ -3,7 +3,7 @@
 // HBM bandwidth and an MFMA-only loop on random operands for dense bf16
 // matrix throughput.  The published MI355X
 // figures (8 TB/s, 2.5 PFLOP/s dense bf16) are the roofline peaks; these are
-// what the box sustains under the same clocks and power limits.
+// what the GPU sustains under the same clocks and power limits.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -17,7 +17,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Both streams give each workgroup one contiguous range of the buffer and use
 // non-temporal accesses with 8 16-byte words in flight per lane: the fastest
-// of the access patterns tried on the box (grid-stride and cached loads reach
+// of the access patterns tried on this GPU (grid-stride and cached loads reach
 // 10-20% less).
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
