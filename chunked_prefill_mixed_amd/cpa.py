@@ -271,10 +271,21 @@ def _check_dev(*tensors):
             raise ValueError("device call needs GPU tensors")
 
 
+def _check_cache(k_cache, v_cache, Hkv, D):
+    """K pages [num_blocks][Hkv][D/8][16][8] (16-token pages in 8-value pieces),
+    V pages [num_blocks][Hkv][D][16]."""
+    nb = k_cache.shape[0]
+    if tuple(k_cache.shape) != (nb, Hkv, D // 8, BLOCK_SIZE, 8) or \
+            tuple(v_cache.shape) != (nb, Hkv, D, BLOCK_SIZE):
+        raise ValueError(f"cache shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} do not match "
+                         f"K [nb, {Hkv}, {D // 8}, 16, 8] and V [nb, {Hkv}, {D}, 16]")
+
+
 def cpa_append_kv(k_new, v_new, query_start_loc, context_lens, block_table, k_cache, v_cache, *,
                   num_seqs, num_tokens, stream=None):
     _check_dev(k_new, v_new, query_start_loc, context_lens, block_table, k_cache, v_cache)
-    Hkv, D = k_cache.shape[1], k_cache.shape[3]
+    Hkv, D = k_new.shape[1], k_new.shape[2]
+    _check_cache(k_cache, v_cache, Hkv, D)
     st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _ptr(query_start_loc), _ptr(context_lens),
                               _ptr(block_table), int(block_table.shape[1]), int(num_seqs),
                               int(num_tokens), int(Hkv), int(D), BLOCK_SIZE, _ptr(k_cache),
@@ -290,6 +301,7 @@ def cpa_attention(q, k_cache, v_cache, block_table, query_start_loc, seq_lens, c
                workspace)
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k_cache.shape[1]
+    _check_cache(k_cache, v_cache, Hkv, D)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().cpa_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                               int(block_table.shape[1]), _ptr(query_start_loc), _ptr(seq_lens),

@@ -10,14 +10,18 @@
 // context_len and the page id: three dependent loads in all, where a binary
 // search would chain about log2(rows) of them.
 //
-// K rows are copied as 16-byte pieces into the token-major K page.  V pages
-// are stored transposed ([D][16] per page and KV head), so one token's V is a
-// column of 2-byte values.  V is therefore written per aligned group of 8
-// slots: the wave of the group's first new token loads the V rows of the
-// group's new tokens (coalesced, Hkv*D*2 bytes each), and every lane turns the
-// 8 values of each of its (head, d) pairs into one 16-byte store.  A group
-// that is only partly new (a decode row's token, the ends of a chunk) keeps
-// its other slots: only the new ones are written, 2 bytes each.
+// Both page layouts keep neighbouring slots side by side, so both are written
+// per aligned group of 8 slots.  K pages hold their keys in 8-value pieces
+// ([D/8][16][8] per KV head): piece c of the group's 8 slots is 128
+// contiguous bytes.  When all 8 slots are new (inside a chunk) the group's 8
+// waves share its K, wave r copying pieces r, r + 8, ... of all 8 slots, so
+// every store fills whole lines; otherwise (a decode row's token, the ends of
+// a chunk) each token's wave copies its own 16-byte pieces.  V pages are
+// stored transposed ([D][16]), so one token's V is a column of 2-byte values:
+// the wave of the group's first new token loads the V rows of the group's new
+// tokens (coalesced, Hkv*D*2 bytes each), and every lane turns the 8 values
+// of each of its (head, d) pairs into one 16-byte store.  A group that is
+// only partly new keeps its other slots: only the new ones are written.
 
 #include "device.h"
 #include "internal.h"
@@ -26,7 +30,7 @@
 namespace cpa {
 
 constexpr int kAppendWaves = 4;  // tokens per workgroup
-constexpr int kVGroup = 8;       // V slots written together (16 bytes)
+constexpr int kVGroup = 8;       // slots written together (16 bytes of a V row, 128 of a K piece)
 
 template <int D>
 __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(
@@ -40,14 +44,6 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(
   const int t = blockIdx.x * kAppendWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= num_tokens) return;  // whole wave; no barrier below
 
-  // the token's K row does not depend on its row: its first two 16-byte
-  // pieces per lane load while the row is looked up
-  const uint4* ksrc = reinterpret_cast<const uint4*>(k_new + (int64_t)t * num_kv_heads * D);
-  const int kpieces = num_kv_heads * kParts;
-  uint4 k0 = make_uint4(0, 0, 0, 0), k1 = make_uint4(0, 0, 0, 0);
-  if (lane < kpieces) k0 = ksrc[lane];
-  if (lane + 64 < kpieces) k1 = ksrc[lane + 64];
-
   // row s = #{i < num_seqs : qsl[i] <= t} - 1; qsl is non-decreasing and
   // qsl[num_seqs] = num_tokens > t
   int count = 0;
@@ -60,28 +56,55 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(
   const int q0 = qsl[s], c = ctx[s];
   const int p = c + (t - q0);
   const int64_t blk = bt[(int64_t)s * bt_stride + p / kBlock];
-  const int slot = p % kBlock;
   const int64_t page0 = blk * num_kv_heads * (int64_t)PAGE;
+  const int gbeg = p & ~(kVGroup - 1);
+  const int row_end = c + (qsl[s + 1] - q0);  // one past the row's last new position
+  const int hd = num_kv_heads * D;
+  const int kpieces = hd / 8;  // 16-byte pieces of a K row: e = head * D/8 + c
 
-  auto kdst = [&](int e) {
-    return reinterpret_cast<uint4*>(k_cache + page0 + (int64_t)(e / kParts) * PAGE + slot * D +
-                                    (e % kParts) * 8);
+  // K piece e of page slot o lands in piece row c of the head's page
+  auto kdst = [&](int e, int o) {
+    return reinterpret_cast<uint4*>(k_cache + page0 + (int64_t)(e / kParts) * PAGE +
+                                    ((e % kParts) * kBlock + o) * 8);
   };
-  if (lane < kpieces) *kdst(lane) = k0;
-  if (lane + 64 < kpieces) *kdst(lane + 64) = k1;
-  for (int e = lane + 128; e < kpieces; e += 64) *kdst(e) = ksrc[e];
+  if (gbeg >= c && gbeg + kVGroup <= row_end) {
+    // all 8 slots new: the pieces come in blocks of 8 and the wave in slot r
+    // of the group takes blocks b = r, r + 8, ...; lane (j = lane / 8,
+    // i = lane % 8) copies piece 8 b + i of slot j, so one instruction reads
+    // 8 whole 128-byte lines of k_new and writes 8 whole lines of the page
+    const int r = p - gbeg, j = lane / kVGroup, i = lane % kVGroup;
+    const uint16_t* src = k_new + (int64_t)(t - r + j) * hd;  // token of slot j
+    for (int b0 = r; b0 < kpieces / 8; b0 += 4 * 8) {
+      uint4 x[4];  // loads clamped into the token's row; stores only in range
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[u] = *reinterpret_cast<const uint4*>(src + min(8 * (b0 + 8 * u) + i, kpieces - 1) * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (b0 + 8 * u < kpieces / 8) *kdst(8 * (b0 + 8 * u) + i, gbeg % kBlock + j) = x[u];
+    }
+  } else {
+    // the token's own pieces
+    const uint16_t* src = k_new + (int64_t)t * hd;
+    for (int e0 = lane; e0 < kpieces; e0 += 4 * 64) {
+      uint4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[u] = *reinterpret_cast<const uint4*>(src + min(e0 + 64 * u, kpieces - 1) * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + 64 * u < kpieces) *kdst(e0 + 64 * u, p % kBlock) = x[u];
+    }
+  }
 
   // V: only the wave of a group's first new token
-  const int gbeg = p & ~(kVGroup - 1);
   if (p != gbeg && t != q0) return;
-  const int row_end = c + (qsl[s + 1] - q0);        // one past the row's last new position
   const int nnew = min(gbeg + kVGroup, row_end) - p;  // new slots p .. p + nnew - 1
   const int lo = p - gbeg;                            // first new slot inside the group
   const bool whole = lo == 0 && nnew == kVGroup;
   uint16_t* vpage = v_cache + page0 + (gbeg % kBlock);  // + g * PAGE + d * 16: the group's 8 slots
   // each lane takes 8 consecutive (head, d) values per pass: one 16-byte load
   // of each new token, one 16-byte store per (head, d)
-  const int hd = num_kv_heads * D;
   for (int f0 = lane * 8; f0 < hd; f0 += 64 * 8) {
     uint4 x[kVGroup];  // x[j]: the values of slot j (token t + j - lo) when new
 #pragma unroll

@@ -60,8 +60,8 @@ int adaptive_cap(int base_chunk, int num_decodes) {
 
 // Pages per decode piece when the caller leaves the split size to the
 // planner.  Decode is bound by HBM bandwidth, so its time is the time of the
-// longest wave: pick the fewest passes k of R resident waves (R from
-// decode_waves_target) for which pieces of at most 64 pages exist, then the
+// longest wave: pick the fewest rounds k of R waves (R = decode_waves_target,
+// one per SIMD) for which pieces of at most 64 pages exist, then the
 // smallest page count p such that the rows, each cut into ceil(pages/p)
 // pieces, give at most k * R waves (piece x KV head).  Every wave then
 // starts in pass 1..k and no wave reads more than p pages.  p is kept at 8 pages or

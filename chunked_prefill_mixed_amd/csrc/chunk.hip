@@ -25,11 +25,13 @@
 // global_load_lds_dwordx4 (straight from memory into LDS, no register
 // staging); the next tile's loads are in flight while the current one is
 // computed.  The lane-to-LDS-slot order of those loads is fixed, so the LDS
-// layout is chosen by which 16 bytes each lane fetches: K row r keeps its
-// 16-byte d pieces XOR-permuted by swz(r), V^T rows keep their two 8-key
-// halves swapped when bit 3 of d is set (conflict-free fragment reads for
-// both).  A tile that reaches past the piece's last key goes through
-// registers instead, so the V slots past the end can be zeroed.
+// layout is chosen by which 16 bytes each lane fetches.  K pages hold their
+// keys in 8-value pieces ([D/8][16][8]) and are copied as they are: the 16
+// keys a 16-lane group reads at one piece are 256 contiguous bytes, which
+// covers all 64 banks.  V^T rows keep their two 8-key halves swapped when
+// bit 3 of d is set (conflict-free fragment reads).  A tile that reaches past
+// the piece's last key goes through registers instead, so the V slots past
+// the end can be zeroed.
 // Only tiles that reach past the first query's last visible key apply the
 // causal mask.
 //
@@ -60,7 +62,6 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials part) {
   constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;               // 32-row d blocks of O^T
-  constexpr int CPR = D / 8;               // 16-byte pieces per K row
   constexpr int PAGE = kBlock * D;         // elements of one (page, KV head)
   constexpr int CHUNKS = 4 * PAGE / 8;     // 16-byte pieces per 64-key tile (K or V)
   constexpr int PER_THREAD = CHUNKS / 256;
@@ -69,9 +70,6 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   // two stages: one tile is read while the next is written
   __shared__ __align__(16) uint16_t k_lds_buf[2][kKvTile * D];
   __shared__ __align__(16) uint16_t v_lds_buf[2][4 * PAGE];
-  // K row r's d piece c sits in 16-byte slot c ^ swz(r) of the row: the 16
-  // rows one 16-lane group reads at the same c then cover all 64 banks
-  auto swz = [](int r) { return (r / (128 / D)) % CPR; };
 
   const int item = xcd_remap(blockIdx.x, num_tiles * num_kv_heads);
   const int g = item / num_tiles;
@@ -176,10 +174,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
   // a whole tile below kv_end: thread tid fills 16-byte LDS slot p = tid +
   // 256 i of the K and of the V stage.  Slot p lies in page p / (PAGE / 8) of
   // the tile (the same page for the whole wave) and at the same place inside
-  // it for every i: K slot p holds key p / CPR, piece (p % CPR) ^ swz(key);
-  // V slot s = p % (PAGE / 8) holds row d = s / 2, half (s & 1) ^ bit 3 of d.
-  const uint32_t k_lane_bytes =
-      2u * (((tid / CPR) % kBlock) * D + 8 * ((tid % CPR) ^ swz(tid / CPR)));
+  // it for every i: K slot s = p % (PAGE / 8) is the page's own slot s (piece
+  // s / 16 of key s % 16); V slot s holds row d = s / 2, half (s & 1) ^ bit 3
+  // of d.
+  const uint32_t k_lane_bytes = 16u * (tid % (PAGE / 8));
   const int v_s = tid % (PAGE / 8), v_d = v_s >> 1;
   const uint32_t v_lane_bytes = 2u * (v_d * kBlock + 8 * ((v_s & 1) ^ ((v_d >> 3) & 1)));
   auto issue_direct = [&](int stage, const int (&ids)[PER_THREAD]) {
@@ -201,9 +199,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
       const int cidx = tid + 256 * i;
       const int kp = cidx / (PAGE / 8);
       const int w = cidx % (PAGE / 8);
-      const int key = kp * kBlock + w / (D / 8);
-      const int dpiece = w % (D / 8);
-      *reinterpret_cast<uint4*>(&k_lds[key * D + 8 * (dpiece ^ swz(key))]) = kreg[i];
+      *reinterpret_cast<uint4*>(&k_lds[kp * PAGE + w * 8]) = kreg[i];
       // V^T row d = w/2 keeps its two 8-key halves swapped when bit 3 of d is
       // set, so 16 lanes reading half 0 of rows d..d+15 hit distinct banks
       const int d = w >> 1, hh = (w & 1) ^ ((d >> 3) & 1);
@@ -259,8 +255,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     uint4 ka[2 * KS];
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
+      // key kr = 32 (i & 1) + krow of the tile, piece 2 (i >> 1) + half
       const int kr = 32 * (i & 1) + krow;
-      ka[i] = *reinterpret_cast<const uint4*>(&k_lds[kr * D + 8 * ((2 * (i >> 1) + half) ^ swz(kr))]);
+      ka[i] = *reinterpret_cast<const uint4*>(
+          &k_lds[(kr / kBlock) * PAGE + ((2 * (i >> 1) + half) * kBlock + kr % kBlock) * 8]);
     }
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i)

@@ -10,10 +10,13 @@
 // run on the matrix cores so the wave's vector work per page stays small
 // next to the time its 8 KiB take to arrive:
 //   S^T[16 keys][16 cols] = K Q^T      v_mfma_f32_16x16x32_bf16, D/32 steps;
-//                                      K page rows are the A operand as
-//                                      loaded, column n of Q^T holds query
-//                                      head n % G (columns n >= G repeat heads
-//                                      and are never stored)
+//                                      K pages hold their keys in 8-value
+//                                      pieces ([D/8][16][8]), so the A operand
+//                                      of step kk (pieces 4kk..4kk+3 of all 16
+//                                      keys) is one contiguous 1 KB load;
+//                                      column n of Q^T holds query head n % G
+//                                      (columns n >= G repeat heads and are
+//                                      never stored)
 //   O^T[D][16 cols] += V^T P^T         v_mfma_f32_16x16x16_bf16, D/16 blocks;
 //                                      V pages are stored transposed ([D][16])
 //                                      so each lane loads its A operand as 8
@@ -83,7 +86,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
   // Loads go through a buffer resource built per page from the wave-uniform
   // page address: scalar base, fixed per-lane byte offsets, and the hardware
   // range check keeps every access inside the one (page, KV head) piece.
-  const uint32_t kbyte = (uint32_t)(n * D + 8 * g4) * 2;   // + 64 kk: K[n][32 kk + 8 g4 ..]
+  // K[n][32 kk + 8 g4 ..] is piece 4 kk + g4 of key n: byte 1024 kk + 16 (16 g4 + n)
+  const uint32_t kbyte = (uint32_t)lane * 16;              // + 1024 kk
   const uint32_t vbyte = (uint32_t)(n * kBlock + 4 * g4) * 2;  // + 512 mb: V^T[16 mb + n][4 g4 ..]
   uint4 kset[kStages][KK];
   uint2 vset[kStages][MB];
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
     const auto kr = make_page_rsrc(k_cache + page, PAGE_BYTES);
     const auto vr = make_page_rsrc(v_cache + page, PAGE_BYTES);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kd[kk] = buffer_load16<kNonTemporal>(kr, kbyte + 64 * kk);
+    for (int kk = 0; kk < KK; ++kk) kd[kk] = buffer_load16<kNonTemporal>(kr, kbyte + 1024 * kk);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) vd[mb] = buffer_load8<kNonTemporal>(vr, vbyte + 512 * mb);
   };

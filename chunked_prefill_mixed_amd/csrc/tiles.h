@@ -6,15 +6,15 @@ namespace cpa {
 constexpr int kBlock = 16;          // tokens per KV page
 constexpr int kChunkRows = 128;     // (token, head) query rows per chunk workgroup: 4 waves x 32
 constexpr int kKvTile = 64;         // keys per LDS-staged K/V tile in the chunk kernel (4 pages)
-// Decode waves resident at once on 256 CUs x 4 SIMDs: the decode kernel's
-// register use leaves room for 3 waves per SIMD at head_dim 128 and 4 at 64.
+// Decode waves per launch round: one per SIMD of the 256 CUs.  The kernel's
+// registers would allow 2 waves per SIMD at head_dim 128 and 4 at 64, but
+// longer pieces at one wave per SIMD read as fast or faster (less start-up
+// and fewer partial results per byte), and a whole number of workgroups per
+// CU keeps every CU's share of the bytes equal; the planner adds whole
+// rounds only when pieces would exceed 64 pages.
 inline int decode_waves_target(int head_dim) {
-#ifdef CPA_DECODE_WAVES_TARGET
   (void)head_dim;
-  return CPA_DECODE_WAVES_TARGET;
-#else
-  return 256 * 4 * (head_dim > 64 ? 3 : 4);
-#endif
+  return 256 * 4;
 }
 constexpr int kDecodeMaxSplit = 64 * kBlock;  // a decode split spans at most 64 pages
 constexpr int kChunkWgTarget = 512;       // chunk workgroups resident at once (2 per CU): one round

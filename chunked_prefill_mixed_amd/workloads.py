@@ -59,7 +59,7 @@ class Workload:
     long_prefill_cap: int
     requests: list
     block_table: np.ndarray  # int32 [n_requests, max_blocks], queue order
-    k_pool: np.ndarray  # uint16 [NB, Hkv, 16, D]
+    k_pool: np.ndarray  # uint16 [NB, Hkv, D/8, 16, 8]
     v_pool: np.ndarray  # uint16 [NB, Hkv, D, 16]
     q: np.ndarray  # uint16 [budget, Hq, D]
     k_new: np.ndarray  # uint16 [budget, Hkv, D]
@@ -141,7 +141,7 @@ def build(name: str, seed: int, instance: int, *, num_q_heads: int, num_kv_heads
     k_new = normal_bf16(streams["k"], token_budget * Hkv * D).reshape(token_budget, Hkv, D)
     v_new = normal_bf16(streams["v"], token_budget * Hkv * D).reshape(token_budget, Hkv, D)
 
-    k_pool = np.full((nb, Hkv, BLOCK_SIZE, D), SENTINEL, dtype=np.uint16)
+    k_pool = np.full((nb, Hkv, D // 8, BLOCK_SIZE, 8), SENTINEL, dtype=np.uint16)
     v_pool = np.full((nb, Hkv, D, BLOCK_SIZE), SENTINEL, dtype=np.uint16)
     # pages holding at least one cached position, with their count of valid slots
     filled_ids, valid = [], []
@@ -156,11 +156,11 @@ def build(name: str, seed: int, instance: int, *, num_q_heads: int, num_kv_heads
         page_elems = Hkv * BLOCK_SIZE * D
         kv_seq, = streams["pool"].spawn(1)
         ks, vs = kv_seq.spawn(2)
-        kp = normal_bf16(ks, len(filled_ids) * page_elems).reshape(-1, Hkv, BLOCK_SIZE, D)
+        kp = normal_bf16(ks, len(filled_ids) * page_elems).reshape(-1, Hkv, D // 8, BLOCK_SIZE, 8)
         vp = normal_bf16(vs, len(filled_ids) * page_elems).reshape(-1, Hkv, D, BLOCK_SIZE)
         slot = np.arange(BLOCK_SIZE)
         empty = slot[None, :] >= valid[:, None]  # [pages, 16]
-        kp[np.broadcast_to(empty[:, None, :, None], kp.shape)] = SENTINEL
+        kp[np.broadcast_to(empty[:, None, None, :, None], kp.shape)] = SENTINEL
         vp[np.broadcast_to(empty[:, None, None, :], vp.shape)] = SENTINEL
         k_pool[filled_ids] = kp
         v_pool[filled_ids] = vp

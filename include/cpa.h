@@ -40,7 +40,9 @@
  *     {1, 2, 4, 8}; block_size 16; bf16 only.
  *
  * KV cache layout (one tensor each for K and V; the same page id in both)
- *   k_cache [num_blocks][num_kv_heads][16][head_dim]   token-major in a page
+ *   k_cache [num_blocks][num_kv_heads][head_dim/8][16][8]
+ *       a page's keys in 8-value pieces: element d of slot s sits at
+ *       [d/8][s][d%8], so each 1 KB run holds 4 pieces of all 16 keys
  *   v_cache [num_blocks][num_kv_heads][head_dim][16]   transposed in a page
  *   Position p of a row lives in page block_table[row][p / 16], slot p % 16.
  *

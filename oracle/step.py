@@ -33,9 +33,10 @@ design notes):
 * Query head h reads KV head h // (Hq / Hkv).
 * A prefill that does not fit the remaining budget is truncated to it (P1 and
   P5), not deferred; several prefills may share a step, in FCFS order.
-* Cache layout: K pages are [num_blocks, Hkv, 16, D]; V pages are stored
-  transposed inside each page, [num_blocks, Hkv, D, 16].  Both are bf16 bit
-  patterns (uint16 here).
+* Cache layout (the library's own choice; the pages fix only 16-token
+  pages): a K page holds its 16 keys in 8-value pieces, piece-major,
+  [num_blocks, Hkv, D/8, 16, 8]; V pages are stored transposed inside each
+  page, [num_blocks, Hkv, D, 16].  Both are bf16 bit patterns (uint16 here).
 """
 
 from __future__ import annotations
@@ -221,7 +222,7 @@ def append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.
             p = context_lens[s] + (t - query_start_loc[s])
             b = int(block_table[s][p // BLOCK_SIZE])
             o = p % BLOCK_SIZE
-            K[b, :, o, :] = k_new[t]
+            K[b, :, :, o, :] = k_new[t].reshape(K.shape[1], -1, 8)  # [Hkv, D/8, 8]
             V[b, :, :, o] = v_new[t]
     return K, V
 
@@ -246,12 +247,23 @@ def _kv_head(h: int, group: int) -> int:
     return h // group
 
 
+def k_rows(k_pool, blocks, g, offs):
+    """K rows [len(blocks), D] (bits) of slots offs[i] of pages blocks[i],
+    KV head g: the 8-value pieces of one key are gathered across the page's
+    D/8 piece rows."""
+    blocks = np.asarray(blocks)
+    # the index arrays are split by a slice, so numpy puts their common
+    # dimension first: [n, D/8, 8]
+    pieces = k_pool[blocks, g, :, np.asarray(offs), :]
+    return pieces.reshape(len(blocks), -1)
+
+
 def _row_keys(k_pool, v_pool, block_table_row, g, length):
     """K and V of keys [0, length) of one row and KV head, as [length, D] fp64."""
     pos = np.arange(length)
     blocks = np.asarray(block_table_row)[pos // BLOCK_SIZE]
     offs = pos % BLOCK_SIZE
-    Ks = bf16_bits_to_f64(k_pool[blocks, g, offs, :])
+    Ks = bf16_bits_to_f64(k_rows(k_pool, blocks, g, offs))
     Vs = bf16_bits_to_f64(v_pool[blocks, g, :, offs])
     return Ks, Vs
 
@@ -264,7 +276,7 @@ def softmax_weights(q, k_pool, block_table_row, context_len, q_row_start, j, h, 
     length = context_len + j + 1
     pos = np.arange(length)
     blocks = np.asarray(block_table_row)[pos // BLOCK_SIZE]
-    Ks = bf16_bits_to_f64(k_pool[blocks, g, pos % BLOCK_SIZE, :])
+    Ks = bf16_bits_to_f64(k_rows(k_pool, blocks, g, pos % BLOCK_SIZE))
     s = scale * (Ks @ bf16_bits_to_f64(q[q_row_start + j, h]))
     w = np.exp(s - s.max())
     return w / w.sum()

@@ -37,12 +37,13 @@ def as_float(b):
 def page_dense(K, V, block_ids, num_blocks):
     """Place dense per-position K/V [L, Hkv, D] (bits) into fresh pools."""
     L, Hkv, D = K.shape
-    kp = np.full((num_blocks, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+    kp = np.full((num_blocks, Hkv, D // 8, BS, 8), 0xFFFF, dtype=np.uint16)
     vp = np.full((num_blocks, Hkv, D, BS), 0xFFFF, dtype=np.uint16)
     for p in range(L):
         b = block_ids[p // BS]
         for g in range(Hkv):
-            kp[b, g, p % BS, :] = K[p, g]
+            for d in range(D):
+                kp[b, g, d // 8, p % BS, d % 8] = K[p, g, d]
             vp[b, g, :, p % BS] = V[p, g]
     return kp, vp
 
@@ -106,7 +107,7 @@ def run_oracle_chunk(q, K, V, ids, nb, c, Hkv, scale):
 BRUTE_CASES = [
     (Hq, G, D, c, n)
     for (Hq, G) in [(1, 1), (4, 1), (4, 2)]
-    for D in (4, 8)
+    for D in (8, 16)
     for c in (0, 1, 15, 16, 17)
     for n in (1, 2, 5, 16)
 ]
@@ -156,7 +157,7 @@ def test_chunking_invariance(L):
     bt = ids[None, :].astype(np.int32)
     results = {}
     for C in (1, 3, 16, 64, 100, L):
-        kp = np.full((nb, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+        kp = np.full((nb, Hkv, D // 8, BS, 8), 0xFFFF, dtype=np.uint16)
         vp = np.full((nb, Hkv, D, BS), 0xFFFF, dtype=np.uint16)
         outs = []
         for a in range(0, L, C):
@@ -264,7 +265,7 @@ def test_append_touches_exactly_the_new_slots_and_is_idempotent():
     bt = rng.permutation(nb)[: 4 * 4].reshape(4, 4).astype(np.int32)
     T = sum(nq)
     qsl = np.concatenate([[0], np.cumsum(nq)]).tolist()
-    kp0 = bits(rng.standard_normal((nb, Hkv, BS, D)))
+    kp0 = bits(rng.standard_normal((nb, Hkv, D // 8, BS, 8)))
     vp0 = bits(rng.standard_normal((nb, Hkv, D, BS)))
     kn = bits(rng.standard_normal((T, Hkv, D)))
     vn = bits(rng.standard_normal((T, Hkv, D)))
@@ -276,10 +277,15 @@ def test_append_touches_exactly_the_new_slots_and_is_idempotent():
             p = ctx[s] + i
             slots.add((int(bt[s, p // BS]), p % BS))
             t = qsl[s] + i
-            assert np.array_equal(kp[bt[s, p // BS], :, p % BS, :], kn[t])
-            assert np.array_equal(vp[bt[s, p // BS], :, :, p % BS], vn[t])
+            b, o = int(bt[s, p // BS]), p % BS
+            # K element (g, d) of slot o: piece d // 8 of the page, offset d % 8
+            for g in range(Hkv):
+                for d in range(D):
+                    flat = (((b * Hkv + g) * (D // 8) + d // 8) * BS + o) * 8 + d % 8
+                    assert kp.ravel()[flat] == kn[t, g, d]
+                    assert vp.ravel()[((b * Hkv + g) * D + d) * BS + o] == vn[t, g, d]
     assert len(slots) == T  # injective
-    kdiff = np.any(kp != kp0, axis=(1, 3))  # [nb, slot]
+    kdiff = np.any(kp != kp0, axis=(1, 2, 4))  # [nb, slot]
     vdiff = np.any(vp != vp0, axis=(1, 2))
     changed = {(b, o) for b, o in zip(*np.nonzero(kdiff | vdiff))}
     assert changed <= slots
@@ -539,7 +545,7 @@ def test_block_aligned_invariants_on_random_mixes():
 
 def _pins_pass():
     try:
-        for args in [(4, 2, 8, 17, 5), (4, 1, 4, 0, 16), (1, 1, 8, 16, 2)]:
+        for args in [(4, 2, 8, 17, 5), (4, 1, 8, 0, 16), (1, 1, 8, 16, 2)]:
             test_brute_force_dense(*args)
         test_closed_form_zero_query_cumulative_mean(5)
         test_decode_row_equals_last_prefill_row()
@@ -553,7 +559,7 @@ def test_pins_pass_unmutated():
 
 
 @pytest.mark.parametrize("mutation", ["mask_off_by_one", "mask_strict", "head_map_modulo",
-                                      "v_read_as_k_layout", "drop_scale"])
+                                      "v_read_as_k_layout", "k_read_token_major", "drop_scale"])
 def test_planted_mistake_is_caught(monkeypatch, mutation):
     if mutation == "mask_off_by_one":
         monkeypatch.setattr(ostep, "_visible", lambda pos, c, js: pos[None, :] <= (c + js + 1)[:, None])
@@ -569,6 +575,10 @@ def test_planted_mistake_is_caught(monkeypatch, mutation):
             Ks, Vs = orig(k_pool, v_pool, bt_row, g, length)
             return Ks, Vs[::-1].copy()
         monkeypatch.setattr(ostep, "_row_keys", bad)
+    elif mutation == "k_read_token_major":
+        # the page's bits taken as [16][D] rows instead of [D/8][16][8] pieces
+        monkeypatch.setattr(ostep, "k_rows", lambda kp, blocks, g, offs: kp[np.asarray(blocks), g].reshape(
+            len(blocks), BS, -1)[np.arange(len(blocks)), np.asarray(offs)])
     elif mutation == "drop_scale":
         orig_att = ostep.attention
 
