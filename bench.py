@@ -18,7 +18,7 @@ last-level cache from the previous step.
 
 Prints ONE JSON line on stdout.  Per-kernel durations come from HIP events
 recorded on the launch stream around each launch inside the timed region, on
-every fifth timed step (``--kernel-event-stride``); the other steps carry no
+every eleventh timed step (``--kernel-event-stride``); the other steps carry no
 events at all (each marker costs a few microseconds of GPU time between two
 launches), and the step rate is the wall clock over all timed steps.
 """
@@ -418,7 +418,7 @@ def main():
                     help="replay each instance's append + attention as one captured HIP graph on "
                          "the unsampled steps (the host metadata build and its copy still run "
                          "every step, outside the graph)")
-    ap.add_argument("--kernel-event-stride", type=int, default=5,
+    ap.add_argument("--kernel-event-stride", type=int, default=11,
                     help="record the per-kernel HIP events on every n-th timed step only (the "
                          "others carry just the step's start and end events, since a marker "
                          "between launches keeps a kernel from starting while the previous one "
