@@ -527,6 +527,12 @@ def main():
         v = kernels[n].get(unit)
         kernels[n]["frac_of_peak"] = None if v is None else v / peak
 
+    # the decode rate with the whole merge launch (decode and chunk merges
+    # together) added to the decode kernel's time
+    t_dm = times["decode_kernel"] + times["merge_kernel"]
+    kernels["decode_kernel"]["frac_of_peak_with_merge_launch"] = (
+        work["decode_bytes"] / t_dm / 1e9 / HBM_PEAK_GBS if t_dm > 0 else None)
+
     dominant = max(("decode_kernel", "chunk_kernel", "append_kernel"), key=lambda n: times[n])
     if dominant == "chunk_kernel":
         ach = kernels["chunk_kernel"]["TFLOP/s"]
@@ -574,6 +580,9 @@ def main():
         "gpu_step_us": gpu_step / NS * 1e6,
         "metadata_upload_us": copy_us / NS,
         "measured_peaks": peaks,
+        "device": {"name": torch.cuda.get_device_name(0),
+                   "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+                   "hip": torch.version.hip, "torch": torch.__version__},
         "kernel_events": {"stride": stride, "sampled_steps": NS},
     }
     if not args.no_cpu_baseline:

@@ -107,6 +107,53 @@ SMALL = [
 ]
 
 
+WIDE = [
+    # many KV heads: the append copies several 64-piece passes per token, and
+    # G = 1 / 2 / 4 decode and chunk kernels at Hkv = 32 / 16 / 16
+    (32, 32, 64, [0, 17, 700], [(33, 33 + 100)], 32),
+    (32, 16, 128, [5, 1500], [(0, 77), (200, 300)], 0),
+    (64, 16, 128, [256, 31], [(1000, 1100)], 64),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE)))
+def test_wide_head_counts(case):
+    Hq, Hkv, D, dec, chunks, split = WIDE[case]
+    w = workloads.random_workload(600 + case, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  decode_ctx=dec, chunks=chunks)
+    check_step(w, decode_split_tokens=split, label=f"wide{case}")
+
+
+def test_empty_step_touches_nothing():
+    """num_tokens = 0: both device calls return CPA_OK without a launch, and
+    the cache and the output buffer keep their bits."""
+    import ctypes
+    import torch
+    w = workloads.random_workload(83, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                  decode_ctx=[40], chunks=[])
+    ds = DeviceStep(w)
+    ds.out.fill_(1.5)
+    k0, v0, o0 = ds.k_cache.clone(), ds.v_cache.clone(), ds.out.clone()
+    lib = cpa.load()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = lib.cpa_append_kv(P(ds.k_new), P(ds.v_new), P(ds.query_start_loc), P(ds.context_lens),
+                           P(ds.block_table), int(ds.block_table.shape[1]), ds.num_seqs, 0, 2, 64,
+                           16, P(ds.k_cache), P(ds.v_cache), stream)
+    assert st == cpa.CPA_OK
+    counts = cpa.cpa_plan_counts_t()
+    st = lib.cpa_attention(P(ds.q), P(ds.k_cache), P(ds.v_cache), P(ds.block_table),
+                           int(ds.block_table.shape[1]), P(ds.query_start_loc), None,
+                           P(ds.context_lens), P(ds.plan), ctypes.byref(counts), 0, 0, 0, 8, 2,
+                           64, 16, ctypes.c_float(0.125), P(ds.out), None, None,
+                           ctypes.c_size_t(0), stream)
+    assert st == cpa.CPA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(ds.k_cache.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(ds.v_cache.view(torch.int16), v0.view(torch.int16))
+    assert torch.equal(ds.out, o0)
+
+
 @pytest.mark.parametrize("case", range(len(SMALL)))
 def test_small_mixed_steps(case):
     Hq, Hkv, D, dec, chunks, split = SMALL[case]
