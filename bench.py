@@ -57,8 +57,8 @@ WORKLOAD_TEXT = {
 }
 
 KERNEL_SOURCES = {
-    "decode_kernel": ["decode.hip", "device.h", "tiles.h"],
-    "chunk_kernel": ["chunk.hip", "device.h", "tiles.h"],
+    "decode_kernel": ["decode.hip", "decode_body.h", "device.h", "tiles.h"],
+    "chunk_kernel": ["chunk.hip", "chunk_body.h", "device.h", "tiles.h"],
     "append_kernel": ["append.hip", "device.h", "tiles.h"],
     "merge_kernel": ["merge.hip", "device.h", "tiles.h"],
 }

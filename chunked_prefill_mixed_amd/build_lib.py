@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpa.so")
 PEAKS_LIB = os.path.join(PKG, "libcpa_peaks.so")
 
-HIP_SOURCES = ["append.hip", "decode.hip", "chunk.hip", "merge.hip", "abi.hip"]
+HIP_SOURCES = ["append.hip", "decode.hip", "chunk.hip", "mixed.hip", "merge.hip", "abi.hip"]
 HOST_SOURCES = ["builder.cpp"]
 ARCH = os.environ.get("CPA_OFFLOAD_ARCH", "gfx950")
 

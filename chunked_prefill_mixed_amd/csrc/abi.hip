@@ -81,14 +81,24 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
   const int32_t* dmerges = tiles + (size_t)n.num_chunk_tiles * CPA_CHUNK_TILE_WORDS;
   const int32_t* cmerges = dmerges + (size_t)n.num_decode_merges * CPA_DECODE_MERGE_WORDS;
 
-  // decode splits and chunk tiles are independent; the merges (one launch) follow them
-  if (n.num_decode_splits > 0) {
+  // decode splits and chunk tiles are independent (one launch when both are
+  // present and the chunk tiles fill a resident round); the merges (one
+  // launch) follow them
+  const bool mixed = n.num_decode_splits > 0 &&
+                     (int64_t)n.num_chunk_tiles * num_kv_heads >= cpa::mixed_slots(head_dim);
+  if (mixed) {
+    st = status_of(cpa::launch_mixed(q, k_cache, v_cache, d_block_table, bt_stride,
+                                     d_query_start_loc, d_context_lens, tiles, n.num_chunk_tiles,
+                                     splits, n.num_decode_splits, num_q_heads, num_kv_heads,
+                                     head_dim, sl2, out, lse, cws, dws, s));
+    if (st != CPA_OK) return st;
+  } else if (n.num_decode_splits > 0) {
     st = status_of(cpa::launch_decode(q, k_cache, v_cache, d_block_table, bt_stride,
                                       d_query_start_loc, splits, n.num_decode_splits, num_q_heads,
                                       num_kv_heads, head_dim, sl2, out, lse, dws, s));
     if (st != CPA_OK) return st;
   }
-  if (n.num_chunk_tiles > 0) {
+  if (!mixed && n.num_chunk_tiles > 0) {
     st = status_of(cpa::launch_chunk(q, k_cache, v_cache, d_block_table, bt_stride,
                                      d_query_start_loc, d_context_lens, tiles, n.num_chunk_tiles,
                                      num_q_heads, num_kv_heads, head_dim, sl2, out, lse, cws, s));

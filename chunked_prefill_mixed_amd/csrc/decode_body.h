@@ -1,0 +1,211 @@
+// Split-KV decode attention, the body of one decode workgroup: the decode
+// kernel (decode.hip) and the mixed launch (mixed.hip) run it.  Its pieces
+// are merged by merge_kernel (merge.hip).
+//
+// A decode row's single query reads its whole cached context from HBM each
+// step ("How Chunked Prefill Stops Decode Starvation", "The stall"; tbr8.org
+// deep dive section 1), so this kernel is bound by HBM bandwidth: about 4
+// flops per byte of K/V at 4 query heads per KV head.
+//
+// One wave per (key piece, KV head).  All G query heads that share the KV
+// head are served by the one read of each 16-token page, and both products
+// run on the matrix cores so the wave's vector work per page stays small
+// next to the time its 8 KiB take to arrive:
+//   S^T[16 keys][16 cols] = K Q^T      v_mfma_f32_16x16x32_bf16, D/32 steps;
+//                                      K pages hold their keys in 8-value
+//                                      pieces ([D/8][16][8]), so the A operand
+//                                      of step kk (pieces 4kk..4kk+3 of all 16
+//                                      keys) is one contiguous 1 KB load;
+//                                      column n of Q^T holds query head n % G
+//                                      (columns n >= G repeat heads and are
+//                                      never stored)
+//   O^T[D][16 cols] += V^T P^T         v_mfma_f32_16x16x16_bf16, D/16 blocks;
+//                                      V pages are stored transposed ([D][16])
+//                                      so each lane loads its A operand as 8
+//                                      contiguous bytes, and P^T is the S^T
+//                                      accumulator itself (lane (g4, n) holds
+//                                      keys 4*g4..+4 of column n in both)
+// Online softmax per column in fp32: the 4 keys of a lane, then across the 4
+// lane groups with two exchanges.  The reference max only moves when a page
+// exceeds it by more than 2^8 (always on the first page), so the accumulator
+// rescale is rare; numerator and denominator share the reference.  A row
+// covered by one piece writes its bf16 output directly; otherwise each piece
+// writes unnormalised fp32 (acc, max, sum) and merge_kernel (merge.hip) combines
+// them:
+//   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
+
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+#include "tiles.h"
+
+#ifndef CPA_DECODE_STAGES
+#define CPA_DECODE_STAGES 2   // pages each wave holds in registers: one computed, the rest loading
+#endif
+
+namespace cpa {
+
+constexpr int kDecodeWaves = 4;  // independent (piece, KV head) waves per workgroup
+constexpr int kStages = CPA_DECODE_STAGES;
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// The work of decode workgroup wg (4 waves, items 4 wg .. 4 wg + 3).
+template <int D, int G>
+__device__ __forceinline__ void decode_body(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
+    const int32_t* __restrict__ splits, int num_q_heads, int num_kv_heads, int num_items,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials ws, int wg) {
+  constexpr int KK = D / 32;  // S^T steps over d
+  constexpr int MB = D / 16;  // O^T blocks of 16 d rows
+  constexpr int PAGE_BYTES = kBlock * D * 2;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int item = wg * kDecodeWaves + wave;
+  if (item >= num_items) return;  // whole wave; no workgroup barrier below
+  const int g = item % num_kv_heads;
+  const int4 e = reinterpret_cast<const int4*>(splits)[item / num_kv_heads];
+  const int row = e.x, kv_begin = e.y, kv_end = e.z, slot = e.w;
+  // decode rows come first and hold one token each, so row s is packed token s
+  const int t = row;
+  const int n = lane & 15;   // column: query head n % G of the group
+  const int g4 = lane >> 4;  // lane group: d pieces of S^T, keys 4*g4..+4 of P^T and O^T
+  const int hq = g * G + n % G;
+
+  // B operand of S^T: Q[hq][32 kk + 8 g4 .. +8]
+  uint4 qf[KK];
+  {
+    const uint16_t* qrow = q + ((int64_t)t * num_q_heads + hq) * D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+  }
+
+  const int32_t* btrow = bt + (int64_t)row * bt_stride;
+  // a piece spans at most 64 pages (the planner guarantees it): one
+  // coalesced load of its page ids, then v_readlane per page
+  const int pg0 = kv_begin / kBlock, npages = (kv_end + kBlock - 1) / kBlock - pg0;
+  const int my_blk = btrow[pg0 + min(lane, npages - 1)];
+  // Loads go through a buffer resource built per page from the wave-uniform
+  // page address: scalar base, fixed per-lane byte offsets, and the hardware
+  // range check keeps every access inside the one (page, KV head) piece.
+  // K[n][32 kk + 8 g4 ..] is piece 4 kk + g4 of key n: byte 1024 kk + 16 (16 g4 + n)
+  const uint32_t kbyte = (uint32_t)lane * 16;              // + 1024 kk
+  const uint32_t vbyte = (uint32_t)(n * kBlock + 4 * g4) * 2;  // + 512 mb: V^T[16 mb + n][4 g4 ..]
+  uint4 kset[kStages][KK];
+  uint2 vset[kStages][MB];
+  auto load_page = [&](int i, uint4 (&kd)[KK], uint2 (&vd)[MB]) {
+    const int blk = __builtin_amdgcn_readlane(my_blk, i);
+    const int64_t page = ((int64_t)blk * num_kv_heads + g) * (kBlock * D);
+    const auto kr = make_page_rsrc(k_cache + page, PAGE_BYTES);
+    const auto vr = make_page_rsrc(v_cache + page, PAGE_BYTES);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kd[kk] = buffer_load16<kNonTemporal>(kr, kbyte + 1024 * kk);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) vd[mb] = buffer_load8<kNonTemporal>(vr, vbyte + 512 * mb);
+  };
+
+  float m = neg_inf(), lsum = 0.f;
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_page = [&](int i, const uint4 (&kc)[KK], uint2 (&vc)[MB]) {
+    const int key0 = (pg0 + i) * kBlock;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[kk]),
+                                                  __builtin_bit_cast(bf16x8_t, qf[kk]), s, 0, 0,
+                                                  0);
+    // the piece's last page (or one past it): mask keys at or past kv_end,
+    // and zero their V entries (unwritten or sentinel data must not reach
+    // P*V, where 0 * NaN would not vanish).  The test is wave-uniform.
+    if (key0 + kBlock > kv_end) {
+      const int nvalid = kv_end - key0 - 4 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r >= nvalid) s[r] = neg_inf();
+      const uint32_t keep0 = (nvalid > 0 ? 0xFFFFu : 0u) | (nvalid > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t keep1 = (nvalid > 2 ? 0xFFFFu : 0u) | (nvalid > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) vc[mb] = make_uint2(vc[mb].x & keep0, vc[mb].y & keep1);
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    // move the reference max only when this page exceeds it by more than 2^8
+    // (always on the first page, where m is -inf)
+    const bool grow = (mx - m) * scale_log2 > 8.f;
+    if (__any(grow)) {
+      // rare: rescale the running sums; the empty asm keeps the compiler from
+      // hoisting this out of the branch and running it on every page
+      asm volatile("" ::: "memory");
+      const float mn = grow ? mx : m;
+      const float alpha = fast_exp2((m - mn) * scale_log2);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+    }
+    const float msc = m * scale_log2;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], scale_log2, -msc));
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    const uint2 pb = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vc[mb]),
+                                                          __builtin_bit_cast(short4_t, pb),
+                                                          acc[mb], 0, 0, 0);
+  };
+
+  // pages in groups of kStages with no early exit: pages past the piece end
+  // are masked in full (p = 0; the running max and sums are unchanged) and
+  // their loads re-read the last page (an L2 hit), which keeps the loop free
+  // of branches around the loads
+#pragma unroll
+  for (int u = 0; u + 1 < kStages; ++u) load_page(min(u, npages - 1), kset[u], vset[u]);
+  for (int i0 = 0; i0 < npages; i0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      constexpr int kLast = kStages - 1;
+      load_page(min(i0 + u + kLast, npages - 1), kset[(u + kLast) % kStages],
+                vset[(u + kLast) % kStages]);
+      compute_page(i0 + u, kset[u], vset[u]);
+    }
+  }
+
+  // column sums over the 4 lane groups (each summed its own keys)
+  lsum += xor_lane(lsum, 16);
+  lsum += xor_lane(lsum, 32);
+  if (n >= G) return;
+  const int d0 = 4 * g4;  // this lane's O^T rows inside each 16-row block
+  if (slot < 0) {
+    const float inv = 1.f / lsum;
+    uint16_t* orow = out + ((int64_t)t * num_q_heads + hq) * D + d0;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      *reinterpret_cast<uint2*>(orow + 16 * mb) =
+          make_uint2(pack_bf16x2(acc[mb][0] * inv, acc[mb][1] * inv),
+                     pack_bf16x2(acc[mb][2] * inv, acc[mb][3] * inv));
+    if (lse && g4 == 0)
+      lse[(int64_t)t * num_q_heads + hq] = (m * scale_log2 + __log2f(lsum)) * kLn2;
+  } else {
+    const int64_t ph = (int64_t)slot * num_q_heads + hq;
+    float* arow = ws.acc + ph * D + d0;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      *reinterpret_cast<float4*>(arow + 16 * mb) =
+          make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+    if (g4 == 0) {
+      ws.m[ph] = m * scale_log2;
+      ws.l[ph] = lsum;
+    }
+  }
+}
+
+}  // namespace cpa

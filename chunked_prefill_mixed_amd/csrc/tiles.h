@@ -7,7 +7,7 @@ constexpr int kBlock = 16;          // tokens per KV page
 constexpr int kChunkRows = 128;     // (token, head) query rows per chunk workgroup: 4 waves x 32
 constexpr int kKvTile = 64;         // keys per LDS-staged K/V tile in the chunk kernel (4 pages)
 // Decode waves per launch round: one per SIMD of the 256 CUs.  The kernel's
-// registers would allow 2 waves per SIMD at head_dim 128 and 4 at 64, but
+// registers would allow 3 waves per SIMD at head_dim 128 and 5 at 64, but
 // longer pieces at one wave per SIMD read as fast or faster (less start-up
 // and fewer partial results per byte), and a whole number of workgroups per
 // CU keeps every CU's share of the bytes equal; the planner adds whole
@@ -19,6 +19,14 @@ inline int decode_waves_target(int head_dim) {
 constexpr int kDecodeMaxSplit = 64 * kBlock;  // a decode split spans at most 64 pages
 constexpr int kChunkWgTarget = 512;       // chunk workgroups resident at once (2 per CU): one round
 constexpr int kChunkMinSplit = 256;       // fewest prefix keys worth a separate chunk piece
+
+// Resident workgroups of the chunk kernel and of the mixed launch (2 per CU
+// at head_dim 128, 3 at 64, on 256 CUs).  A step runs its decode pieces and
+// chunk tiles as one launch only when the chunk tiles alone fill a round:
+// then decode workgroups either run beside them or fill the slots their last
+// round leaves idle.  With fewer chunk tiles the two run as separate
+// launches, which measured as fast or faster there.
+inline int mixed_slots(int head_dim) { return 256 * (head_dim > 64 ? 2 : 3); }
 
 // Query tokens one chunk workgroup covers when G query heads share a KV head.
 inline int chunk_tile_tokens(int group) { return kChunkRows / group; }

@@ -252,6 +252,42 @@ def test_two_streams_match_one_stream():
     assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
 
 
+def _mixed_case(case):
+    if case == "d64":
+        # head_dim 64, G = 2: 192 tiles x 8 KV heads = 1536 chunk workgroups
+        rng = np.random.default_rng(84)
+        ctx = rng.integers(100, 3000, size=40).tolist()
+        return workloads.random_workload(84, num_q_heads=16, num_kv_heads=8, head_dim=64,
+                                         decode_ctx=ctx, chunks=[(0, 12288)])
+    return workloads.make_workload(case, 0)
+
+
+@pytest.mark.parametrize("case", [3, 4, 5, "d64"])
+def test_one_launch_matches_separate_sections(case):
+    """When the chunk tiles fill a resident round (512 workgroups at head_dim
+    128, 768 at 64), a step runs its decode pieces and chunk tiles as one
+    launch: decode workgroups first when they fit one round (budget-8192,
+    long-context and the head_dim-64 steps), chunk tiles first otherwise
+    (heavy mixed).  The same plan run section by section, one launch each,
+    gives the same bits."""
+    import torch
+    w = _mixed_case(case)
+    a = DeviceStep(w, validate=False)
+    c = a.counts
+    slots = 256 * (2 if w.head_dim > 64 else 3)
+    assert c.num_decode_splits > 0 and c.num_chunk_tiles * w.num_kv_heads >= slots
+    a.run()
+    b = DeviceStep(w, validate=False)
+    b.append()
+    for sec in ("decode_splits", "chunk_tiles", "decode_merges", "chunk_merges"):
+        b._section_call(sec, None)
+    torch.cuda.synchronize()
+    for name in ("out", "lse"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y), name
+
+
 @pytest.mark.parametrize("C", [1, 7, 16, 64, 100, 256])
 def test_gpu_chunking_invariance(C):
     """One 256-token prompt prefilled in chunks of C, each chunk appended
