@@ -23,8 +23,8 @@ round-to-nearest-even):
 * Page contents: random values at positions below ``num_computed``; every other
   slot, and every unused page, holds the sentinel 0xFFFF (a bf16 NaN) so a
   stray write or an unmasked read shows up.
-* KV layout: K pages [num_blocks, Hkv, 16, D]; V pages [num_blocks, Hkv, D, 16]
-  (V transposed inside each page).
+* KV layout: K pages [num_blocks, Hkv, D/8, 16, 8] (a page's keys in 8-value
+  pieces); V pages [num_blocks, Hkv, D, 16] (V transposed inside each page).
 """
 
 from __future__ import annotations
