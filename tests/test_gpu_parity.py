@@ -373,3 +373,31 @@ def test_graph_replay_matches_eager():
         assert torch.equal(ds.out.view(torch.int16), ref_out.view(torch.int16)), rep
         assert torch.equal(ds.k_cache.view(torch.int16), ref_k.view(torch.int16)), rep
         assert torch.equal(ds.v_cache.view(torch.int16), ref_v.view(torch.int16)), rep
+
+
+def _random_case(seed):
+    """A small random mixed step: supported head shapes, decode contexts from
+    0 to 3000, chunks of 1 to 300 tokens at prefixes from 0 to 2000, and
+    random split settings."""
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8])) if G < 8 else int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    dec = rng.integers(0, 3001, size=int(rng.integers(0, 7))).tolist()
+    chunks = []
+    for _ in range(int(rng.integers(0 if dec else 1, 4))):
+        c = int(rng.integers(0, 2001))
+        chunks.append((c, c + int(rng.integers(1, 301))))
+    dsplit = int(rng.choice([0, 0, 16, 64, 256]))
+    csplit = int(rng.choice([0, 0, 64, 192]))
+    return G * Hkv, Hkv, D, dec, chunks, dsplit, csplit
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_mixed_steps(seed):
+    Hq, Hkv, D, dec, chunks, dsplit, csplit = _random_case(7000 + seed)
+    w = workloads.random_workload(7000 + seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  decode_ctx=dec, chunks=chunks)
+    check_step(w, decode_split_tokens=dsplit, chunk_split_tokens=csplit,
+               label=f"random{seed} Hq={Hq} Hkv={Hkv} D={D} dec={dec} chunks={chunks} "
+                     f"splits={dsplit}/{csplit}")
