@@ -4,9 +4,10 @@
 A step is one pass of the whole path over one packed batch: the host
 decode-first budget split and work plan (cpa_build_metadata), one H2D copy of
 the step metadata, the paged KV append (cpa_append_kv), then cpa_attention:
-the split-KV decode kernel, the MFMA prefill-chunk kernel and one log-sum-exp
-merge launch for the split pieces of both, all on one stream
-(``--two-streams`` runs the chunk kernel on a second stream).
+the split-KV decode kernel and the MFMA prefill-chunk kernel (one launch when
+the chunk tiles fill a resident round) and one log-sum-exp merge launch for
+the split pieces of both, all on one stream (``--two-streams`` runs the chunk
+kernel on a second stream).
 Inputs (q, new K/V, the paged KV pool) are resident in HBM before timing.
 
 Default workload (Page-1 defaults of the chunked-prefill essay): 32 decode
@@ -18,9 +19,11 @@ last-level cache from the previous step.
 
 Prints ONE JSON line on stdout.  Per-kernel durations come from HIP events
 recorded on the launch stream around each launch inside the timed region, on
-every eleventh timed step (``--kernel-event-stride``); the other steps carry no
-events at all (each marker costs a few microseconds of GPU time between two
-launches), and the step rate is the wall clock over all timed steps.
+every eleventh timed step (``--kernel-event-stride``), which runs each plan
+section as its own launch so each kernel has its own span; the other steps
+make the one cpa_attention call and carry no events at all (each marker costs
+a few microseconds of GPU time between two launches), and the step rate is
+the wall clock over all timed steps.
 """
 
 from __future__ import annotations
