@@ -7,6 +7,7 @@ row exactly once."""
 import math
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -456,3 +457,23 @@ def test_replay_figures_arithmetic():
     assert math.isclose(f["ttft_ms"], 0.5) and math.isclose(f["worst_gap_us"], 250.0)
     assert math.isclose(f["stall_us"], 170.0) and math.isclose(f["mean_step_us"], 500 / 3)
     assert math.isclose(f["ttft_vs_unchunked"], 1.25)
+
+
+def test_c_program_uses_the_abi(lib, tmp_path):
+    """tests/c_abi/abi_check.c, compiled as C11 with -Wall -Werror against
+    include/cpa.h and linked to libcpa.so, runs the host calls (page 1's
+    512-token budget with 32 users; the budget floor) and prints ok."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    libdir = os.path.dirname(cpa.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(root, "include"),
+                    os.path.join(here, "c_abi", "abi_check.c"), "-o", exe, "-L", libdir, "-lcpa",
+                    f"-Wl,-rpath,{libdir}"], check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "ok"
