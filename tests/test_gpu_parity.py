@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from chunked_prefill_mixed_amd import cpa, workloads
-from chunked_prefill_mixed_amd.step import DeviceStep
+from chunked_prefill_mixed_amd.step import DeviceStep, bf16_to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -286,6 +286,53 @@ def test_one_launch_matches_separate_sections(case):
         x, y = getattr(a, name), getattr(b, name)
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y), name
+
+
+# (Hq, Hkv, D, decode contexts, chunks): chunk tiles below a resident round
+# (decode and chunk as separate launches), at one (one launch), head_dim 64
+FAR_POOL = {
+    "separate": (32, 8, 128, [700, 1500, 33], [(300, 800)]),
+    "one_launch": (32, 8, 128, [900, 2100], [(1024, 3072)]),
+    "d64": (16, 4, 64, [517, 60], [(250, 700)]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FAR_POOL))
+def test_pages_past_4_gib_of_the_pool(case):
+    """Every page of the step sits past the first 2^31 elements (4 GiB) of
+    each cache, so every page address needs 64-bit arithmetic: the step's
+    pages are moved to block ids offset by that much in a pool whose lower
+    blocks hold the sentinel.  The moved pages match the oracle bit for bit,
+    the lower blocks keep the sentinel, and the outputs match the oracle."""
+    import torch
+    Hq, Hkv, D, dec, chunks = FAR_POOL[case]
+    w = workloads.random_workload(1200 + sorted(FAR_POOL).index(case), num_q_heads=Hq,
+                                  num_kv_heads=Hkv, head_dim=D, decode_ctx=dec, chunks=chunks)
+    ds = DeviceStep(w)
+    off = (1 << 31) // (Hkv * 16 * D) + 3  # first moved block starts past element 2^31
+    big = []
+    for small in (ds.k_cache, ds.v_cache):
+        t = torch.empty((off + small.shape[0],) + tuple(small.shape[1:]), dtype=small.dtype,
+                        device=small.device)
+        t[:off].view(torch.int16).fill_(-1)  # 0xFFFF sentinel
+        t[off:] = small
+        big.append(t)
+    del small
+    ds.k_cache, ds.v_cache = big
+    ds.block_table += off
+    ds.run()
+    torch.cuda.synchronize()
+    tokens = sample_tokens(ds.meta, np.random.default_rng(5))
+    kp, vp, out, lse = oracle_step(w, ds.meta, tokens)
+    for name, t, ref in (("K", big[0], kp), ("V", big[1], vp)):
+        low = t[:off].view(torch.int16)
+        assert int(low.min()) == -1 and int(low.max()) == -1, f"{name}: a lower block was written"
+        got = bf16_to_bits(t[off:])
+        assert np.array_equal(got, ref), f"{name} pool differs at {np.argwhere(got != ref)[:5]}"
+    got = ds.out_f64()[tokens]
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got - out[tokens])) <= OUT_TOL
+    assert np.max(np.abs(ds.lse_f64()[tokens] - lse[tokens])) <= LSE_TOL
 
 
 @pytest.mark.parametrize("C", [1, 7, 16, 64, 100, 256])
