@@ -288,6 +288,20 @@ def test_one_launch_matches_separate_sections(case):
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y), name
 
 
+@pytest.mark.parametrize("rows", [449, 511, 512, 700])
+def test_many_rows(rows):
+    """Steps of 449 to 700 rows (one chunk, the rest decode rows with short
+    contexts).  The append finds each token's row among fewer than 512 rows
+    from registers (449 and 511 use all eight 64-row groups) and from memory
+    at 512 rows and more; every row's K/V and outputs match the oracle."""
+    rng = np.random.default_rng(rows)
+    dec = rng.integers(0, 200, size=rows - 1).tolist()
+    w = workloads.random_workload(1300 + rows, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                  decode_ctx=dec, chunks=[(40, 140)])
+    ds, _ = check_step(w, label=f"rows{rows}")
+    assert ds.num_seqs == rows
+
+
 # (Hq, Hkv, D, decode contexts, chunks): chunk tiles below a resident round
 # (decode and chunk as separate launches), at one (one launch), head_dim 64
 FAR_POOL = {
