@@ -302,6 +302,18 @@ def test_many_rows(rows):
     assert ds.num_seqs == rows
 
 
+def test_128k_token_rows():
+    """A decode row with 131071 cached tokens and a 100-token chunk after a
+    100000-token prefix: 128 decode pieces and dozens of chunk prefix pieces
+    per row go through the merge; K/V and outputs match the oracle."""
+    w = workloads.random_workload(1400, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                  decode_ctx=[131071, 5], chunks=[(100000, 100100)])
+    ds, _ = check_step(w, label="128k")
+    c = ds.counts
+    assert c.num_decode_merges >= 1 and c.num_chunk_merges >= 1
+    assert c.num_decode_partials >= 128
+
+
 # (Hq, Hkv, D, decode contexts, chunks): chunk tiles below a resident round
 # (decode and chunk as separate launches), at one (one launch), head_dim 64
 FAR_POOL = {
