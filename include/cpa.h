@@ -224,8 +224,11 @@ int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_build_params
  *
  * d_* pointers are device int32 arrays: query_start_loc [num_seqs+1],
  * context_lens [num_seqs], block_table [num_seqs][bt_stride] (rows in output
- * row order).  Returns CPA_OK, CPA_ERR_UNSUPPORTED, CPA_ERR_INVALID (negative
- * sizes) or CPA_ERR_DEVICE.
+ * row order).  num_tokens = 0 returns CPA_OK without a launch.  Returns
+ * CPA_OK, CPA_ERR_UNSUPPORTED (head_dim, block size), CPA_ERR_INVALID
+ * (negative sizes, bt_stride <= 0, or a NULL pointer when num_tokens > 0) or
+ * CPA_ERR_DEVICE.  Device-side inputs are trusted: row starts, contexts and
+ * page ids must be those cpa_build_metadata accepted.
  */
 int cpa_append_kv(const void* k_new, const void* v_new, const int32_t* d_query_start_loc,
                   const int32_t* d_context_lens, const int32_t* d_block_table, int bt_stride,
