@@ -151,6 +151,7 @@ class Instance:
         meta.plan_capacity = max(1, words)
         meta.plan = pn[off["plan"]:].ctypes.data_as(i32p)
         self.build_host()  # fills the pinned buffer once
+        self.host_build_s, self.host_builds = 0.0, 0  # host time of the per-step builds
         assert self.meta.num_tokens == ds.num_tokens and self.meta.plan_words == words
         # device tensors of the step now live in the packed buffer
         d = self.dev
@@ -241,7 +242,10 @@ class Instance:
         launches), and the step is one cpa_attention call, or the replay of
         the captured graph with ``--graph``."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
+        t0 = time.perf_counter()
         self.build_host()
+        self.host_build_s += time.perf_counter() - t0
+        self.host_builds += 1
         main = self.torch.cuda.current_stream()
         if per_kernel:
             events[8].record(main)  # before the metadata copy
@@ -582,6 +586,10 @@ def main():
         # between its launches) and of its metadata upload before it
         "gpu_step_us": gpu_step / NS * 1e6,
         "metadata_upload_us": copy_us / NS,
+        # host wall time of cpa_build_metadata (budget split + work plan) per
+        # step, every step run; it overlaps the GPU work of the step before
+        "host_build_us": (sum(i.host_build_s for i in insts)
+                          / max(1, sum(i.host_builds for i in insts)) * 1e6),
         "measured_peaks": peaks,
         "device": {"name": torch.cuda.get_device_name(0),
                    "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
