@@ -23,7 +23,9 @@ every eleventh timed step (``--kernel-event-stride``), which runs each plan
 section as its own launch so each kernel has its own span; the other steps
 make the one cpa_attention call and carry no events at all (each marker costs
 a few microseconds of GPU time between two launches), and the step rate is
-the wall clock over all timed steps.
+the wall clock over all timed steps.  ``host_build_us`` is the host time of
+``cpa_build_metadata`` per step, which overlaps the GPU work of the step
+before.
 """
 
 from __future__ import annotations
