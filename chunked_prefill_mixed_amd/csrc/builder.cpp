@@ -51,11 +51,19 @@ int check_params(const cpa_build_params_t* p) {
 }
 
 // Per-request chunk size from the decode queue depth (tbr8.org deep dive 7.1).
+// The rule is a table: the first row whose bound exceeds the decode count
+// scales the base chunk by mul / div (at least one token, at most INT32_MAX).
+struct AdaptiveRow {
+  int64_t below;
+  int64_t mul, div;
+};
+constexpr AdaptiveRow kAdaptiveRows[] = {{1, 4, 1}, {10, 2, 1}, {50, 1, 1}, {INT64_MAX, 1, 2}};
+
 int adaptive_cap(int base_chunk, int num_decodes) {
-  if (num_decodes == 0) return base_chunk * 4;
-  if (num_decodes < 10) return base_chunk * 2;
-  if (num_decodes < 50) return base_chunk;
-  return std::max(1, base_chunk / 2);
+  for (const AdaptiveRow& r : kAdaptiveRows)
+    if (num_decodes < r.below)
+      return (int)std::min<int64_t>(INT32_MAX, std::max<int64_t>(1, base_chunk * r.mul / r.div));
+  return base_chunk;
 }
 
 // Pages per decode piece when the caller leaves the split size to the

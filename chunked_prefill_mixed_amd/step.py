@@ -24,6 +24,42 @@ def bf16_to_bits(t) -> np.ndarray:
     return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+# The library's cache layout (include/cpa.h) made from logical pages
+# [num_blocks, Hkv, 16, D] and back.  Pure data movement on the device.
+def k_pages_to_cache(t):
+    """[nb, Hkv, 16, D] -> K cache [nb, Hkv, D/8, 16, 8] (8-value pieces)."""
+    nb, h, b, d = t.shape
+    return t.reshape(nb, h, b, d // 8, 8).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def v_pages_to_cache(t):
+    """[nb, Hkv, 16, D] -> V cache [nb, Hkv, D, 16] (transposed in a page)."""
+    return t.permute(0, 1, 3, 2).contiguous()
+
+
+def k_cache_to_pages(t):
+    """K cache [nb, Hkv, D/8, 16, 8] -> [nb, Hkv, 16, D]."""
+    nb, h, p, b, e = t.shape
+    return t.permute(0, 1, 3, 2, 4).reshape(nb, h, b, p * e)
+
+
+def v_cache_to_pages(t):
+    """V cache [nb, Hkv, D, 16] -> [nb, Hkv, 16, D]."""
+    return t.permute(0, 1, 3, 2)
+
+
+def caches_from_pools(k_pool, v_pool, device):
+    """Device K and V caches in the library's layout from logical uint16 pools."""
+    return (k_pages_to_cache(_bits_to_bf16(k_pool, device)),
+            v_pages_to_cache(_bits_to_bf16(v_pool, device)))
+
+
+def pools_from_caches(k_cache, v_cache):
+    """Logical uint16 pools [nb, Hkv, 16, D] of device caches."""
+    return (bf16_to_bits(k_cache_to_pages(k_cache).contiguous()),
+            bf16_to_bits(v_cache_to_pages(v_cache).contiguous()))
+
+
 class DeviceStep:
     """One step of a workload, resident on the GPU."""
 
@@ -50,8 +86,7 @@ class DeviceStep:
         self.context_lens = i32(m["context_lens"])
         plan = m["plan"] if m["plan"].size else np.zeros(1, dtype=np.int32)
         self.plan = i32(plan)
-        self.k_cache = _bits_to_bf16(w.k_pool, device)
-        self.v_cache = _bits_to_bf16(w.v_pool, device)
+        self.k_cache, self.v_cache = caches_from_pools(w.k_pool, w.v_pool, device)
         self.q = _bits_to_bf16(w.q[:T], device)
         self.k_new = _bits_to_bf16(w.k_new[:T], device)
         self.v_new = _bits_to_bf16(w.v_new[:T], device)
@@ -130,7 +165,8 @@ class DeviceStep:
 
     # host copies for checking
     def pools_bits(self):
-        return bf16_to_bits(self.k_cache), bf16_to_bits(self.v_cache)
+        """Both caches as logical pools [nb, Hkv, 16, D] of bf16 bits."""
+        return pools_from_caches(self.k_cache, self.v_cache)
 
     def out_f64(self):
         import torch

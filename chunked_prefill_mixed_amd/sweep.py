@@ -48,6 +48,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import cpa, workloads
+from .step import caches_from_pools
 
 HQ, HKV, D = 32, 8, 128
 NUM_STREAMS = 32   # budget scenario
@@ -151,8 +152,7 @@ class _Gpu:
         dev = "cuda"
         bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
             torch.bfloat16)
-        self.k_cache0 = bits(w.k_pool)
-        self.v_cache0 = bits(w.v_pool)
+        self.k_cache0, self.v_cache0 = caches_from_pools(w.k_pool, w.v_pool, dev)
         self.k_cache = self.k_cache0.clone()
         self.v_cache = self.v_cache0.clone()
         self.q = bits(w.q)

@@ -23,8 +23,9 @@ round-to-nearest-even):
 * Page contents: random values at positions below ``num_computed``; every other
   slot, and every unused page, holds the sentinel 0xFFFF (a bf16 NaN) so a
   stray write or an unmasked read shows up.
-* KV layout: K pages [num_blocks, Hkv, D/8, 16, 8] (a page's keys in 8-value
-  pieces); V pages [num_blocks, Hkv, D, 16] (V transposed inside each page).
+* KV pools are logical: [num_blocks, Hkv, 16, D] for K and for V (one
+  D-vector per page slot).  The library's own cache layout is made from them
+  on the device (``step.py``).
 """
 
 from __future__ import annotations
@@ -59,8 +60,8 @@ class Workload:
     long_prefill_cap: int
     requests: list
     block_table: np.ndarray  # int32 [n_requests, max_blocks], queue order
-    k_pool: np.ndarray  # uint16 [NB, Hkv, D/8, 16, 8]
-    v_pool: np.ndarray  # uint16 [NB, Hkv, D, 16]
+    k_pool: np.ndarray  # uint16 [NB, Hkv, 16, D]
+    v_pool: np.ndarray  # uint16 [NB, Hkv, 16, D]
     q: np.ndarray  # uint16 [budget, Hq, D]
     k_new: np.ndarray  # uint16 [budget, Hkv, D]
     v_new: np.ndarray  # uint16 [budget, Hkv, D]
@@ -141,8 +142,8 @@ def build(name: str, seed: int, instance: int, *, num_q_heads: int, num_kv_heads
     k_new = normal_bf16(streams["k"], token_budget * Hkv * D).reshape(token_budget, Hkv, D)
     v_new = normal_bf16(streams["v"], token_budget * Hkv * D).reshape(token_budget, Hkv, D)
 
-    k_pool = np.full((nb, Hkv, D // 8, BLOCK_SIZE, 8), SENTINEL, dtype=np.uint16)
-    v_pool = np.full((nb, Hkv, D, BLOCK_SIZE), SENTINEL, dtype=np.uint16)
+    k_pool = np.full((nb, Hkv, BLOCK_SIZE, D), SENTINEL, dtype=np.uint16)
+    v_pool = np.full((nb, Hkv, BLOCK_SIZE, D), SENTINEL, dtype=np.uint16)
     # pages holding at least one cached position, with their count of valid slots
     filled_ids, valid = [], []
     for i, r in enumerate(requests):
@@ -156,12 +157,12 @@ def build(name: str, seed: int, instance: int, *, num_q_heads: int, num_kv_heads
         page_elems = Hkv * BLOCK_SIZE * D
         kv_seq, = streams["pool"].spawn(1)
         ks, vs = kv_seq.spawn(2)
-        kp = normal_bf16(ks, len(filled_ids) * page_elems).reshape(-1, Hkv, D // 8, BLOCK_SIZE, 8)
-        vp = normal_bf16(vs, len(filled_ids) * page_elems).reshape(-1, Hkv, D, BLOCK_SIZE)
+        kp = normal_bf16(ks, len(filled_ids) * page_elems).reshape(-1, Hkv, BLOCK_SIZE, D)
+        vp = normal_bf16(vs, len(filled_ids) * page_elems).reshape(-1, Hkv, BLOCK_SIZE, D)
         slot = np.arange(BLOCK_SIZE)
         empty = slot[None, :] >= valid[:, None]  # [pages, 16]
-        kp[np.broadcast_to(empty[:, None, None, :, None], kp.shape)] = SENTINEL
-        vp[np.broadcast_to(empty[:, None, None, :], vp.shape)] = SENTINEL
+        kp[np.broadcast_to(empty[:, None, :, None], kp.shape)] = SENTINEL
+        vp[np.broadcast_to(empty[:, None, :, None], vp.shape)] = SENTINEL
         k_pool[filled_ids] = kp
         v_pool[filled_ids] = vp
 
@@ -329,3 +330,72 @@ def random_workload(seed: int, *, num_q_heads: int, num_kv_heads: int, head_dim:
     return build(f"random/{seed}", seed, 0, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                  head_dim=head_dim, token_budget=token_budget, long_prefill_cap=long_prefill_cap,
                  requests=reqs, reach=reach, pool_blocks=pool_blocks, streams=st)
+
+
+# ---------------------------------------------------------------------------
+# Score staircases: inputs whose attention scores climb in steps along a row
+# ---------------------------------------------------------------------------
+
+# Rises of a row's score level, in log2 units of the scaled score, at
+# fractions of the row's key range: (fraction of the keys before the rise,
+# rise).  Most rises are several times the 8-unit margin past which an
+# online softmax has to move its running max; one is a fall.
+STAIR_RISES = ((0.07, 9.5), (0.21, 12.0), (0.38, -6.0), (0.46, 17.0), (0.63, 10.5),
+               (0.81, 21.0), (0.93, 9.0))
+# and inside a chunk, at fractions of its new tokens (its causal diagonal)
+STAIR_CHUNK_RISES = ((0.2, 11.0), (0.55, 14.0), (0.85, 9.25))
+
+
+def stair_levels(context: int, new: int, is_chunk: bool) -> np.ndarray:
+    """Score level (log2 units) of each key position [0, context + new) of a
+    row: the sum of the rises at or before it."""
+    L = context + new
+    lv = np.zeros(L)
+    for frac, up in STAIR_RISES:
+        lv[int(frac * L):] += up
+    if is_chunk:
+        for frac, up in STAIR_CHUNK_RISES:
+            lv[context + int(frac * new):] += up
+    return lv
+
+
+def staircase_workload(seed: int, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                       decode_ctx: list, chunks: list, noise: float = 0.25) -> Workload:
+    """A random workload whose keys are re-drawn so that scores climb in steps.
+
+    Per (request, KV head) a direction u ~ N(0,1)^D is drawn; every query of
+    the request's G heads that share the KV head is u + noise * N(0,1), and
+    key p of the request is a_p u + noise * N(0,1) with
+    a_p = level(p) / (scale * log2(e) * |u|^2), so its scaled score against
+    any of those queries is close to level(p) in log2 units (stair_levels).
+    Values stay N(0,1).  Decode rows get the row-wide rises, chunks also rises
+    inside their new tokens.
+    """
+    w = random_workload(seed, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, decode_ctx=decode_ctx, chunks=chunks)
+    Hkv, D = num_kv_heads, head_dim
+    G = num_q_heads // Hkv
+    log2e = 1.4426950408889634
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    qsl = 0
+    q = w.q.view(np.uint16)
+    for i, r in enumerate(w.requests):
+        c = r.num_computed
+        n = 1 if r.is_decode else r.target_len - r.num_computed
+        lv = stair_levels(c, n, not r.is_decode)
+        pos = np.arange(c + n)
+        blocks = w.block_table[i][pos // BLOCK_SIZE]
+        offs = pos % BLOCK_SIZE
+        for g in range(Hkv):
+            u = _to_bf16_bits(rng.standard_normal(D, dtype=np.float32))
+            uf = (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            a = lv / (w.scale * log2e * float(uf @ uf))
+            keys = a[:, None] * uf[None, :] + noise * rng.standard_normal((c + n, D))
+            kb = _to_bf16_bits(keys.astype(np.float32))
+            w.k_pool[blocks[:c], g, offs[:c], :] = kb[:c]
+            w.k_new[qsl:qsl + n, g, :] = kb[c:]
+            qs = uf[None, None, :] + noise * rng.standard_normal((n, G, D))
+            q[qsl:qsl + n, g * G:(g + 1) * G, :] = _to_bf16_bits(qs.astype(np.float32))
+        qsl += n
+    w.name = f"staircase/{seed}"
+    return w

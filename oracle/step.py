@@ -33,10 +33,10 @@ design notes):
 * Query head h reads KV head h // (Hq / Hkv).
 * A prefill that does not fit the remaining budget is truncated to it (P1 and
   P5), not deferred; several prefills may share a step, in FCFS order.
-* Cache layout (the library's own choice; the pages fix only 16-token
-  pages): a K page holds its 16 keys in 8-value pieces, piece-major,
-  [num_blocks, Hkv, D/8, 16, 8]; V pages are stored transposed inside each
-  page, [num_blocks, Hkv, D, 16].  Both are bf16 bit patterns (uint16 here).
+* Cache pages are logical: [num_blocks, Hkv, 16, D] for both K and V, one
+  contiguous D-vector per (page, KV head, slot).  The pages fix only 16-token
+  pages; how a library lays a page out in memory is its own choice, and the
+  tests convert the library's pool to this form before comparing.
 """
 
 from __future__ import annotations
@@ -68,17 +68,19 @@ class Request(NamedTuple):
 POLICIES = ("truncate", "defer", "quota")
 
 
+# P4 7.1's queue-depth rule as rows of (decode count below which the row
+# applies, multiplier, divisor); the first row whose bound exceeds the decode
+# count scales the base chunk, and the last row (no bound) halves it.
+ADAPTIVE_CHUNK_ROWS = ((1, 4, 1), (10, 2, 1), (50, 1, 1), (None, 1, 2))
+
+
 def adaptive_chunk(base_chunk: int, num_decodes: int) -> int:
-    """Per-request chunk size from the decode queue depth (P4 7.1): four times
-    the base chunk when no decode runs, twice under 10 decodes, the base under
-    50, half of it otherwise (at least one token)."""
-    if num_decodes == 0:
-        return base_chunk * 4
-    if num_decodes < 10:
-        return base_chunk * 2
-    if num_decodes < 50:
-        return base_chunk
-    return max(1, base_chunk // 2)
+    """Per-request chunk size from the decode queue depth (P4 7.1), read off
+    ADAPTIVE_CHUNK_ROWS; at least one token."""
+    for bound, mul, div in ADAPTIVE_CHUNK_ROWS:
+        if bound is None or num_decodes < bound:
+            return max(1, base_chunk * mul // div)
+    raise AssertionError("the last row has no bound")
 
 
 def schedule(requests: Sequence[Request], token_budget: int, long_prefill_cap: int = 0,
@@ -206,6 +208,17 @@ def advance(requests: Sequence[Request], sched: dict) -> list[Request]:
 # C2: paged KV append (bit copy)
 # --------------------------------------------------------------------------
 
+def _pages(block_table, s: int) -> np.ndarray:
+    """Page ids of packed row s: its own block-table row (P4 4.2: a request
+    owns a list of pages)."""
+    return np.asarray(block_table[s])
+
+
+def _context(context_lens, s: int) -> int:
+    """Tokens of packed row s already cached before this step (P4 3.3)."""
+    return int(context_lens[s])
+
+
 def append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
            query_start_loc: Sequence[int], context_lens: Sequence[int],
            block_table: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
@@ -218,12 +231,14 @@ def append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.
     K = k_pool.copy()
     V = v_pool.copy()
     for s in range(len(context_lens)):
+        pages = _pages(block_table, s)
+        c = _context(context_lens, s)
         for t in range(query_start_loc[s], query_start_loc[s + 1]):
-            p = context_lens[s] + (t - query_start_loc[s])
-            b = int(block_table[s][p // BLOCK_SIZE])
+            p = c + (t - query_start_loc[s])
+            b = int(pages[p // BLOCK_SIZE])
             o = p % BLOCK_SIZE
-            K[b, :, :, o, :] = k_new[t].reshape(K.shape[1], -1, 8)  # [Hkv, D/8, 8]
-            V[b, :, :, o] = v_new[t]
+            K[b, :, o, :] = k_new[t]
+            V[b, :, o, :] = v_new[t]
     return K, V
 
 
@@ -247,24 +262,14 @@ def _kv_head(h: int, group: int) -> int:
     return h // group
 
 
-def k_rows(k_pool, blocks, g, offs):
-    """K rows [len(blocks), D] (bits) of slots offs[i] of pages blocks[i],
-    KV head g: the 8-value pieces of one key are gathered across the page's
-    D/8 piece rows."""
-    blocks = np.asarray(blocks)
-    # the index arrays are split by a slice, so numpy puts their common
-    # dimension first: [n, D/8, 8]
-    pieces = k_pool[blocks, g, :, np.asarray(offs), :]
-    return pieces.reshape(len(blocks), -1)
-
-
-def _row_keys(k_pool, v_pool, block_table_row, g, length):
-    """K and V of keys [0, length) of one row and KV head, as [length, D] fp64."""
+def _row_keys(k_pool, v_pool, pages, g, length):
+    """K and V of keys [0, length) of one row and KV head, as [length, D] fp64:
+    key k sits in page pages[k // 16], slot k % 16."""
     pos = np.arange(length)
-    blocks = np.asarray(block_table_row)[pos // BLOCK_SIZE]
+    blocks = np.asarray(pages)[pos // BLOCK_SIZE]
     offs = pos % BLOCK_SIZE
-    Ks = bf16_bits_to_f64(k_rows(k_pool, blocks, g, offs))
-    Vs = bf16_bits_to_f64(v_pool[blocks, g, :, offs])
+    Ks = bf16_bits_to_f64(k_pool[blocks, g, offs, :])
+    Vs = bf16_bits_to_f64(v_pool[blocks, g, offs, :])
     return Ks, Vs
 
 
@@ -273,10 +278,7 @@ def softmax_weights(q, k_pool, block_table_row, context_len, q_row_start, j, h, 
     its visible keys [0, context_len + j]; returns a 1-D fp64 array."""
     Hq = q.shape[1]
     g = _kv_head(h, Hq // num_kv_heads)
-    length = context_len + j + 1
-    pos = np.arange(length)
-    blocks = np.asarray(block_table_row)[pos // BLOCK_SIZE]
-    Ks = bf16_bits_to_f64(k_rows(k_pool, blocks, g, pos % BLOCK_SIZE))
+    Ks, _ = _row_keys(k_pool, k_pool, block_table_row, g, context_len + j + 1)
     s = scale * (Ks @ bf16_bits_to_f64(q[q_row_start + j, h]))
     w = np.exp(s - s.max())
     return w / w.sum()
@@ -311,11 +313,12 @@ def attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         js = np.nonzero(want[t0:t1])[0]
         if js.size == 0:
             continue
-        c = int(context_lens[s])
+        c = _context(context_lens, s)
+        pages = _pages(block_table, s)
         length = c + (t1 - t0)
         pos = np.arange(length)
         for g in range(num_kv_heads):
-            Ks, Vs = _row_keys(k_pool, v_pool, block_table[s], g, length)
+            Ks, Vs = _row_keys(k_pool, v_pool, pages, g, length)
             heads = [h for h in range(Hq) if _kv_head(h, G) == g]
             for a in range(0, js.size, row_chunk):
                 jj = js[a:a + row_chunk]

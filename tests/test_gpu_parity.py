@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from chunked_prefill_mixed_amd import cpa, workloads
-from chunked_prefill_mixed_amd.step import DeviceStep, bf16_to_bits
+from chunked_prefill_mixed_amd.step import DeviceStep, pools_from_caches
 
 pytestmark = pytest.mark.gpu
 
@@ -179,7 +179,7 @@ def test_zero_query_gives_cumulative_mean():
     for j in (0, 1, 37, 69):
         t = ds.meta["query_start_loc"][s] + j
         keys = np.arange(c + j + 1)
-        V = oracle.bf16_bits_to_f64(vp[bt[s][keys // 16], 0, :, keys % 16])
+        V = oracle.bf16_bits_to_f64(vp[bt[s][keys // 16], 0, keys % 16, :])
         assert np.max(np.abs(out[t, 0] - V.mean(axis=0))) <= OUT_TOL
 
 
@@ -350,10 +350,10 @@ def test_pages_past_4_gib_of_the_pool(case):
     torch.cuda.synchronize()
     tokens = sample_tokens(ds.meta, np.random.default_rng(5))
     kp, vp, out, lse = oracle_step(w, ds.meta, tokens)
-    for name, t, ref in (("K", big[0], kp), ("V", big[1], vp)):
+    gk, gv = pools_from_caches(big[0][off:], big[1][off:])
+    for name, t, got, ref in (("K", big[0], gk, kp), ("V", big[1], gv, vp)):
         low = t[:off].view(torch.int16)
         assert int(low.min()) == -1 and int(low.max()) == -1, f"{name}: a lower block was written"
-        got = bf16_to_bits(t[off:])
         assert np.array_equal(got, ref), f"{name} pool differs at {np.argwhere(got != ref)[:5]}"
     got = ds.out_f64()[tokens]
     assert np.isfinite(got).all()
@@ -405,19 +405,88 @@ def test_workspace_too_small_is_rejected():
     assert e.value.status == cpa.CPA_ERR_CAPACITY
 
 
+def oracle_step_parallel(w, meta, workers=None):
+    """oracle_step over every packed token, run in threads over interleaved
+    64-token blocks (numpy's array kernels release the GIL, BLAS runs one
+    thread per worker); the results of the threads cover disjoint tokens."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    T = meta["num_tokens"]
+    bt = w.block_table[meta["order"]]
+    kp, vp = oracle.append(w.k_pool, w.v_pool, w.k_new[:T], w.v_new[:T], meta["query_start_loc"],
+                           meta["context_lens"], bt)
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    blocks = np.arange(T) // 64
+    parts = [np.nonzero(blocks % workers == k)[0] for k in range(workers)]
+
+    def run(tok):
+        return tok, oracle.attention(w.q[:T], kp, vp, meta["query_start_loc"],
+                                     meta["context_lens"], bt, w.num_kv_heads, w.scale,
+                                     tokens=tok)
+
+    out = np.full((T, w.num_q_heads, w.head_dim), np.nan)
+    lse = np.full((T, w.num_q_heads), np.nan)
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        for tok, (o, l) in ex.map(run, [p for p in parts if p.size]):
+            out[tok] = o[tok]
+            lse[tok] = l[tok]
+    return kp, vp, out, lse
+
+
 @pytest.mark.parametrize("config", [2, 3, 4, 5])
 def test_config_end_to_end(config):
-    """The measured configurations at full size: whole pool bit-exact, outputs
-    of every decode row and of sampled chunk tokens (first/last 16 of each
-    chunk and random ones) against the oracle."""
-    rng = np.random.default_rng(config)
+    """The measured configurations at full size, every instance: the whole pool
+    bit-exact, and the outputs and lse of every token of every row against
+    the oracle."""
+    import torch
     for inst in range(workloads.num_instances(config)):
         w = workloads.make_workload(config, inst)
-        meta = cpa.cpa_build_metadata(
-            w.requests, token_budget=w.token_budget, long_prefill_cap=w.long_prefill_cap,
-            num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim)
-        toks = sample_tokens(meta, rng)
-        check_step(w, tokens=toks, label=f"{w.name}")
+        ds = DeviceStep(w)
+        print(f"config {config} instance {inst}: {w.name}, {ds.num_tokens} tokens", flush=True)
+        ds.run()
+        torch.cuda.synchronize()
+        kp, vp, out, lse = oracle_step_parallel(w, ds.meta)
+        gk, gv = ds.pools_bits()
+        assert np.array_equal(gk, kp), f"{w.name}: K pool differs at {np.argwhere(gk != kp)[:5]}"
+        assert np.array_equal(gv, vp), f"{w.name}: V pool differs at {np.argwhere(gv != vp)[:5]}"
+        del gk, gv, kp, vp
+        got = ds.out_f64()
+        assert np.isfinite(got).all() and np.isfinite(out).all(), w.name
+        err = np.max(np.abs(got - out))
+        assert err <= OUT_TOL, f"{w.name}: max |err| {err}"
+        lerr = np.max(np.abs(ds.lse_f64() - lse))
+        assert lerr <= LSE_TOL, f"{w.name}: lse err {lerr}"
+        print(f"  max |out err| {err:.3e}, max |lse err| {lerr:.3e}", flush=True)
+        del ds
+
+
+# (Hq, Hkv, D, decode contexts, chunks, decode split tokens, chunk split tokens)
+STAIRCASES = [
+    (32, 8, 128, [3000, 777, 64, 15], [(1000, 1300), (0, 200)], 0, 0),
+    (32, 8, 128, [3000, 777], [(1000, 1300)], 64, 192),
+    (32, 8, 128, [2000], [(700, 1100)], 16, 64),
+    (8, 2, 64, [900, 300, 77], [(500, 700), (0, 160)], 0, 0),
+    (8, 2, 64, [900, 300], [(500, 700)], 32, 64),
+    (8, 8, 64, [1200], [(300, 420)], 256, 128),
+    (64, 8, 128, [500], [(900, 1000)], 0, 0),
+    (16, 16, 128, [1500], [(2000, 2100)], 48, 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(STAIRCASES)))
+def test_score_staircase_moves_the_running_max(case):
+    """Scores that climb in steps of 9 to 21 log2 units along each row, and
+    again inside each chunk, make the kernels move their running max mid-row
+    with a finite rescale factor: inside decode pieces and chunk pieces,
+    across 64-key tiles, across split pieces (the log-sum-exp merge), and on
+    the masked diagonal tiles; head_dim 64 and 128, G = 1 to 8.  Every token
+    and the whole pool against the oracle."""
+    Hq, Hkv, D, dec, chunks, dsplit, csplit = STAIRCASES[case]
+    w = workloads.staircase_workload(900 + case, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                     decode_ctx=dec, chunks=chunks)
+    check_step(w, decode_split_tokens=dsplit, chunk_split_tokens=csplit,
+               label=f"staircase{case} Hq={Hq} Hkv={Hkv} D={D} splits={dsplit}/{csplit}")
 
 
 @pytest.mark.parametrize("config", [2, 3])

@@ -35,22 +35,25 @@ def as_float(b):
 
 
 def page_dense(K, V, block_ids, num_blocks):
-    """Place dense per-position K/V [L, Hkv, D] (bits) into fresh pools."""
+    """Place dense per-position K/V [L, Hkv, D] (bits) into fresh logical
+    pools [num_blocks, Hkv, 16, D]: position p goes to page block_ids[p // 16],
+    slot p % 16."""
     L, Hkv, D = K.shape
-    kp = np.full((num_blocks, Hkv, D // 8, BS, 8), 0xFFFF, dtype=np.uint16)
-    vp = np.full((num_blocks, Hkv, D, BS), 0xFFFF, dtype=np.uint16)
+    kp = np.full((num_blocks, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+    vp = np.full((num_blocks, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
     for p in range(L):
         b = block_ids[p // BS]
         for g in range(Hkv):
             for d in range(D):
-                kp[b, g, d // 8, p % BS, d % 8] = K[p, g, d]
-            vp[b, g, :, p % BS] = V[p, g]
+                kp[b, g, p % BS, d] = K[p, g, d]
+                vp[b, g, p % BS, d] = V[p, g, d]
     return kp, vp
 
 
-def brute_force(q_bits, K_bits, V_bits, c, scale, Hkv):
+def brute_force(q_bits, K_bits, V_bits, c, scale, Hkv, with_lse=False):
     """Pure-Python loops over a dense layout: out[j][h][d] for a chunk of n
-    queries at context c, explicit [n, c+n] visibility matrix."""
+    queries at context c, explicit [n, c+n] visibility matrix (and lse[j][h]
+    = log of the sum of exp(score) when asked)."""
     n, Hq, D = q_bits.shape
     G = Hq // Hkv
     L = c + n
@@ -59,6 +62,7 @@ def brute_force(q_bits, K_bits, V_bits, c, scale, Hkv):
     Vf = np.array(as_float(V_bits)).reshape(L, Hkv, D)
     mask = [[k <= c + j for k in range(L)] for j in range(n)]
     out = np.zeros((n, Hq, D))
+    lse = np.zeros((n, Hq))
     for j in range(n):
         for h in range(Hq):
             g = h // G
@@ -72,9 +76,10 @@ def brute_force(q_bits, K_bits, V_bits, c, scale, Hkv):
             mx = max(v for _, v in sc)
             ws = [(k, math.exp(v - mx)) for k, v in sc]
             tot = sum(w for _, w in ws)
+            lse[j, h] = mx + math.log(tot)
             for d in range(D):
                 out[j, h, d] = sum(w * Vf[k, g, d] for k, w in ws) / tot
-    return out
+    return (out, lse) if with_lse else out
 
 
 def random_case(rng, Hq, Hkv, D, c, n, num_blocks=None):
@@ -157,8 +162,8 @@ def test_chunking_invariance(L):
     bt = ids[None, :].astype(np.int32)
     results = {}
     for C in (1, 3, 16, 64, 100, L):
-        kp = np.full((nb, Hkv, D // 8, BS, 8), 0xFFFF, dtype=np.uint16)
-        vp = np.full((nb, Hkv, D, BS), 0xFFFF, dtype=np.uint16)
+        kp = np.full((nb, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+        vp = np.full((nb, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
         outs = []
         for a in range(0, L, C):
             b = min(L, a + C)
@@ -252,6 +257,69 @@ def test_token_subset_matches_full():
     assert np.isnan(sub[1]).all()
 
 
+# rows of a packed batch: (context, tokens this step); decodes (one token) first
+PACKED_ROWS = [(0, 1), (17, 1), (33, 1), (13, 7), (0, 9), (31, 2)]
+
+
+def packed_case(seed=2024, Hq=4, Hkv=2, D=8):
+    """Dense per-row keys/values/queries of a packed batch, and a shared pool
+    in which every row owns its own randomly placed pages."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    all_pages = sum(math.ceil((c + n) / BS) for c, n in PACKED_ROWS)
+    nb = all_pages + 5
+    ids = rng.permutation(nb)
+    at = 0
+    width = max(math.ceil((c + n) / BS) for c, n in PACKED_ROWS)
+    bt = np.full((len(PACKED_ROWS), width), -1, dtype=np.int32)
+    for s, (c, n) in enumerate(PACKED_ROWS):
+        npg = math.ceil((c + n) / BS)
+        bt[s, :npg] = ids[at:at + npg]
+        at += npg
+        rows.append(dict(c=c, n=n, K=bits(rng.standard_normal((c + n, Hkv, D))),
+                         V=bits(rng.standard_normal((c + n, Hkv, D))),
+                         q=bits(rng.standard_normal((n, Hq, D)))))
+    return rows, bt, nb
+
+
+def test_packed_rows_match_per_row_brute_force():
+    """One packed batch of six rows -- three decode rows and three chunks with
+    distinct contexts, each with its own pages of one shared pool -- through
+    oracle.append and oracle.attention equals brute force on each row's own
+    dense keys, for outputs and lse (P2 section 4: rows of one 1-D batch told
+    apart by query_start_loc; P4 4.2: each request owns its page list)."""
+    Hq, Hkv, D = 4, 2, 8
+    scale = 0.35
+    rows, bt, nb = packed_case(Hq=Hq, Hkv=Hkv, D=D)
+    # prefixes placed by the test, row by row, into the shared pool
+    kp = np.full((nb, Hkv, BS, D), 0xFFFF, dtype=np.uint16)
+    vp = kp.copy()
+    want_k, want_v = kp.copy(), vp.copy()
+    for s, r in enumerate(rows):
+        for p in range(r["c"] + r["n"]):
+            b, o = bt[s, p // BS], p % BS
+            want_k[b, :, o, :] = r["K"][p]
+            want_v[b, :, o, :] = r["V"][p]
+            if p < r["c"]:
+                kp[b, :, o, :] = r["K"][p]
+                vp[b, :, o, :] = r["V"][p]
+    qsl = [0]
+    for r in rows:
+        qsl.append(qsl[-1] + r["n"])
+    ctx = [r["c"] for r in rows]
+    k_new = np.concatenate([r["K"][r["c"]:] for r in rows])
+    v_new = np.concatenate([r["V"][r["c"]:] for r in rows])
+    q = np.concatenate([r["q"] for r in rows])
+    kp2, vp2 = oracle.append(kp, vp, k_new, v_new, qsl, ctx, bt)
+    assert np.array_equal(kp2, want_k) and np.array_equal(vp2, want_v)
+    out, lse = oracle.attention(q, kp2, vp2, qsl, ctx, bt, Hkv, scale)
+    for s, r in enumerate(rows):
+        ref, ref_lse = brute_force(r["q"], r["K"], r["V"], r["c"], scale, Hkv, with_lse=True)
+        got = out[qsl[s]:qsl[s + 1]]
+        assert np.max(np.abs(got - ref)) < 1e-12, s
+        assert np.max(np.abs(lse[qsl[s]:qsl[s + 1]] - ref_lse)) < 1e-12, s
+
+
 # ---------------------------------------------------------------------------
 # C2 append pins
 # ---------------------------------------------------------------------------
@@ -265,8 +333,8 @@ def test_append_touches_exactly_the_new_slots_and_is_idempotent():
     bt = rng.permutation(nb)[: 4 * 4].reshape(4, 4).astype(np.int32)
     T = sum(nq)
     qsl = np.concatenate([[0], np.cumsum(nq)]).tolist()
-    kp0 = bits(rng.standard_normal((nb, Hkv, D // 8, BS, 8)))
-    vp0 = bits(rng.standard_normal((nb, Hkv, D, BS)))
+    kp0 = bits(rng.standard_normal((nb, Hkv, BS, D)))
+    vp0 = bits(rng.standard_normal((nb, Hkv, BS, D)))
     kn = bits(rng.standard_normal((T, Hkv, D)))
     vn = bits(rng.standard_normal((T, Hkv, D)))
     kp, vp = oracle.append(kp0, vp0, kn, vn, qsl, ctx, bt)
@@ -278,15 +346,15 @@ def test_append_touches_exactly_the_new_slots_and_is_idempotent():
             slots.add((int(bt[s, p // BS]), p % BS))
             t = qsl[s] + i
             b, o = int(bt[s, p // BS]), p % BS
-            # K element (g, d) of slot o: piece d // 8 of the page, offset d % 8
+            # element (g, d) of slot o of page b, at its flat offset
             for g in range(Hkv):
                 for d in range(D):
-                    flat = (((b * Hkv + g) * (D // 8) + d // 8) * BS + o) * 8 + d % 8
+                    flat = ((b * Hkv + g) * BS + o) * D + d
                     assert kp.ravel()[flat] == kn[t, g, d]
-                    assert vp.ravel()[((b * Hkv + g) * D + d) * BS + o] == vn[t, g, d]
+                    assert vp.ravel()[flat] == vn[t, g, d]
     assert len(slots) == T  # injective
-    kdiff = np.any(kp != kp0, axis=(1, 2, 4))  # [nb, slot]
-    vdiff = np.any(vp != vp0, axis=(1, 2))
+    kdiff = np.any(kp != kp0, axis=(1, 3))  # [nb, slot]
+    vdiff = np.any(vp != vp0, axis=(1, 3))
     changed = {(b, o) for b, o in zip(*np.nonzero(kdiff | vdiff))}
     assert changed <= slots
     kp2, vp2 = oracle.append(kp, vp, kn, vn, qsl, ctx, bt)
@@ -549,6 +617,7 @@ def _pins_pass():
             test_brute_force_dense(*args)
         test_closed_form_zero_query_cumulative_mean(5)
         test_decode_row_equals_last_prefill_row()
+        test_packed_rows_match_per_row_brute_force()
     except AssertionError:
         return False
     return True
@@ -558,8 +627,12 @@ def test_pins_pass_unmutated():
     assert _pins_pass()
 
 
-@pytest.mark.parametrize("mutation", ["mask_off_by_one", "mask_strict", "head_map_modulo",
-                                      "v_read_as_k_layout", "k_read_token_major", "drop_scale"])
+MUTATIONS = ["mask_off_by_one", "mask_strict", "head_map_modulo", "v_rows_reversed",
+             "slot_reversed", "drop_scale", "rows_share_first_table", "rows_share_first_context",
+             "append_drops_context"]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS)
 def test_planted_mistake_is_caught(monkeypatch, mutation):
     if mutation == "mask_off_by_one":
         monkeypatch.setattr(ostep, "_visible", lambda pos, c, js: pos[None, :] <= (c + js + 1)[:, None])
@@ -568,17 +641,22 @@ def test_planted_mistake_is_caught(monkeypatch, mutation):
                             lambda pos, c, js: (pos[None, :] < (c + js)[:, None]) | (pos[None, :] == 0))
     elif mutation == "head_map_modulo":
         monkeypatch.setattr(ostep, "_kv_head", lambda h, G: h % 2 if G > 1 else h)
-    elif mutation == "v_read_as_k_layout":
+    elif mutation == "v_rows_reversed":
         orig = ostep._row_keys
 
-        def bad(k_pool, v_pool, bt_row, g, length):
-            Ks, Vs = orig(k_pool, v_pool, bt_row, g, length)
+        def bad(k_pool, v_pool, pages, g, length):
+            Ks, Vs = orig(k_pool, v_pool, pages, g, length)
             return Ks, Vs[::-1].copy()
         monkeypatch.setattr(ostep, "_row_keys", bad)
-    elif mutation == "k_read_token_major":
-        # the page's bits taken as [16][D] rows instead of [D/8][16][8] pieces
-        monkeypatch.setattr(ostep, "k_rows", lambda kp, blocks, g, offs: kp[np.asarray(blocks), g].reshape(
-            len(blocks), BS, -1)[np.arange(len(blocks)), np.asarray(offs)])
+    elif mutation == "slot_reversed":
+        # key p read from slot 15 - p % 16 of its page instead of slot p % 16
+        def bad(k_pool, v_pool, pages, g, length):
+            pos = np.arange(length)
+            blocks = np.asarray(pages)[pos // BS]
+            offs = BS - 1 - pos % BS
+            return (ostep.bf16_bits_to_f64(k_pool[blocks, g, offs, :]),
+                    ostep.bf16_bits_to_f64(v_pool[blocks, g, offs, :]))
+        monkeypatch.setattr(ostep, "_row_keys", bad)
     elif mutation == "drop_scale":
         orig_att = ostep.attention
 
@@ -587,4 +665,22 @@ def test_planted_mistake_is_caught(monkeypatch, mutation):
             a[7] = 1.0
             return orig_att(*a, **k)
         monkeypatch.setattr(oracle, "attention", no_scale)
+    elif mutation == "rows_share_first_table":
+        # every packed row reads (and writes) the pages of row 0
+        monkeypatch.setattr(ostep, "_pages", lambda block_table, s: np.asarray(block_table[0]))
+    elif mutation == "rows_share_first_context":
+        monkeypatch.setattr(ostep, "_context", lambda context_lens, s: int(context_lens[0]))
+    elif mutation == "append_drops_context":
+        # the append writes token t of a row at position t - qsl[s], as if the
+        # row had no cached prefix; attention still reads the true context
+        orig_ctx = ostep._context
+        orig_append = ostep.append
+
+        def append_no_ctx(*a, **k):
+            monkeypatch.setattr(ostep, "_context", lambda context_lens, s: 0)
+            try:
+                return orig_append(*a, **k)
+            finally:
+                monkeypatch.setattr(ostep, "_context", orig_ctx)
+        monkeypatch.setattr(oracle, "append", append_no_ctx)
     assert not _pins_pass()
