@@ -6,33 +6,33 @@ decode-first budget split and work plan (cpa_build_metadata), one H2D copy of
 the step metadata, the paged KV append (cpa_append_kv), then cpa_attention:
 the split-KV decode kernel and the MFMA prefill-chunk kernel (one launch when
 the chunk tiles fill a resident round) and one log-sum-exp merge launch for
-the split pieces of both, all on one stream (``--two-streams`` runs the chunk
-kernel on a second stream).
-Inputs (q, new K/V, the paged KV pool) are resident in HBM before timing.
+the split pieces of both, all on one stream.  Inputs (q, new K/V, the paged
+KV pool) are resident in HBM before timing.
 
-Default workload (Page-1 defaults of the chunked-prefill essay): 32 decode
-rows with contexts uniform in [512, 4096] plus one 480-token chunk (budget
-512) of an 8192-token prompt at prefix 0, 3840 and 7680; Hq=32, Hkv=8,
-D=128, bf16, 16-token pages.  The three prefix instances have their own KV
-pools and are rotated step by step, so no step finds its K/V in the 256 MB
-last-level cache from the previous step.
+Default workload, the largest of the configurations (heavy mixed step): 256
+decode rows (contexts lognormal, median 1024, sigma 0.75, capped at 16384)
+plus prefill chunks of 2048, 2048 and 3840 tokens at random prefixes in
+[0, 16384], budget 8192, a 2 GiB KV pool; Hq=32, Hkv=8, D=128, bf16,
+16-token pages.  Two instances of the recipe (two seeds), each with its own
+pool, are rotated step by step, so no step finds its K/V in the 256 MB
+last-level cache from the step before.  ``--config N`` picks another
+configuration; the other configurations are also run briefly after the
+headline and reported under ``other_configs``.
 
 Prints ONE JSON line on stdout.  Per-kernel durations come from HIP events
 recorded on the launch stream around each launch inside the timed region, on
-every eleventh timed step (``--kernel-event-stride``), which runs each plan
-section as its own launch so each kernel has its own span; the other steps
-make the one cpa_attention call and carry no events at all (each marker costs
-a few microseconds of GPU time between two launches), and the step rate is
-the wall clock over all timed steps.  ``host_build_us`` is the host time of
-``cpa_build_metadata`` per step, which overlaps the GPU work of the step
-before.
+whole rounds of instances (the first step of every instance, every
+``--kernel-event-stride``-th round), which run each plan section as its own
+launch (append, decode, chunk, decode merge, chunk merge) so each kernel has
+its own span; the other steps make the one cpa_attention call and carry no
+events (a marker costs a few microseconds of GPU time between two launches).
+The step rate is the wall clock over all timed steps.
 """
 
 from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -61,24 +61,12 @@ WORKLOAD_TEXT = {
        "2 GiB KV pool; Hq=32 Hkv=8 D=128",
 }
 
-KERNEL_SOURCES = {
-    "decode_kernel": ["decode.hip", "decode_body.h", "device.h", "tiles.h"],
-    "chunk_kernel": ["chunk.hip", "chunk_body.h", "device.h", "tiles.h"],
-    "append_kernel": ["append.hip", "device.h", "tiles.h"],
-    "merge_kernel": ["merge.hip", "device.h", "tiles.h"],
-}
+# kernels timed on their own in the sampled steps, in launch order
+SPANS = ("append_kernel", "decode_kernel", "chunk_kernel", "decode_merge", "chunk_merge")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash(kernel: str) -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "chunked_prefill_mixed_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -111,9 +99,10 @@ def step_work(meta, Hq, Hkv, D):
 # ---------------------------------------------------------------------------
 
 class Instance:
-    def __init__(self, w, torch, cpa, DeviceStep, aux_stream=None):
+    def __init__(self, w, torch, cpa, DeviceStep):
+        import numpy as np
         self.w = w
-        self.aux_stream = aux_stream
+        self.torch = torch
         self.ds = ds = DeviceStep(w, validate=True, with_lse=False)
         lib = self.lib = cpa.load()
         m = ds.meta
@@ -137,7 +126,6 @@ class Instance:
         self.params = cpa.cpa_build_params_t(w.token_budget, w.long_prefill_cap, 16, w.num_q_heads,
                                              w.num_kv_heads, w.head_dim, 0, 0,
                                              cpa.CPA_POLICY_TRUNCATE, 0)
-        import numpy as np
         self.scratch = {k: np.zeros(max(1, self.nreq), dtype=np.int32)
                         for k in ("order", "nsch", "newb")}
         meta = self.meta = cpa.cpa_meta_t()
@@ -165,8 +153,9 @@ class Instance:
         torch.cuda.synchronize()
         self.copy_done = torch.cuda.Event()
         self.copy_done.record()
-        self._prepare_calls(torch, cpa)
+        self._prepare_calls(cpa)
         self.work = step_work(m, w.num_q_heads, w.num_kv_heads, w.head_dim)
+        self.graph = None
 
     def build_host(self):
         st = self.lib.cpa_build_metadata(self.reqs, self.nreq, ctypes.byref(self.params), None, 0,
@@ -174,45 +163,35 @@ class Instance:
         if st != 0:
             raise RuntimeError(f"cpa_build_metadata failed: {st}")
 
-    def _prepare_calls(self, torch, cpa):
-        ds, w = self.ds, self.w
+    def _prepare_calls(self, cpa):
+        ds, w, torch = self.ds, self.w, self.torch
         vp = ctypes.c_void_p
         P = lambda t: vp(t.data_ptr()) if t is not None else None
         self.stream = vp(torch.cuda.current_stream().cuda_stream)
         c = ds.counts
         plan_base = ds.plan.data_ptr()
         off = cpa.section_offsets(c)
-        self.parts = []
-        common_tail = (ds.num_seqs, ds.num_decodes, ds.num_tokens, w.num_q_heads, w.num_kv_heads,
-                       w.head_dim, 16, ctypes.c_float(w.scale), P(ds.out), None,
-                       P(ds.workspace), ctypes.c_size_t(0 if ds.workspace is None
-                                                        else ds.workspace.numel()),
-                       self.stream)
+        tail = (ds.num_seqs, ds.num_decodes, ds.num_tokens, w.num_q_heads, w.num_kv_heads,
+                w.head_dim, 16, ctypes.c_float(w.scale), P(ds.out), None, P(ds.workspace),
+                ctypes.c_size_t(0 if ds.workspace is None else ds.workspace.numel()), self.stream)
         head = (P(ds.q), P(ds.k_cache), P(ds.v_cache), P(ds.block_table),
                 int(ds.block_table.shape[1]), P(ds.query_start_loc), P(ds.seq_lens),
                 P(ds.context_lens))
         zero = dict(num_decode_splits=0, num_decode_merges=0, num_chunk_tiles=0,
                     num_chunk_merges=0)
-        # one launch per call, in the library's own order, so HIP events can
-        # bracket each kernel (both merge sections are one launch)
-        sections = [
-            ("decode_kernel", ("num_decode_splits",), "decode_splits"),
-            ("chunk_kernel", ("num_chunk_tiles",), "chunk_tiles"),
-            ("merge_kernel", ("num_decode_merges", "num_chunk_merges"), "decode_merges"),
-        ]
-        for name, fields, sec in sections:
-            counts = c.copy(**{**zero, **{f: getattr(c, f) for f in fields}})
-            self.parts.append((name, counts, head + (vp(plan_base + 4 * off[sec]),
-                                                     ctypes.byref(counts)) + common_tail))
+        # one plan section per call, so HIP events can bracket each launch
+        self.section_args = {}
+        self._keep = []
+        for name, field, sec in (("decode_kernel", "num_decode_splits", "decode_splits"),
+                                 ("chunk_kernel", "num_chunk_tiles", "chunk_tiles"),
+                                 ("decode_merge", "num_decode_merges", "decode_merges"),
+                                 ("chunk_merge", "num_chunk_merges", "chunk_merges")):
+            counts = c.copy(**{**zero, field: getattr(c, field)})
+            self._keep.append(counts)
+            self.section_args[name] = head + (vp(plan_base + 4 * off[sec]),
+                                              ctypes.byref(counts)) + tail
         # the whole plan in one call, as a caller runs a step
-        self.full_args = head + (vp(plan_base), ctypes.byref(c)) + common_tail
-        self.torch = torch
-        self.graph = None
-        self.aux_parts = {}
-        if self.aux_stream is not None:
-            aux_tail = common_tail[:-1] + (vp(self.aux_stream.cuda_stream),)
-            for name, counts, args in self.parts:
-                self.aux_parts[name] = args[:len(head) + 2] + aux_tail
+        self.full_args = head + (vp(plan_base), ctypes.byref(c)) + tail
         self.append_args = (P(ds.k_new), P(ds.v_new), P(ds.query_start_loc), P(ds.context_lens),
                             P(ds.block_table), int(ds.block_table.shape[1]), ds.num_seqs,
                             ds.num_tokens, w.num_kv_heads, w.head_dim, 16, P(ds.k_cache),
@@ -235,82 +214,155 @@ class Instance:
             raise RuntimeError(f"launch failed during capture with status {st}")
         self.graph = g
 
-    def step(self, events, aux=None, per_kernel=True):
-        """One full step.  events: 9 torch events.  With ``aux`` (a second
-        stream) the chunk kernel runs on it, concurrently with the decode
-        kernel on the main stream; both wait for the append, and the merge
-        follows both on the main stream.  Without ``per_kernel`` only the
-        step's first and last events are recorded (no markers between the
-        launches), and the step is one cpa_attention call, or the replay of
-        the captured graph with ``--graph``."""
+    def step(self, events=None):
+        """One full step.  With ``events`` (len(SPANS) + 2 HIP events) every
+        launch runs on its own between two of them: events[0] before the
+        metadata copy, events[1 + i] before span i, events[-1] after the
+        last; without, the step is one cpa_attention call (or the replay of
+        the captured graph) and carries no events."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         t0 = time.perf_counter()
         self.build_host()
         self.host_build_s += time.perf_counter() - t0
         self.host_builds += 1
         main = self.torch.cuda.current_stream()
-        if per_kernel:
-            events[8].record(main)  # before the metadata copy
-        self.dev.copy_(self.pinned, non_blocking=True)
-        self.copy_done.record()
         lib = self.lib
-        parts = dict((name, args) for name, _, args in self.parts)
-        st = 0
-        if per_kernel:
-            events[0].record(main)
-        if self.graph is None or per_kernel or aux is not None:
-            st |= lib.cpa_append_kv(*self.append_args)
-        if aux is None and not per_kernel:
+        if events is None:
+            self.dev.copy_(self.pinned, non_blocking=True)
+            self.copy_done.record()
             if self.graph is not None:
                 self.graph.replay()
-            else:
-                st |= lib.cpa_attention(*self.full_args)
+                return
+            st = lib.cpa_append_kv(*self.append_args)
+            st |= lib.cpa_attention(*self.full_args)
             if st != 0:
                 raise RuntimeError(f"launch failed with status {st}")
             return
-        events[1].record(main)
-        if aux is None:
-            st |= lib.cpa_attention(*parts["decode_kernel"])
-            events[2].record(main)
-            events[5].record(main)
-            st |= lib.cpa_attention(*parts["chunk_kernel"])
-            events[6].record(main)
-            events[3].record(main)
-            st |= lib.cpa_attention(*parts["merge_kernel"])
-            events[4].record(main)
-            events[7].record(main)
-        else:
-            aux.wait_event(events[1])
-            events[5].record(aux)
-            st |= lib.cpa_attention(*self.aux_parts["chunk_kernel"])
-            events[6].record(aux)
-            st |= lib.cpa_attention(*parts["decode_kernel"])
-            events[2].record(main)
-            main.wait_event(events[6])
-            events[3].record(main)
-            st |= lib.cpa_attention(*parts["merge_kernel"])
-            events[4].record(main)
-            events[7].record(main)
+        events[0].record(main)
+        self.dev.copy_(self.pinned, non_blocking=True)
+        self.copy_done.record()
+        st = 0
+        for i, name in enumerate(SPANS):
+            events[1 + i].record(main)
+            if name == "append_kernel":
+                st |= lib.cpa_append_kv(*self.append_args)
+            else:
+                st |= lib.cpa_attention(*self.section_args[name])
+        events[-1].record(main)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
-
-
-def traffic_for(kernel: str, config: int):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    counter runs, if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{config_key(config)}_counters.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_hash(kernel):
-        return None
-    return rec.get("traffic_bytes_per_launch")
 
 
 def config_key(config: int) -> str:
     from chunked_prefill_mixed_amd import workloads
     return workloads.CONFIG_NAMES[config]
+
+
+def traffic_for(kernel: str, config: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counter record, if it was taken on the current library sources."""
+    from chunked_prefill_mixed_amd import counters
+    rec = counters.traffic_record(kernel, config_key(config), os.path.join(ROOT, "profiles"))
+    return None if rec is None else rec["traffic_bytes_per_launch"]
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = (len(xs) - 1) * q
+    lo, hi = math.floor(k), math.ceil(k)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, DeviceStep):
+    """Warm up, then time ``steps`` steps of the configuration's instances,
+    rotated; returns the measurements (see main)."""
+    t_setup = time.perf_counter()
+    ws = [workloads.make_workload(config, i) for i in range(workloads.num_instances(config))]
+    insts = [Instance(w, torch, cpa, DeviceStep) for w in ws]
+    log(f"config {config} setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
+        f"{[i.ds.num_tokens for i in insts]} tokens/step")
+    I = len(insts)
+    NEV = len(SPANS) + 2
+    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
+    for s in range(warmup):
+        insts[s % I].step(ev_w)
+    torch.cuda.synchronize()
+    if graph:
+        for inst in insts:
+            inst.capture()
+        for inst in insts:  # one replay each before timing
+            inst.step()
+        torch.cuda.synchronize()
+    # the first step of every instance in every stride-th round carries events
+    order = [(warmup + s) % I for s in range(steps)]
+    sampled = [s for s in range(steps) if (s // I) % max(1, stride) == 0]
+    events = {s: [torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for s in sampled}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        insts[order[s]].step(events.get(s))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    tokens = sum(insts[order[s]].work["tokens"] for s in range(steps))
+    durs = {n: [] for n in SPANS}
+    work = {n: [] for n in SPANS}
+    wkey = {"append_kernel": "append_bytes", "decode_kernel": "decode_bytes",
+            "chunk_kernel": "chunk_flops", "decode_merge": None, "chunk_merge": None}
+    gpu_step, copy_us = [], []
+    for s in sampled:
+        ev = events[s]
+        copy_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        gpu_step.append(ev[1].elapsed_time(ev[-1]) * 1e3)
+        for i, n in enumerate(SPANS):
+            durs[n].append(ev[1 + i].elapsed_time(ev[2 + i]) * 1e3)  # us
+            work[n].append(insts[order[s]].work[wkey[n]] if wkey[n] else 0)
+
+    def stats(n):
+        d = durs[n]
+        return {"avg_us": sum(d) / len(d), "p10_us": percentile(d, 0.1),
+                "p50_us": percentile(d, 0.5), "p90_us": percentile(d, 0.9)}
+
+    kernels = {n: stats(n) for n in SPANS}
+    for n, unit, scale, peak in (("append_kernel", "GB/s", 1e9, HBM_PEAK_GBS),
+                                 ("decode_kernel", "GB/s", 1e9, HBM_PEAK_GBS),
+                                 ("chunk_kernel", "TFLOP/s", 1e12, MFMA_BF16_PEAK_TFS)):
+        t = sum(durs[n]) * 1e-6
+        v = sum(work[n]) / t / scale if t > 0 else None
+        kernels[n][unit] = v
+        kernels[n]["frac_of_peak"] = None if v is None else v / peak
+        # the same rate at the median launch of each instance's launches
+        kernels[n][unit + "_at_p50"] = (
+            None if not durs[n] else
+            percentile([w / d for w, d in zip(work[n], durs[n]) if d > 0], 0.5) * 1e6 / scale)
+    # decode with its own merge counted (the pieces of a split row are not
+    # attention output until merged)
+    t_dm = (sum(durs["decode_kernel"]) + sum(durs["decode_merge"])) * 1e-6
+    kernels["decode_kernel"]["frac_of_peak_with_decode_merge"] = (
+        sum(work["decode_kernel"]) / t_dm / 1e9 / HBM_PEAK_GBS if t_dm > 0 else None)
+    host_us = (sum(i.host_build_s for i in insts) / max(1, sum(i.host_builds for i in insts))
+               * 1e6)
+    res = {
+        "value": tokens / elapsed,
+        "ms_per_step": elapsed / steps * 1e3,
+        "tokens_per_step": sorted({i.ds.num_tokens for i in insts}),
+        "instances": [i.w.name for i in insts],
+        "kernels": kernels,
+        "gpu_step_us": sum(gpu_step) / len(gpu_step),
+        "metadata_upload_us": sum(copy_us) / len(copy_us),
+        "host_build_us": host_us,
+        "kernel_events": {"round_stride": stride, "sampled_steps": len(sampled),
+                          "per_instance": [sum(1 for s in sampled if order[s] == k)
+                                           for k in range(I)]},
+        "work_per_step": {k: [i.work[k] for i in insts]
+                          for k in ("decode_bytes", "chunk_flops", "append_bytes")},
+    }
+    res["workloads"] = ws
+    del insts
+    torch.cuda.empty_cache()
+    return res
 
 
 def measured_peaks(torch, build_lib):
@@ -372,8 +424,13 @@ def measured_peaks(torch, build_lib):
 
 
 def cpu_baseline(workloads_list, seconds: float):
-    """The fp64 oracle (as it stands) on the host cores, whole steps of the
-    same instances, round-robin until ``seconds`` of CPU work have run."""
+    """The fp64 oracle (as it stands) on the host cores, on a bounded sample of
+    the same instances, round-robin until ``seconds`` of CPU work have run.
+    Each sampled step runs the oracle's append of the whole step and its
+    attention for every k-th packed token, k chosen so one step's sample is a
+    few seconds of work; the attention time is scaled by the tokens left out,
+    so the rate is whole steps per second of the oracle, extrapolated from the
+    sample."""
     import numpy as np
 
     import oracle
@@ -385,9 +442,10 @@ def cpu_baseline(workloads_list, seconds: float):
         blas_name = ",".join(sorted({f"{i.get('internal_api')}" for i in blas}))
     except Exception:  # pragma: no cover
         cores, blas_name = len(os.sched_getaffinity(0)), "unknown"
-    done_tokens, done_steps, t_total = 0, 0, 0.0
+    t_app = t_att = spent = 0.0
+    n_tok = n_sel = steps = 0
     k = 0
-    while t_total < seconds or done_steps == 0:
+    while spent < seconds or steps == 0:
         w = workloads_list[k % len(workloads_list)]
         m = cpa.cpa_build_metadata(w.requests, token_budget=w.token_budget,
                                    long_prefill_cap=w.long_prefill_cap,
@@ -395,44 +453,52 @@ def cpu_baseline(workloads_list, seconds: float):
                                    head_dim=w.head_dim)
         bt = w.block_table[m["order"]]
         T = m["num_tokens"]
+        flops = step_work(m, w.num_q_heads, w.num_kv_heads, w.head_dim)["chunk_flops"]
+        stride = max(1, int(math.ceil(flops / 30e9 / 3.0)))  # ~3 s at ~30 GFLOP/s fp64
+        sel = np.arange(0, T, stride)
         t0 = time.perf_counter()
         kp, vp = oracle.append(w.k_pool, w.v_pool, w.k_new[:T], w.v_new[:T],
                                m["query_start_loc"], m["context_lens"], bt)
+        t1 = time.perf_counter()
         oracle.attention(w.q[:T], kp, vp, m["query_start_loc"], m["context_lens"], bt,
-                         w.num_kv_heads, w.scale)
-        t_total += time.perf_counter() - t0
-        done_tokens += T
-        done_steps += 1
+                         w.num_kv_heads, w.scale, tokens=sel)
+        t2 = time.perf_counter()
+        spent += t2 - t0
+        t_app += t1 - t0
+        t_att += (t2 - t1) * T / sel.size
+        n_tok += T
+        n_sel += sel.size
+        steps += 1
         k += 1
         del kp, vp
-    return {"value": done_tokens / t_total, "unit": "tokens/s", "cores": int(cores),
+    return {"value": n_tok / (t_app + t_att), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{done_steps} whole steps (append + attention of every token) of the same "
-                      f"instances, round-robin, {t_total:.1f} s of fp64 numpy ({blas_name} BLAS)"}
+            "sample": f"{steps} step(s) of the same instances, round-robin, {spent:.1f} s of CPU "
+                      f"work: the append of every "
+                      f"token and the attention of {n_sel} of the {n_tok} packed tokens (every "
+                      f"k-th token), the attention time scaled to all tokens; fp64 numpy "
+                      f"({blas_name} BLAS)"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=90)
-    ap.add_argument("--warmup", type=int, default=15)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--other-configs", default="2,3,4",
+                    help="configurations run briefly after the headline and reported under "
+                         "other_configs (comma list; empty for none)")
+    ap.add_argument("--other-steps", type=int, default=24)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--two-streams", action="store_true",
-                    help="run the chunk kernel on a second stream, concurrently with the "
-                         "decode kernel; the merge follows both (default: one stream, so each "
-                         "kernel's HIP-event time is its own)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each instance's append + attention as one captured HIP graph on "
                          "the unsampled steps (the host metadata build and its copy still run "
                          "every step, outside the graph)")
-    ap.add_argument("--kernel-event-stride", type=int, default=11,
-                    help="record the per-kernel HIP events on every n-th timed step only (the "
-                         "others carry just the step's start and end events, since a marker "
-                         "between launches keeps a kernel from starting while the previous one "
-                         "drains); per-kernel durations average the sampled steps.  Keep it "
-                         "coprime to the number of rotated instances so each is sampled")
+    ap.add_argument("--kernel-event-stride", type=int, default=3,
+                    help="record per-kernel HIP events on every n-th round of instances (each "
+                         "instance's step of that round); the other steps carry no event")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -462,96 +528,43 @@ def main():
         build_lib.build()
     cpa.load()
 
-    t_setup = time.perf_counter()
-    ws = [workloads.make_workload(args.config, i)
-          for i in range(workloads.num_instances(args.config))]
-    aux = torch.cuda.Stream() if args.two_streams else None  # default priority
-    insts = [Instance(w, torch, cpa, DeviceStep, aux) for w in ws]
-    log(f"setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
-        f"{[i.ds.num_tokens for i in insts]} tokens/step")
-
     K, W = args.steps, args.warmup
-    NEV = 9
-    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
-    for s in range(W):
-        insts[s % len(insts)].step(ev_w, aux)
-    torch.cuda.synchronize()
-    if args.graph and aux is None:
-        for inst in insts:
-            inst.capture()
-        for s in range(len(insts)):  # one replay each before timing
-            insts[s].step(ev_w, None, per_kernel=False)
-        torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(K)]
-    order = [(W + s) % len(insts) for s in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    stride = max(1, args.kernel_event_stride) if aux is None else 1
-    sampled = [s for s in range(K) if s % stride == 0]
-    for s in range(K):
-        insts[order[s]].step(events[s], aux, per_kernel=(s % stride == 0))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    # (kernel, start event, end event) on the stream the kernel ran on
-    spans = {"append_kernel": (0, 1), "decode_kernel": (1, 2), "chunk_kernel": (5, 6),
-             "merge_kernel": (3, 4)}
-    names = list(spans)
-    times = {n: 0.0 for n in names}
-    gpu_step = 0.0
-    work = {"decode_bytes": 0, "chunk_flops": 0, "append_bytes": 0, "tokens": 0}
-    tokens = 0
-    copy_us = 0.0
-    for s in range(K):
-        tokens += insts[order[s]].work["tokens"]
-    for s in sampled:
-        gpu_step += events[s][0].elapsed_time(events[s][7]) * 1e-3
-        copy_us += events[s][8].elapsed_time(events[s][0]) * 1e3
-    for s in sampled:  # per-kernel durations and work over the sampled steps
-        ev = events[s]
-        for n, (a, b) in spans.items():
-            times[n] += ev[a].elapsed_time(ev[b]) * 1e-3
-        wk = insts[order[s]].work
-        for key in work:
-            work[key] += wk[key]
-    NS = len(sampled)
-    value = tokens / elapsed
-
-    def rate(n, amount, scale):
-        return amount / times[n] / scale if times[n] > 0 else None
-
-    kernels = {
-        "append_kernel": {"avg_us": times["append_kernel"] / NS * 1e6,
-                          "GB/s": rate("append_kernel", work["append_bytes"], 1e9)},
-        "decode_kernel": {"avg_us": times["decode_kernel"] / NS * 1e6,
-                          "GB/s": rate("decode_kernel", work["decode_bytes"], 1e9)},
-        "merge_kernel": {"avg_us": times["merge_kernel"] / NS * 1e6},
-        "chunk_kernel": {"avg_us": times["chunk_kernel"] / NS * 1e6,
-                         "TFLOP/s": rate("chunk_kernel", work["chunk_flops"], 1e12)},
-    }
-    for n, peak, unit in (("append_kernel", HBM_PEAK_GBS, "GB/s"),
-                          ("decode_kernel", HBM_PEAK_GBS, "GB/s"),
-                          ("chunk_kernel", MFMA_BF16_PEAK_TFS, "TFLOP/s")):
-        v = kernels[n].get(unit)
-        kernels[n]["frac_of_peak"] = None if v is None else v / peak
-
-    # the decode rate with the whole merge launch (decode and chunk merges
-    # together) added to the decode kernel's time
-    t_dm = times["decode_kernel"] + times["merge_kernel"]
-    kernels["decode_kernel"]["frac_of_peak_with_merge_launch"] = (
-        work["decode_bytes"] / t_dm / 1e9 / HBM_PEAK_GBS if t_dm > 0 else None)
-
-    dominant = max(("decode_kernel", "chunk_kernel", "append_kernel"), key=lambda n: times[n])
+    head = run_config(args.config, K, W, args.kernel_event_stride, args.graph, torch, cpa,
+                      workloads, DeviceStep)
+    ws = head.pop("workloads")
+    kernels = head["kernels"]
+    # the dominant kernel of the step: the one with the largest time
+    dominant = max(("decode_kernel", "chunk_kernel", "append_kernel"),
+                   key=lambda n: kernels[n]["avg_us"])
     if dominant == "chunk_kernel":
-        ach = kernels["chunk_kernel"]["TFLOP/s"]
+        ach = kernels[dominant]["TFLOP/s"]
         roofline = {"bound": "mfma", "kernel": dominant, "achieved": ach,
-                    "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFS}
+                    "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
     else:
         ach = kernels[dominant]["GB/s"]
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
+                    "unit": "GB/s"}
+    roofline["frac"] = ach / roofline["peak"]
     roofline["traffic"] = traffic_for(dominant, args.config)
+    wk = {"chunk_kernel": "chunk_flops", "decode_kernel": "decode_bytes",
+          "append_kernel": "append_bytes"}[dominant]
+    roofline["algorithmic_per_launch"] = (sum(head["work_per_step"][wk])
+                                          / len(head["work_per_step"][wk]))
+    roofline["avg_launch_us"] = kernels[dominant]["avg_us"]
+
+    others = {}
+    for c in [int(x) for x in args.other_configs.split(",") if x.strip()]:
+        if c == args.config:
+            continue
+        r = run_config(c, args.other_steps, 4, args.kernel_event_stride, False, torch, cpa,
+                       workloads, DeviceStep)
+        r.pop("workloads")
+        others[config_key(c)] = {
+            "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+            "tokens_per_step": r["tokens_per_step"],
+            "kernels": {n: {k: v for k, v in d.items()} for n, d in r["kernels"].items()},
+        }
+
     peaks = measured_peaks(torch, build_lib)
     for n, key, unit in (("append_kernel", "hbm_copy_GB/s", "GB/s"),
                          ("decode_kernel", "hbm_read_GB/s", "GB/s"),
@@ -565,38 +578,33 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": elapsed / K * 1e3,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "config": config_key(args.config),
-                   "tokens_per_step": sorted({i.ds.num_tokens for i in insts}),
-                   "instances": len(insts)},
+                   "tokens_per_step": head["tokens_per_step"],
+                   "instances": head["instances"]},
         "roofline": roofline,
         "kernels": kernels,
-        "streams": ("decode and chunk on two streams, concurrently" if args.two_streams
-                    else "one stream"),
-        "graph": bool(args.graph and aux is None),
-        # GPU time of a sampled step (append through merge, with the markers
-        # between its launches) and of its metadata upload before it
-        "gpu_step_us": gpu_step / NS * 1e6,
-        "metadata_upload_us": copy_us / NS,
-        # host wall time of cpa_build_metadata (budget split + work plan) per
-        # step, every step run; it overlaps the GPU work of the step before
-        "host_build_us": (sum(i.host_build_s for i in insts)
-                          / max(1, sum(i.host_builds for i in insts)) * 1e6),
+        "graph": bool(args.graph),
+        "gpu_step_us": head["gpu_step_us"],
+        "metadata_upload_us": head["metadata_upload_us"],
+        "host_build_us": head["host_build_us"],
+        "kernel_events": head["kernel_events"],
+        "work_per_step": head["work_per_step"],
+        "other_configs": others,
         "measured_peaks": peaks,
         "device": {"name": torch.cuda.get_device_name(0),
                    "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
                    "hip": torch.version.hip, "torch": torch.__version__},
-        "kernel_events": {"stride": stride, "sampled_steps": NS},
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host cores ...")

@@ -13,6 +13,7 @@ int check_heads(int num_q_heads, int num_kv_heads, int head_dim, int block_size)
   if (num_q_heads % num_kv_heads) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_group(num_q_heads / num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_head_dim(head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_kv_heads(num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   return CPA_OK;
 }
 
@@ -28,6 +29,7 @@ extern "C" int cpa_append_kv(const void* k_new, const void* v_new, const int32_t
   if (head_dim <= 0 || num_kv_heads <= 0) return CPA_ERR_INVALID;
   if (block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_head_dim(head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_kv_heads(num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_seqs < 0 || bt_stride <= 0) return CPA_ERR_INVALID;
   if (num_tokens == 0) return CPA_OK;
   if (num_seqs == 0 || !k_new || !v_new || !d_query_start_loc || !d_context_lens ||

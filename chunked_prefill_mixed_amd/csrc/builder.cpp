@@ -37,6 +37,7 @@ int check_params(const cpa_build_params_t* p) {
   if (p->num_q_heads % p->num_kv_heads) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_group(p->num_q_heads / p->num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_head_dim(p->head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_kv_heads(p->num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (p->decode_split_tokens % cpa::kBlock || p->decode_split_tokens > cpa::kDecodeMaxSplit)
     return CPA_ERR_INVALID;
   if (p->chunk_split_tokens % cpa::kKvTile) return CPA_ERR_INVALID;

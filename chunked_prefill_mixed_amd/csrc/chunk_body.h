@@ -23,17 +23,28 @@
 // is exactly the B-operand layout of the PV MFMA, so P never goes through
 // LDS.  V is stored transposed inside each cache page ([D][16]), so the PV
 // A operand is one 16-byte read per lane, with no transpose.
-// K/V tiles of 64 keys (4 pages) are staged in LDS by all 256 threads with
-// global_load_lds_dwordx4 (straight from memory into LDS, no register
-// staging); the next tile's loads are in flight while the current one is
-// computed.  The lane-to-LDS-slot order of those loads is fixed, so the LDS
-// layout is chosen by which 16 bytes each lane fetches.  K pages hold their
-// keys in 8-value pieces ([D/8][16][8]) and are copied as they are: the 16
-// keys a 16-lane group reads at one piece are 256 contiguous bytes, which
-// covers all 64 banks.  V^T rows keep their two 8-key halves swapped when
-// bit 3 of d is set (conflict-free fragment reads).  A tile that reaches past
-// the piece's last key goes through registers instead, so the V slots past
-// the end can be zeroed.
+//
+// Software pipeline, one 64-key tile t per iteration: the matrix cores
+// compute S(t+1) = K(t+1) Q^T while the vector units turn S(t) into
+// probabilities, then O += V(t) P(t).  So each wave always has matrix work
+// to overlap with its own exponentials, whatever the other wave on its SIMD
+// is doing.  K runs two tiles ahead of its use and V one, in two LDS stages
+// each: iteration t loads K(t+2) into the stage K(t) used and V(t+1) into
+// the stage V(t-1) used, with one barrier per tile.  The loads go straight
+// from memory into LDS (global_load_lds_dwordx4, by all 256 threads, issued
+// as inline assembly so the compiler does not make the current tile's LDS
+// reads wait for them).  The lane-to-LDS-slot order of those loads is fixed,
+// so the LDS layout is chosen by which 16 bytes each lane fetches.  K pages
+// hold their keys in 8-value pieces ([D/8][16][8]) and are copied as they
+// are: the 16 keys a 16-lane group reads at one piece are 256 contiguous
+// bytes, which covers all 64 banks.  V^T rows keep their two 8-key halves
+// swapped when bit 3 of d is set (conflict-free fragment reads).
+//
+// The last tile of a piece may reach past the piece's last key: its pages at
+// or past the end load page 0 (any valid page) instead.  Its keys past the
+// end lie past every row's causal limit, so the mask removes their scores;
+// their V values (unwritten or stale slots, possibly NaN) are zeroed in the
+// fragment registers before the PV product, where 0 * NaN would not vanish.
 // Only tiles that reach past the first query's last visible key apply the
 // causal mask.
 //
@@ -42,14 +53,13 @@
 // the GPU); such a piece writes its unnormalised fp32 output, running max and
 // sum, and merge_kernel (merge.hip) combines the pieces:
 //   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
-// The running max used as the exponent reference is only moved when a tile's
-// max exceeds it by more than 2^8, so the 16-64 accumulator rescale almost
-// never runs; the sums stay exact because numerator and denominator share the
+// The running max used as the exponent reference is the first tile's row max
+// and moves only when a later tile's max exceeds it by more than 8 (log2
+// units of the scaled score), so the 16-64 accumulator rescale almost never
+// runs; the sums stay exact because numerator and denominator share the
 // reference, and each probability stays below 2^8.
 
 #pragma once
-
-#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -72,7 +82,7 @@ __device__ __forceinline__ void chunk_body(
   constexpr int PER_THREAD = CHUNKS / 256;
   static_assert(CHUNKS % 256 == 0, "tile must split evenly over 256 threads");
 
-  // two stages: one tile is read while the next is written
+  // two stages each: K(t+1) is read while K(t+2) is written, V(t) while V(t+1)
   __shared__ __align__(16) uint16_t k_lds_buf[2][kKvTile * D];
   __shared__ __align__(16) uint16_t v_lds_buf[2][4 * PAGE];
 
@@ -88,7 +98,7 @@ __device__ __forceinline__ void chunk_body(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ncol = lane & 31, half = lane >> 5;
-  const int r = wave * 32 + ncol;
+  int r = wave * 32 + ncol;  // the wave's row, one per lane column
   int j = qb + r / G;
   const bool row_ok = j < qe;
   if (!row_ok) j = qe - 1;  // ragged tail: recompute the last query, store nothing
@@ -109,7 +119,6 @@ __device__ __forceinline__ void chunk_body(
   const int mb = ncol >> 3, mh = (ncol >> 2) & 1, mi = ncol & 3;
   const int krow = 16 * (mb >> 1) + 8 * mh + 4 * (mb & 1) + mi;
 
-  float m = neg_inf(), lsum = 0.f;
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -120,18 +129,32 @@ __device__ __forceinline__ void chunk_body(
   const int kt0 = kv_begin / kKvTile;
   const int n_kv = (kv_end + kKvTile - 1) / kKvTile;
 
-  uint4 kreg[PER_THREAD], vreg[PER_THREAD];
   // Page ids come in windows of 64 pages (16 tiles), one id per lane, read a
-  // window ahead of their use; a tile's ids are taken with v_readlane.  The
-  // pages slot i of a wave stages is the same for all its lanes.
+  // window ahead of their use.  Pages at or past kv_end read as page 0, so the
+  // last tile's loads stay inside the pool.  id_cur holds window win and
+  // id_next window win + 1; the K loads, the leading ones, move them on.
   auto load_window = [&](int w) {
     const int pg = 64 * w + lane;
     return pg * kBlock < kv_end ? btrow[pg] : 0;
   };
-  int win = kt0 / 16;  // window held in id_cur
+  int win = kt0 / 16;
   int id_cur = load_window(win), id_next = load_window(win + 1);
-  auto tile_ids = [&](int kt, int (&ids)[PER_THREAD]) {
-    if (kt / 16 != win) {  // first tile of the next window
+  // Load slot i of this wave covers 16-byte slot p = tid + 256 i of a stage:
+  // page p / (PAGE / 8) of the tile (the same page for the whole wave) at the
+  // same place inside it for every i.  K slot s = p % (PAGE / 8) is the
+  // page's own slot s (piece s / 16 of key s % 16); V slot s holds row
+  // d = s / 2, half (s & 1) ^ bit 3 of d.
+  const uint32_t k_lane_bytes = 16u * (tid % (PAGE / 8));
+  const int v_s = tid % (PAGE / 8), v_d = v_s >> 1;
+  const uint32_t v_lane_bytes = 2u * (v_d * kBlock + 8 * ((v_s & 1) ^ ((v_d >> 3) & 1)));
+  // byte offset, in either cache, of this KV head's part of the page under
+  // load slot i of tile kt (wave-uniform); computed once per tile, when its
+  // K is loaded, and used again for its V one iteration later
+  const char* k_head = reinterpret_cast<const char*>(k_cache) + (int64_t)g * PAGE * 2;
+  const char* v_head = reinterpret_cast<const char*>(v_cache) + (int64_t)g * PAGE * 2;
+  const uint32_t page_bytes = (uint32_t)num_kv_heads * PAGE * 2;  // below 2^21 (kMaxKvHeads)
+  auto page_offsets = [&](int kt, int64_t (&off)[PER_THREAD]) {
+    if ((kt >> 4) != win) {  // tiles advance one at a time: at most one window
       id_cur = id_next;
       ++win;
       id_next = load_window(win + 1);
@@ -139,204 +162,186 @@ __device__ __forceinline__ void chunk_body(
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int pg = kt * 4 + (wave_u * 64 + 256 * i) / (PAGE / 8);
-      ids[i] = __builtin_amdgcn_readlane(id_cur, pg - 64 * win);
+      // page ids are non-negative: an unsigned 32 x 32 -> 64-bit product
+      off[i] = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readlane(id_cur, pg & 63) *
+                         page_bytes);
     }
   };
-  // the ragged last tile of a piece, through registers: pages at or past
-  // kv_end are not read, V slots past it are zeroed
-  auto load_tile = [&](int kt, const int (&ids)[PER_THREAD]) {
+  auto issue_k = [&](const int64_t (&off)[PER_THREAD], int stage) {
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int kp = cidx / (PAGE / 8);
-      const int w = cidx % (PAGE / 8);
-      const int pg = kt * 4 + kp;
-      const int key0 = pg * kBlock;
-      if (key0 < kv_end) {
-        const int64_t base = ((int64_t)ids[i] * num_kv_heads + g) * PAGE;
-        kreg[i] = *reinterpret_cast<const uint4*>(k_cache + base + w * 8);
-        uint4 v = *reinterpret_cast<const uint4*>(v_cache + base + w * 8);
-        // V piece w covers d = w/2 and page slots 8*(w%2)..+8; zero slots
-        // at or past kv_end (unwritten or sentinel data must not reach P*V)
-        const int nvalid = kv_end - key0 - 8 * (w & 1);
-        if (nvalid < 8) {
-          uint32_t x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t keep = ((2 * e < nvalid) ? 0xFFFFu : 0u) |
-                                  ((2 * e + 1 < nvalid) ? 0xFFFF0000u : 0u);
-            x[e] &= keep;
-          }
-          v = make_uint4(x[0], x[1], x[2], x[3]);
-        }
-        vreg[i] = v;
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < PER_THREAD; ++i)
+      load_lds16(k_head + off[i], k_lane_bytes,
+                 lds_address(&k_lds_buf[stage][(wave_u * 64 + 256 * i) * 8]));
   };
-  // a whole tile below kv_end: thread tid fills 16-byte LDS slot p = tid +
-  // 256 i of the K and of the V stage.  Slot p lies in page p / (PAGE / 8) of
-  // the tile (the same page for the whole wave) and at the same place inside
-  // it for every i: K slot s = p % (PAGE / 8) is the page's own slot s (piece
-  // s / 16 of key s % 16); V slot s holds row d = s / 2, half (s & 1) ^ bit 3
-  // of d.
-  const uint32_t k_lane_bytes = 16u * (tid % (PAGE / 8));
-  const int v_s = tid % (PAGE / 8), v_d = v_s >> 1;
-  const uint32_t v_lane_bytes = 2u * (v_d * kBlock + 8 * ((v_s & 1) ^ ((v_d >> 3) & 1)));
-  auto issue_direct = [&](int stage, const int (&ids)[PER_THREAD]) {
+  auto issue_v = [&](const int64_t (&off)[PER_THREAD], int stage) {
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int64_t base = ((int64_t)ids[i] * num_kv_heads + g) * PAGE * 2;  // bytes
-      const int lds_off = (wave_u * 64 + 256 * i) * 8;
-      load_lds16(reinterpret_cast<const char*>(k_cache) + base + k_lane_bytes,
-                 &k_lds_buf[stage][lds_off]);
-      load_lds16(reinterpret_cast<const char*>(v_cache) + base + v_lane_bytes,
-                 &v_lds_buf[stage][lds_off]);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    uint16_t* k_lds = k_lds_buf[stage];
-    uint16_t* v_lds = v_lds_buf[stage];
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int cidx = tid + 256 * i;
-      const int kp = cidx / (PAGE / 8);
-      const int w = cidx % (PAGE / 8);
-      *reinterpret_cast<uint4*>(&k_lds[kp * PAGE + w * 8]) = kreg[i];
-      // V^T row d = w/2 keeps its two 8-key halves swapped when bit 3 of d is
-      // set, so 16 lanes reading half 0 of rows d..d+15 hit distinct banks
-      const int d = w >> 1, hh = (w & 1) ^ ((d >> 3) & 1);
-      *reinterpret_cast<uint4*>(&v_lds[kp * PAGE + d * kBlock + 8 * hh]) = vreg[i];
-    }
+    for (int i = 0; i < PER_THREAD; ++i)
+      load_lds16(v_head + off[i], v_lane_bytes,
+                 lds_address(&v_lds_buf[stage][(wave_u * 64 + 256 * i) * 8]));
   };
 
-  // tile kt is whole (all 64 keys below kv_end) or the ragged last one
-  auto whole = [&](int kt) { return (kt + 1) * kKvTile <= kv_end; };
-  {
-    int ids[PER_THREAD];
-    tile_ids(kt0, ids);
-    if (whole(kt0)) {
-      issue_direct(0, ids);
-    } else {
-      load_tile(kt0, ids);
-      store_tile(0);
-    }
-  }
-  wait_vmem();
-  __syncthreads();
-
-  // one 64-key tile; MASK is a compile-time switch so tiles wholly visible to
-  // every row of the tile carry no masking code at all.  On entry the tile is
-  // in LDS stage (kt - kt0) & 1.
-  auto tile = [&](auto mask_tag, int kt) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int stage = (kt - kt0) & 1;
-    const uint16_t* k_lds = k_lds_buf[stage];
-    const uint16_t* v_lds = v_lds_buf[stage];
-    // start the next tile into the other stage (last read in tile kt - 1,
-    // before the barrier that ended it)
-    const bool more = kt + 1 < n_kv;
-    const bool next_whole = whole(kt + 1);
-    if (more) {
-      int ids[PER_THREAD];
-      tile_ids(kt + 1, ids);
-      if (next_whole)
-        issue_direct(stage ^ 1, ids);
-      else
-        load_tile(kt + 1, ids);
-    }
-
-    // S^T = K Q^T for two 32-key blocks, the two accumulator chains interleaved
-    f32x16_t s[2];
+  // S^T = K Q^T of the tile in K stage `stage`: two 32-key blocks, their
+  // accumulator chains interleaved, K fragments read kAhead MFMAs before use
+  constexpr int kAhead = 4;
+  auto kfrag = [&](int stage, int i) {
+    // key kr = 32 (i & 1) + krow of the tile, piece 2 (i >> 1) + half
+    const int kr = 32 * (i & 1) + krow;
+    return *reinterpret_cast<const uint4*>(
+        &k_lds_buf[stage][(kr / kBlock) * PAGE + ((2 * (i >> 1) + half) * kBlock + kr % kBlock) * 8]);
+  };
+  auto mask = [&](f32x16_t (&s)[2], int kt) {
+    const int key_base = kt * kKvTile;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    // K fragments are read kAhead MFMAs before their use, so LDS latency
-    // hides behind the MFMAs in flight
-    constexpr int kAhead = 4;
-    uint4 ka[2 * KS];
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      // key kr = 32 (i & 1) + krow of the tile, piece 2 (i >> 1) + half
-      const int kr = 32 * (i & 1) + krow;
-      ka[i] = *reinterpret_cast<const uint4*>(
-          &k_lds[(kr / kBlock) * PAGE + ((2 * (i >> 1) + half) * kBlock + kr % kBlock) * 8]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i)
-      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
-                                                         __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
-                                                         s[i & 1], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS - kAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
-
-    if constexpr (MASK) {
-      const int key_base = kt * kKvTile;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = key_base + 32 * kb + 16 * (rr >> 3) + 8 * half + (rr & 7);
-          if (key > qlimit) s[kb][rr] = neg_inf();
-        }
-    }
-
-    // the first PV A operands (V^T fragments, independent of P) are read
-    // now, so their LDS latency hides behind the softmax below
-    const int vh = half ^ ((ncol >> 3) & 1);  // the swizzled half holding keys 8*half..
-    auto vfrag = [&](int i) {  // i = kp * DB + db
-      return *reinterpret_cast<const uint4*>(
-          &v_lds[(i / DB) * PAGE + (32 * (i % DB) + ncol) * kBlock + 8 * vh]);
-    };
-    constexpr int kVAhead = 4;
-    uint4 va[kVAhead];
-#pragma unroll
-    for (int i = 0; i < kVAhead; ++i) va[i] = vfrag(i);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // tile max per row (four independent chains, then across the half-waves)
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = key_base + 32 * kb + 16 * (rr >> 3) + 8 * half + (rr & 7);
+        if (key > qlimit) s[kb][rr] = neg_inf();
+      }
+  };
+  auto row_max = [&](const f32x16_t (&s)[2]) {
     float pm[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) pm[rr & 3] = fmaxf(pm[rr & 3], s[kb][rr]);
-    const float mx = half_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
+    return half_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
+  };
 
-    // probabilities against the current reference max, bf16-rounded as the
-    // PV product uses them, and their row sum (two per v_dot2, four partial
-    // sums).  They are computed before the tile max is known, and computed
-    // again in the rare case the reference has to move.
-    uint4 pb[4];
-    float ps[4];
-    auto probs = [&](float msc) {
+  // probabilities of S(t) against the reference max, bf16-rounded as the PV
+  // product uses them, and their sums (two per v_dot2, four partial sums)
+  uint4 pb[4];
+  float ps[4];
+  auto probs = [&](const f32x16_t (&s)[2], float msc) {
 #pragma unroll
-      for (int kp = 0; kp < 4; ++kp) {
-        float pv[8];
+    for (int kp = 0; kp < 4; ++kp) {
+      float pv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          pv[i] = fast_exp2(__builtin_fmaf(s[kp >> 1][8 * (kp & 1) + i], scale_log2, -msc));
-        pb[kp] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
-        ps[kp] = sum2_bf16(pb[kp].w,
-                           sum2_bf16(pb[kp].z, sum2_bf16(pb[kp].y, sum2_bf16(pb[kp].x, 0.f))));
+      for (int i = 0; i < 8; ++i)
+        pv[i] = fast_exp2(__builtin_fmaf(s[kp >> 1][8 * (kp & 1) + i], scale_log2, -msc));
+      pb[kp] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                          pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+      ps[kp] = sum2_bf16(pb[kp].w,
+                         sum2_bf16(pb[kp].z, sum2_bf16(pb[kp].y, sum2_bf16(pb[kp].x, 0.f))));
+    }
+  };
+  // S(t+1) into sn while the probabilities of S(t) are computed: each MFMA
+  // is followed by its share of the vector work (the scheduling groups ask
+  // the compiler for that interleave)
+  auto qk_and_probs = [&](f32x16_t (&sn)[2], int kstage, const f32x16_t (&s)[2], float msc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[kb][i] = 0.f;
+    uint4 ka[2 * KS];
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) ka[i] = kfrag(kstage, i);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i)
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
+                                                          __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
+                                                          sn[i & 1], 0, 0, 0);
+    probs(s, msc);
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i + kAhead < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+  };
+  auto qk = [&](f32x16_t (&sn)[2], int kstage) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[kb][i] = 0.f;
+    uint4 ka[2 * KS];
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) ka[i] = kfrag(kstage, i);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i)
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
+                                                          __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
+                                                          sn[i & 1], 0, 0, 0);
+  };
+  // O^T += V^T P^T over the tile in V stage `stage`, one page (16 keys) per
+  // MFMA, the DB accumulator chains interleaved.  With `ragged`, V values of
+  // keys at or past kv_end (key base kt * 64) are zeroed first.
+  constexpr int kVAhead = 4;
+  const int vh = half ^ ((ncol >> 3) & 1);  // the swizzled half holding keys 8*half..
+  auto vfrag = [&](int stage, int i) {  // i = kp * DB + db
+    return *reinterpret_cast<const uint4*>(
+        &v_lds_buf[stage][(i / DB) * PAGE + (32 * (i % DB) + ncol) * kBlock + 8 * vh]);
+  };
+  auto pv = [&](int stage, bool ragged, int kt) {
+    uint4 va[4 * DB];
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) va[i] = vfrag(stage, i);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      uint4 a = va[i];
+      if (ragged) {
+        // keys kt*64 + 16 kp + 8 half + e, e < 8, of this lane's fragment
+        const int nvalid = kv_end - (kt * kKvTile + 16 * (i / DB) + 8 * half);
+        uint32_t x[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t keep = ((2 * e < nvalid) ? 0xFFFFu : 0u) |
+                                ((2 * e + 1 < nvalid) ? 0xFFFF0000u : 0u);
+          x[e] &= keep;
+        }
+        a = make_uint4(x[0], x[1], x[2], x[3]);
       }
-    };
-    probs(m * scale_log2);
-    // move the reference max only when this tile exceeds it by more than 2^8
-    // (always on a row's first tile, where m is -inf)
-    const bool grow = (mx - m) * scale_log2 > 8.f;
-    if (__builtin_expect(__any(grow), 0)) {
-      // rare: rescale the running sums; the empty asm keeps the compiler from
-      // hoisting this out of the branch and running it on every tile
+      o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, pb[i / DB]),
+                                                          o[i % DB], 0, 0, 0);
+    }
+    if (!ragged) {
+      // V fragments read kVAhead MFMAs before their use
+      __builtin_amdgcn_sched_group_barrier(0x100, kVAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kVAhead < 4 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+
+  // tile kt needs the causal mask iff its last key is past the tile's first
+  // query's limit: kt*64 + 63 > context + q_begin
+  const int kt_mask = max(kt0, min(n_kv, (c + qb + 1) / kKvTile));
+
+  // prologue: K(kt0) in K stage 0; then K(kt0+1) and V(kt0) load while
+  // S(kt0) is computed; its row max is the first reference max
+  int64_t off_a[PER_THREAD], off_b[PER_THREAD];  // page offsets of tiles kt0, kt0 + 1
+  page_offsets(kt0, off_a);
+  issue_k(off_a, 0);
+  wait_vmem();
+  __syncthreads();
+  issue_v(off_a, 0);
+  if (kt0 + 1 < n_kv) {
+    page_offsets(kt0 + 1, off_b);
+    issue_k(off_b, 1);
+  }
+  f32x16_t sa[2], sb[2];
+  qk(sa, 0);
+  if (kt0 >= kt_mask) mask(sa, kt0);
+  float m = row_max(sa);  // finite: every row sees the piece's first key
+  float lsum = 0.f;
+  wait_vmem();
+  __syncthreads();
+
+  // the rare move of the reference max: the tile's row max beats it by more
+  // than 8, which a probability above 2^8, and then the sum, shows
+  auto rescale_if_needed = [&](const f32x16_t (&s)[2]) {
+    float tsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (__builtin_expect(__any(!(tsum <= 256.f)), 0)) {
+      // the empty asm keeps the compiler from hoisting this out of the
+      // branch and running it on every tile
       asm volatile("" ::: "memory");
+      const float mx = row_max(s);
+      const bool grow = (mx - m) * scale_log2 > 8.f;  // the same in both halves of a row
       const float mn = grow ? mx : m;
       const float alpha = fast_exp2((m - mn) * scale_log2);
       m = mn;
@@ -345,36 +350,58 @@ __device__ __forceinline__ void chunk_body(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      probs(m * scale_log2);
+      probs(s, m * scale_log2);
+      tsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
-    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-
-    // O^T += V^T P^T, one page (16 keys) per MFMA, the DB accumulator chains
-    // interleaved; V fragments read kVAhead MFMAs before their use
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      const uint4 a = va[i % kVAhead];
-      if (i + kVAhead < 4 * DB) va[i % kVAhead] = vfrag(i + kVAhead);
-      o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          __builtin_bit_cast(bf16x8_t, pb[i / DB]),
-                                                          o[i % DB], 0, 0, 0);
-    }
-
-    // the next tile must be in LDS before any wave reads it
-    if (more) {
-      if (!next_whole) store_tile(stage ^ 1);
-      wait_vmem();
-      __syncthreads();
-    }
+    lsum += tsum;
   };
-
-  // tile kt needs the causal mask iff its last key is past the tile's first
-  // query's limit: kt*64 + 63 > context + q_begin
-  const int kt_mask = max(kt0, min(n_kv, (c + qb + 1) / kKvTile));
-  for (int kt = kt0; kt < kt_mask; ++kt) tile(std::integral_constant<bool, false>(), kt);
-  for (int kt = kt_mask; kt < n_kv; ++kt) tile(std::integral_constant<bool, true>(), kt);
+  // Tile kt with a next tile: s holds S(kt), sn receives S(kt+1).  LDS holds
+  // V(kt) in V stage st and K(kt+1) in K stage st ^ 1; off_next holds the page
+  // offsets of tile kt+1 and receives those of tile kt+2.
+  auto step = [&](const f32x16_t (&s)[2], f32x16_t (&sn)[2], int64_t (&off_next)[PER_THREAD],
+                  int64_t (&off_after)[PER_THREAD], int kt) {
+    const int st = (kt - kt0) & 1;
+    if (kt + 2 < n_kv) {
+      page_offsets(kt + 2, off_after);
+      issue_k(off_after, st);  // K(kt) was read in the previous iteration
+    }
+    issue_v(off_next, st ^ 1);  // V(kt-1) likewise
+    qk_and_probs(sn, st ^ 1, s, m * scale_log2);
+    rescale_if_needed(s);
+    pv(st, false, kt);
+    if (kt + 1 >= kt_mask) mask(sn, kt + 1);
+    // the next tiles must be in LDS, and every wave done with this one,
+    // before any wave goes on
+    wait_vmem();
+    __syncthreads();
+  };
+  // every tile but the last, two per trip so that S(kt) and S(kt+1) swap
+  // registers without copies; the last tile, the only one that can reach
+  // past kv_end, on its own
+  const int last = n_kv - 1;
+  int kt = kt0;
+  for (; kt + 2 <= last; kt += 2) {
+    step(sa, sb, off_b, off_a, kt);
+    step(sb, sa, off_a, off_b, kt + 1);
+  }
+  if (kt < last) {
+    step(sa, sb, off_b, off_a, kt);
+    ++kt;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+  }
+  probs(sa, m * scale_log2);
+  rescale_if_needed(sa);
+  if ((last + 1) * kKvTile > kv_end)
+    pv((last - kt0) & 1, true, last);
+  else
+    pv((last - kt0) & 1, false, last);
 
   lsum = half_sum(lsum);
+  // the output addresses are derived again here rather than kept in
+  // registers through the loop
+  asm volatile("" : "+v"(j), "+v"(r));
+  const int hq_out = g * G + (r % G);
   if (row_ok && slot >= 0) {
     // one piece of a split tile: unnormalised partial for merge_kernel
     const int64_t pr = ((int64_t)slot * num_kv_heads + g) * kChunkRows + r;
@@ -393,7 +420,7 @@ __device__ __forceinline__ void chunk_body(
     }
   } else if (row_ok) {
     const float inv = 1.f / lsum;
-    uint16_t* orow = out + ((int64_t)(t0 + j) * num_q_heads + hq) * D;
+    uint16_t* orow = out + ((int64_t)(t0 + j) * num_q_heads + hq_out) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -405,7 +432,7 @@ __device__ __forceinline__ void chunk_body(
         *reinterpret_cast<uint2*>(orow + d) = v;
       }
     if (lse && half == 0)
-      lse[(int64_t)(t0 + j) * num_q_heads + hq] = (m * scale_log2 + __log2f(lsum)) * kLn2;
+      lse[(int64_t)(t0 + j) * num_q_heads + hq_out] = (m * scale_log2 + __log2f(lsum)) * kLn2;
   }
 }
 

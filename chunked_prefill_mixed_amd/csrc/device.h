@@ -65,14 +65,31 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t
 
 // 16 bytes per lane from global memory straight into LDS
 // (global_load_lds_dwordx4): lane l's bytes land at lds_wave_base + 16 * l,
-// and lds_wave_base must be the same for every lane of the wave.  Completion
-// is counted by vmcnt, so the data may be read after s_waitcnt vmcnt(0) and a
-// barrier.
-__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// and lds_wave_base (a byte address in LDS) must be the same for every lane of
+// the wave.  Completion is counted by vmcnt, so the data may be read after
+// s_waitcnt vmcnt(0) and a barrier.  The load is written as inline assembly:
+// the compiler then does not see it write LDS and does not make later LDS
+// reads wait for it (with the builtin it adds that wait wherever it cannot
+// tell two double-buffered stages apart).  The caller orders it: wait_vmem()
+// and a barrier before any wave reads the bytes.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_wave_base) : "memory");
+}
+// The same with a wave-uniform 64-bit base (SGPRs) and a 32-bit per-lane byte
+// offset: the lane's 16 bytes come from base + lane_offset.
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t lane_offset,
+                                           uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_offset), "s"(base), "{m0}"(lds_wave_base)
+               : "memory");
+}
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 
 // DPP lane exchanges inside a 16-lane row.
 template <int CTRL>

@@ -35,6 +35,10 @@ inline bool supported_group(int group) {
   return group == 1 || group == 2 || group == 4 || group == 8;
 }
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
+// at most 256 KV heads: one page of all KV heads then spans under 2^21 bytes,
+// and the chunk kernel forms page offsets as 32 x 32-bit products
+constexpr int kMaxKvHeads = 256;
+inline bool supported_kv_heads(int h) { return h >= 1 && h <= kMaxKvHeads; }
 
 }  // namespace cpa
 

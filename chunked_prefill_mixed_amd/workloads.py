@@ -202,7 +202,11 @@ PREFIXES = {2: (0, 3840, 7680), 3: (0, 2048, 4096, 6144)}
 
 
 def num_instances(config: int) -> int:
-    return {1: 4, 2: 3, 3: 4, 4: 1, 5: 1}[config]
+    """Instances of a configuration: its prefix positions (configs 2 and 3),
+    the steps of the tiny run, or two seeds of the same recipe (configs 4
+    and 5), so that steps rotated over them never find their K/V in the
+    256 MB last-level cache from the step before."""
+    return {1: 4, 2: 3, 3: 4, 4: 2, 5: 2}[config]
 
 
 def make_workload(config: int, instance: int = 0) -> Workload:
@@ -239,7 +243,7 @@ def make_workload(config: int, instance: int = 0) -> Workload:
         reqs = [Req(i, int(c), int(c) + 1, True) for i, c in enumerate(ctx)]
         reqs.append(Req(64, 31744, 32768, False))
         reach = [int(c) + 1 for c in ctx] + [32768]
-        return build("long_context/prefix31744", seed, instance, num_q_heads=32,
+        return build(f"long_context/prefix31744/seed{instance}", seed, instance, num_q_heads=32,
                      num_kv_heads=8, head_dim=128, token_budget=8192, long_prefill_cap=0,
                      requests=reqs, reach=reach, pool_blocks=None, streams=st)
     if config == 5:
@@ -254,7 +258,7 @@ def make_workload(config: int, instance: int = 0) -> Workload:
             reqs.append(Req(256 + k, int(offs[k]), int(offs[k]) + lefts[k], False))
         reach = [int(c) + 1 for c in ctx] + [int(offs[k]) + lefts[k] for k in range(3)]
         # 2 GiB of K+V: 32768 pages of 64 KiB (32 KiB K + 32 KiB V)
-        return build("heavy_mixed", seed, instance, num_q_heads=32, num_kv_heads=8,
+        return build(f"heavy_mixed/seed{instance}", seed, instance, num_q_heads=32, num_kv_heads=8,
                      head_dim=128, token_budget=8192, long_prefill_cap=0, requests=reqs,
                      reach=reach, pool_blocks=32768, streams=st)
     raise ValueError(f"unknown config {config}")

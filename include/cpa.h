@@ -37,7 +37,7 @@
  *     never throws across the ABI.  CPA_ERR_DEVICE carries a launch failure
  *     reported by hipGetLastError.
  *   - Supported shapes: head_dim in {64, 128}; num_q_heads / num_kv_heads in
- *     {1, 2, 4, 8}; block_size 16; bf16 only.
+ *     {1, 2, 4, 8}; num_kv_heads at most 256; block_size 16; bf16 only.
  *
  * KV cache layout (one tensor each for K and V; the same page id in both)
  *   k_cache [num_blocks][num_kv_heads][head_dim/8][16][8]

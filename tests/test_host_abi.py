@@ -305,6 +305,7 @@ def test_builder_rejects_unknown_policy_value(lib):
     ("group_3", cpa.CPA_ERR_UNSUPPORTED),
     ("heads_not_multiple", cpa.CPA_ERR_UNSUPPORTED),
     ("block_size_32", cpa.CPA_ERR_UNSUPPORTED),
+    ("kv_heads_over_256", cpa.CPA_ERR_UNSUPPORTED),
     ("split_not_page_multiple", cpa.CPA_ERR_INVALID),
     ("split_over_64_pages", cpa.CPA_ERR_INVALID),
     ("chunk_split_not_tile_multiple", cpa.CPA_ERR_INVALID),
@@ -338,6 +339,8 @@ def test_builder_error_paths(lib, case, status):
         args.update(Hq=7, Hkv=2)
     elif case == "block_size_32":
         kw["block_size"] = 32
+    elif case == "kv_heads_over_256":
+        args.update(Hq=257, Hkv=257)
     elif case == "split_not_page_multiple":
         kw["decode_split_tokens"] = 24
     elif case == "split_over_64_pages":
