@@ -225,31 +225,45 @@ __device__ __forceinline__ void chunk_body(
                          sum2_bf16(pb[kp].z, sum2_bf16(pb[kp].y, sum2_bf16(pb[kp].x, 0.f))));
     }
   };
-  // S(t+1) into sn while the probabilities of S(t) are computed: each MFMA
-  // is followed by its share of the vector work (the scheduling groups ask
-  // the compiler for that interleave)
+  // S(t+1) into sn while the probabilities of S(t) are computed.  The work
+  // is laid out in 2 KS slots, one MFMA each: slot i issues the K fragment
+  // read for slot i + kAhead, MFMA i, then its share of the 16 probability
+  // units (unit u: elements 2u and 2u+1 of the lane's 32: two fma, two
+  // exponentials, one bf16 pack, one v_dot2 into the page's sum; one unit
+  // per slot at head_dim 128, two at 64).  The vector work runs while the
+  // MFMA does; a scheduling barrier after each slot keeps the compiler from
+  // regrouping all MFMAs ahead of all vector work.
+  constexpr int kUnitsPerSlot = 16 / (2 * KS);
+  static_assert(kUnitsPerSlot * 2 * KS == 16, "16 probability units over the MFMA slots");
   auto qk_and_probs = [&](f32x16_t (&sn)[2], int kstage, const f32x16_t (&s)[2], float msc) {
+    uint4 ka[kAhead];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < kAhead; ++i) ka[i] = kfrag(kstage, i);
+    uint32_t pw[4][4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sn[kb][i] = 0.f;
-    uint4 ka[2 * KS];
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) ka[i] = kfrag(kstage, i);
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i)
-      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[i]),
-                                                          __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
-                                                          sn[i & 1], 0, 0, 0);
-    probs(s, msc);
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+    for (int kp = 0; kp < 4; ++kp) ps[kp] = 0.f;
+    const f32x16_t zero = {};
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
-      if (i + kAhead < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      const uint4 a = ka[i % kAhead];
+      if (i + kAhead < 2 * KS) ka[i % kAhead] = kfrag(kstage, i + kAhead);
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
+                                                          i < 2 ? zero : sn[i & 1], 0, 0, 0);
+#pragma unroll
+      for (int uu = 0; uu < kUnitsPerSlot; ++uu) {
+        const int u = i * kUnitsPerSlot + uu;
+        const int kp = u >> 2, e2 = u & 3;  // page kp, pair e2 of its 8 keys
+        const int x = 8 * (kp & 1) + 2 * e2;
+        const float p0 = fast_exp2(__builtin_fmaf(s[kp >> 1][x], scale_log2, -msc));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kp >> 1][x + 1], scale_log2, -msc));
+        pw[kp][e2] = pack_bf16x2(p0, p1);
+        ps[kp] = sum2_bf16(pw[kp][e2], ps[kp]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) pb[kp] = make_uint4(pw[kp][0], pw[kp][1], pw[kp][2], pw[kp][3]);
   };
   auto qk = [&](f32x16_t (&sn)[2], int kstage) {
 #pragma unroll
