@@ -29,7 +29,8 @@ CHUNK_TILE_WORDS = 8
 CHUNK_MERGE_WORDS = 8
 
 EXPORTED = ("cpa_build_metadata", "cpa_append_kv", "cpa_workspace_size", "cpa_attention",
-            "cpa_status_string")
+            "cpa_attention_noalloc", "cpa_status_string")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CPA_NOALLOC_SCRATCH_BYTES
 
 i32p = ctypes.POINTER(ctypes.c_int32)
 i64p = ctypes.POINTER(ctypes.c_int64)
@@ -136,6 +137,11 @@ def load():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_float, vp, vp, vp, ctypes.c_size_t, vp]
     lib.cpa_attention.restype = ctypes.c_int
+    lib.cpa_attention_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                          ctypes.POINTER(cpa_plan_counts_t), ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+    lib.cpa_attention_noalloc.restype = ctypes.c_int
     lib.cpa_status_string.argtypes = [ctypes.c_int]
     lib.cpa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -311,3 +317,21 @@ def cpa_attention(q, k_cache, v_cache, block_table, query_start_loc, seq_lens, c
                               _ptr(workspace), int(ws_bytes), _stream(stream))
     if st != CPA_OK:
         raise CpaError(st, "cpa_attention")
+
+
+def cpa_attention_noalloc(q, k_cache, v_cache, block_table, query_start_loc, seq_lens,
+                          context_lens, plan, counts, *, num_seqs, num_decodes, num_tokens,
+                          softmax_scale, out, lse=None, stream=None):
+    """cpa_attention with the library's own scratch array for split pieces."""
+    _check_dev(q, k_cache, v_cache, block_table, query_start_loc, context_lens, plan, out, lse)
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k_cache.shape[1]
+    _check_cache(k_cache, v_cache, Hkv, D)
+    st = load().cpa_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                      int(block_table.shape[1]), _ptr(query_start_loc),
+                                      _ptr(seq_lens), _ptr(context_lens), _ptr(plan),
+                                      ctypes.byref(counts), int(num_seqs), int(num_decodes),
+                                      int(num_tokens), int(Hq), int(Hkv), int(D), BLOCK_SIZE,
+                                      float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream))
+    if st != CPA_OK:
+        raise CpaError(st, "cpa_attention_noalloc")

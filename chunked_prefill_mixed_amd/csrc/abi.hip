@@ -1,6 +1,8 @@
 // C-ABI device entry points: argument checks, then kernel launches on the
 // caller's stream.  Declarations and contracts are in include/cpa.h.
 
+#include <atomic>
+
 #include "../../include/cpa.h"
 #include "internal.h"
 #include "tiles.h"
@@ -113,4 +115,65 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
     if (st != CPA_OK) return st;
   }
   return CPA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// cpa_attention_noalloc: the same call with the partial-result workspace in a
+// file-scope device array, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;  // CPA_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == CPA_NOALLOC_SCRATCH_BYTES, "header and library agree");
+
+// One copy per GPU, held until the process ends.  Host code never passes this
+// name to a kernel (on the host it is only a stand-in): the device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_address[kMaxDevices];
+
+// Device address of the current device's scratch array.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CPA_ERR_DEVICE;
+  void* p = scratch_address[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return CPA_ERR_DEVICE;
+    scratch_address[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" int cpa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* d_block_table, int bt_stride,
+                                     const int32_t* d_query_start_loc, const int32_t* d_seq_lens,
+                                     const int32_t* d_context_lens, const int32_t* d_plan,
+                                     const cpa_plan_counts_t* counts, int num_seqs,
+                                     int num_decodes, int num_tokens, int num_q_heads,
+                                     int num_kv_heads, int head_dim, int block_size,
+                                     float softmax_scale, void* out, float* lse, void* stream) {
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != CPA_OK) return st;
+  if (!counts || counts->num_decode_partials < 0 || counts->num_chunk_partials < 0)
+    return CPA_ERR_INVALID;
+  const cpa::WorkspaceLayout wl =
+      cpa::workspace_layout(counts->num_decode_partials, counts->num_chunk_partials, num_q_heads,
+                            num_kv_heads, head_dim);
+  if (wl.total > kScratchBytes) return CPA_ERR_CAPACITY;
+  void* ws = nullptr;
+  if (wl.total > 0 && num_tokens > 0) {
+    st = current_scratch(&ws);
+    if (st != CPA_OK) return st;
+  }
+  return cpa_attention(q, k_cache, v_cache, d_block_table, bt_stride, d_query_start_loc,
+                       d_seq_lens, d_context_lens, d_plan, counts, num_seqs, num_decodes,
+                       num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, softmax_scale,
+                       out, lse, ws, ws ? kScratchBytes : 0, stream);
 }

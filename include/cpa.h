@@ -277,6 +277,36 @@ int cpa_attention(const void* q, const void* k_cache, const void* v_cache,
                   float softmax_scale, void* out, float* lse, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * cpa_attention_noalloc -- cpa_attention for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, meaning and results as cpa_attention, without workspace /
+ * workspace_bytes: the fp32 partial results of split pieces live in a
+ * file-scope device array of CPA_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one copy per GPU, held until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, no hipFree); the first call on a device
+ * looks the array's device address up once (hipGetSymbolAddress) on the
+ * current device, which must be the device of `stream`.  Its contents need no
+ * initialisation (every partial is written before it is read).  All calls on
+ * one GPU share the array: two calls whose launches may overlap on one GPU
+ * (different streams, or a graph replayed while another call runs) race on it
+ * and must be ordered by the caller.  Returns CPA_ERR_CAPACITY, with nothing
+ * launched, when cpa_workspace_size(counts, ...) exceeds
+ * CPA_NOALLOC_SCRATCH_BYTES; CPA_ERR_DEVICE if the current device cannot be
+ * read; otherwise as cpa_attention.
+ */
+#define CPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int cpa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* d_block_table, int bt_stride,
+                          const int32_t* d_query_start_loc, const int32_t* d_seq_lens,
+                          const int32_t* d_context_lens, const int32_t* d_plan,
+                          const cpa_plan_counts_t* counts, int num_seqs, int num_decodes,
+                          int num_tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, float softmax_scale, void* out, float* lse,
+                          void* stream);
+
 /* cpa_status_string -- static, human-readable name of a status code. */
 const char* cpa_status_string(int status);
 
