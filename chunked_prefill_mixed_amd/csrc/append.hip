@@ -2,34 +2,31 @@
 // attention reads the cache ("05. Chunked Prefill" section 8; tbr8.org deep
 // dive 4.2, 16-token pages).  Pure bit copy.
 //
-// One wave per packed token, 4 tokens per workgroup.  A token's row is found
-// in one step: the wave's lanes read query_start_loc and context_lens in
-// parallel (64 entries per load, all loads in flight together) and the row is
-// the number of rows that start at or before the token, minus one (rows that
-// schedule no token share their start with the next row and are skipped by
-// the count).  The row's start, end and context are then read out of those
-// registers, so the page id is the second and last dependent load, where a
-// binary search would chain about log2(rows) of them (steps of 512 rows or
-// more reload the three values: one more dependent load).
+// One workgroup per page task: a (row, page) pair the step writes into, with
+// its new slots [o0, o1) (a whole page inside a chunk; a partial page at a
+// chunk's ends; one slot for a decode row).  The grid covers an upper bound
+// on the number of tasks (a row of n tokens touches at most n/16 + 2 pages);
+// the first wave of each workgroup finds its task by a prefix count of the
+// rows' page counts (the counts of 512 rows loaded in one round), and
+// workgroups past the last task exit.  After that one dependent round, every
+// thread issues all of its loads (up to 8 K pieces and one V unit per round;
+// one round at 8 KV heads of 128) before its first store, and the page id
+// arrives by a scalar load in the meantime, so a task costs about two memory
+// latencies.
 //
-// Both page layouts keep neighbouring slots side by side, so both are written
-// per aligned group of 8 slots.  K pages hold their keys in 8-value pieces
-// ([D/8][16][8] per KV head): piece c of the group's 8 slots is 128
-// contiguous bytes.  When all 8 slots are new (inside a chunk) the group's 8
-// waves share its K, wave r copying the blocks of 8 pieces r, r + 8, ... of
-// all 8 slots, so every store fills whole lines; otherwise (a decode row's token, the ends of
-// a chunk) each token's wave copies its own 16-byte pieces.  V pages are
-// stored transposed ([D][16]), so one token's V is a column of 2-byte values:
-// the wave of the group's first new token loads the V rows of the group's new
-// tokens (coalesced, Hkv*D*2 bytes each), and every lane turns the 8 values
-// of each of its (head, d) pairs into one 16-byte store.  A group that is
-// only partly new keeps its other slots: only the new ones are written; a
-// group with one new slot (a decode token) stores the values of the token's
-// own V row, which load before the row lookup, so its chain after the lookup
-// is the stores alone.  When
-// a whole page is new, its 16 waves share its V instead and write whole
-// 32-byte rows (whole lines): two 8-slot halves written by different waves
-// would meet in one line as partial writes.
+// K pages hold their keys in 8-value pieces ([Hkv][D/8][16][8]), so piece c
+// of slot o of head h is 16 bytes at ((h * D/8 + c) * 16 + o) * 16: with the
+// new slots innermost, consecutive threads write consecutive 16-byte pieces
+// (a whole page is 32 KB written front to back at head_dim 128, Hkv 8) and
+// read 16 bytes of consecutive tokens' rows.
+//
+// V pages are stored transposed ([Hkv][D][16]): row (h, d) holds the 16
+// slots' values, 32 bytes.  A thread takes a unit (h, 8 d values, one half of
+// the page's slots): it loads the 8 d values of each of the half's 8 tokens
+// (16 bytes each), transposes the 8 x 8 block of 2-byte values in registers
+// (one byte-permute per output dword) and stores 8 half-rows of 16 bytes.  A
+// half that is only partly new stores its new slots' 2-byte values alone,
+// leaving the others as they are.
 
 #include "device.h"
 #include "internal.h"
@@ -37,197 +34,179 @@
 
 namespace cpa {
 
-constexpr int kAppendWaves = 4;  // tokens per workgroup
-constexpr int kVGroup = 8;       // slots written together (16 bytes of a V row, 128 of a K piece)
-constexpr int kLookupChunks = 8;  // rows the lookup holds in registers: fewer than 512
+constexpr int kAppendThreads = 256;
+
+// Inclusive prefix sum over the wave (64 lanes).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int y = __shfl_up(x, k, 64);
+    if (lane >= k) x += y;
+  }
+  return x;
+}
+
+// dword i (0..3) and 16-bit element e (0..7) of the 16 bytes in v
+__device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t elem16(const uint4& v, int e) {
+  return (dword(v, e >> 1) >> (16 * (e & 1))) & 0xFFFFu;
+}
+
+constexpr int kRowsPerLane = 8;  // rows each lookup lane holds: 512 per round
 
 template <int D>
-__global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
-    const int32_t* __restrict__ bt, int bt_stride, int num_seqs, int num_tokens,
-    int num_kv_heads, uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache) {
-  constexpr int PAGE = kBlock * D;
-  constexpr int kParts = D / 8;  // 16-byte pieces per head row
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kAppendWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (t >= num_tokens) return;  // whole wave; no barrier below
-  const int hd = num_kv_heads * D;  // values of one token's K (or V) row
+    const int32_t* __restrict__ bt, int bt_stride, int num_seqs, int num_kv_heads,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache) {
+  constexpr int PAGE = kBlock * D;  // elements of one (page, KV head)
+  constexpr int PIECES = D / 8;     // 16-byte pieces per head row
+  constexpr int T = kAppendThreads;
+  __shared__ int task[5];  // row, page index in the row, o0, o1, packed token of slot o0
 
-  // the token's own V values (8 per lane, two passes) do not depend on its
-  // row: they load while the row is looked up, for the one-new-slot case
-  uint4 vown[2];
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    // the task's row: the first row whose running page count passes the
+    // workgroup id; rows that schedule no token touch no page.  Lane i holds
+    // rows 8i .. 8i+7 of a round of 512 (clamped, unconditional loads, all in
+    // flight together), sums their page counts, and one wave scan over the
+    // lanes' sums finds the lane whose rows hold the task.
+    const int lane = tid;
+    const int want = blockIdx.x;
+    int base = 0;
+    bool found = false;
+    for (int r0 = 0; r0 < num_seqs && !found; r0 += 64 * kRowsPerLane) {
+      const int first = r0 + kRowsPerLane * lane;
+      int q[kRowsPerLane + 1], c[kRowsPerLane], pages[kRowsPerLane];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    vown[u] = *reinterpret_cast<const uint4*>(v_new + (int64_t)t * hd + min(lane * 8 + 512 * u, hd - 8));
-
-  // row s = #{i < num_seqs : qsl[i] <= t} - 1; qsl is non-decreasing and
-  // qsl[num_seqs] = num_tokens > t
-  int s, q0, q1, c;
-  if (num_seqs < 64 * kLookupChunks) {
-    // lane i of chunk k holds qsl[64 k + i] and context_lens[64 k + i], all
-    // loaded at once; the row's start, end and context are then read out of
-    // those registers, so the page id is the second dependent load
-    const int nchunks = num_seqs / 64 + 1;  // chunks holding qsl[0 .. num_seqs]
-    int qv[kLookupChunks] = {}, cv[kLookupChunks] = {};
+      for (int j = 0; j <= kRowsPerLane; ++j) q[j] = qsl[min(first + j, num_seqs)];
 #pragma unroll
-    for (int k = 0; k < kLookupChunks; ++k) {
-      if (k < nchunks) {  // wave-uniform
-        const int i = 64 * k + lane;
-        qv[k] = i <= num_seqs ? qsl[i] : 0x7fffffff;
-        cv[k] = i < num_seqs ? ctx[i] : 0;
+      for (int j = 0; j < kRowsPerLane; ++j) c[j] = ctx[min(first + j, num_seqs - 1)];
+      int total = 0;
+#pragma unroll
+      for (int j = 0; j < kRowsPerLane; ++j) {
+        // rows past the last one clamp both starts to query_start_loc[num_seqs]: no tokens
+        const int n = q[j + 1] - q[j];
+        pages[j] = n > 0 ? (c[j] + n + kBlock - 1) / kBlock - c[j] / kBlock : 0;
+        total += pages[j];
       }
-    }
-    int count = 0;
+      const int incl = base + wave_inclusive_scan(total);
+      const bool mine = want >= incl - total && want < incl;
+      found = __ballot(mine) != 0;
+      if (mine) {
+        // the lane's row that holds the task: the first whose pages pass want
+        int run = incl - total, sel = -1, before = 0;
 #pragma unroll
-    for (int k = 0; k < kLookupChunks; ++k)
-      if (k < nchunks) count += __builtin_popcountll(__ballot(64 * k + lane < num_seqs && qv[k] <= t));
-    s = count - 1;
-    auto pick = [&](const int (&v)[kLookupChunks], int i) {  // v[i / 64] of lane i % 64
-      int x = 0;
-#pragma unroll
-      for (int k = 0; k < kLookupChunks; ++k)
-        if (k == i / 64) x = __builtin_amdgcn_readlane(v[k], i % 64);
-      return x;
-    };
-    q0 = pick(qv, s);
-    q1 = pick(qv, s + 1);
-    c = pick(cv, s);
-  } else {
-    int count = 0;
-    for (int base = 0; base < num_seqs; base += 64) {
-      const int i = base + lane;
-      const bool le = i < num_seqs && qsl[i] <= t;
-      count += __builtin_popcountll(__ballot(le));
-    }
-    s = count - 1;
-    q0 = qsl[s];
-    q1 = qsl[s + 1];
-    c = ctx[s];
-  }
-  const int p = c + (t - q0);
-  const int64_t blk = bt[(int64_t)s * bt_stride + p / kBlock];
-  const int64_t page0 = blk * num_kv_heads * (int64_t)PAGE;
-  const int gbeg = p & ~(kVGroup - 1);
-  const int row_end = c + (q1 - q0);  // one past the row's last new position
-  const int kpieces = hd / 8;  // 16-byte pieces of a K row: e = head * D/8 + c
-
-  // K piece e of page slot o lands in piece row c of the head's page
-  auto kdst = [&](int e, int o) {
-    return reinterpret_cast<uint4*>(k_cache + page0 + (int64_t)(e / kParts) * PAGE +
-                                    ((e % kParts) * kBlock + o) * 8);
-  };
-  if (gbeg >= c && gbeg + kVGroup <= row_end) {
-    // all 8 slots new: the pieces come in blocks of 8 and the wave in slot r
-    // of the group takes blocks b = r, r + 8, ...; lane (j = lane / 8,
-    // i = lane % 8) copies piece 8 b + i of slot j, so one instruction reads
-    // 8 whole 128-byte lines of k_new and writes 8 whole lines of the page
-    const int r = p - gbeg, j = lane / kVGroup, i = lane % kVGroup;
-    const uint16_t* src = k_new + (int64_t)(t - r + j) * hd;  // token of slot j
-    for (int b0 = r; b0 < kpieces / 8; b0 += 4 * 8) {
-      uint4 x[4];  // loads clamped into the token's row; stores only in range
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        x[u] = *reinterpret_cast<const uint4*>(src + min(8 * (b0 + 8 * u) + i, kpieces - 1) * 8);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (b0 + 8 * u < kpieces / 8) *kdst(8 * (b0 + 8 * u) + i, gbeg % kBlock + j) = x[u];
-    }
-  } else {
-    // the token's own pieces
-    const uint16_t* src = k_new + (int64_t)t * hd;
-    for (int e0 = lane; e0 < kpieces; e0 += 4 * 64) {
-      uint4 x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        x[u] = *reinterpret_cast<const uint4*>(src + min(e0 + 64 * u, kpieces - 1) * 8);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (e0 + 64 * u < kpieces) *kdst(e0 + 64 * u, p % kBlock) = x[u];
-    }
-  }
-
-  // V, whole page new (inside a chunk): the page's 16 waves share its V.  The
-  // wave in slot r takes the rows f = (head, d) in [r R, r R + R), R = Hkv D /
-  // 16, one per lane: it gathers the row's 16 values (one 2-byte load from
-  // each token; a lane group reads 128 contiguous bytes) and stores the whole
-  // 32-byte row, so 4 neighbouring lanes fill a 128-byte line.
-  const int pbeg = p & ~(kBlock - 1);
-  if (pbeg >= c && pbeg + kBlock <= row_end) {
-    const int r = p - pbeg, R = hd / kBlock;
-    const uint16_t* src = v_new + (int64_t)(t - r) * hd;  // token of page slot 0
-    for (int f = r * R + lane; f < (r + 1) * R; f += 64) {
-      uint32_t w[kBlock / 2];
-#pragma unroll
-      for (int j = 0; j < kBlock / 2; ++j)
-        w[j] = (uint32_t)src[(int64_t)(2 * j) * hd + f] |
-               ((uint32_t)src[(int64_t)(2 * j + 1) * hd + f] << 16);
-      uint4* dst = reinterpret_cast<uint4*>(v_cache + page0 + (int64_t)(f / D) * PAGE +
-                                            (f % D) * kBlock);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    }
-    return;
-  }
-
-  // V otherwise: only the wave of a group's first new token
-  if (p != gbeg && t != q0) return;
-  const int nnew = min(gbeg + kVGroup, row_end) - p;  // new slots p .. p + nnew - 1
-  const int lo = p - gbeg;                            // first new slot inside the group
-  const bool whole = lo == 0 && nnew == kVGroup;
-  uint16_t* vpage = v_cache + page0 + (gbeg % kBlock);  // + g * PAGE + d * 16: the group's 8 slots
-  if (nnew == 1) {
-    // one new slot (a decode token): the token's 8 values per lane and pass
-    // (the first two passes already loaded), one 2-byte store per (head, d)
-    uint16_t* vslot = vpage + lo;
-    for (int f0 = lane * 8; f0 < hd; f0 += 2 * 64 * 8) {
-      uint4 x[2] = {vown[0], vown[1]};
-      if (f0 != lane * 8) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          x[u] = *reinterpret_cast<const uint4*>(v_new + (int64_t)t * hd + min(f0 + 512 * u, hd - 8));
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (f0 + 512 * u >= hd) continue;
-        const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int f = f0 + 512 * u + e;
-          vslot[(int64_t)(f / D) * PAGE + (f % D) * kBlock] = (uint16_t)(wd[e / 2] >> (16 * (e & 1)));
+        for (int j = 0; j < kRowsPerLane; ++j) {
+          if (sel < 0 && want < run + pages[j]) {
+            sel = j;
+            before = run;
+          }
+          run += pages[j];
         }
+        int q0 = 0, n = 0, cc = 0;
+#pragma unroll
+        for (int j = 0; j < kRowsPerLane; ++j)
+          if (j == sel) {
+            q0 = q[j];
+            n = q[j + 1] - q[j];
+            cc = c[j];
+          }
+        const int pg = cc / kBlock + (want - before);
+        const int o0 = max(cc, pg * kBlock) - pg * kBlock;
+        task[0] = first + sel;
+        task[1] = pg;
+        task[2] = o0;
+        task[3] = min(cc + n, pg * kBlock + kBlock) - pg * kBlock;  // o1
+        task[4] = q0 + (pg * kBlock + o0 - cc);
       }
+      base = __builtin_amdgcn_readlane(incl, 63);
     }
-    return;
+    if (lane == 0 && !found) task[0] = -1;
   }
-  // each lane takes 8 consecutive (head, d) values per pass: one 16-byte load
-  // of each new token, one 16-byte store per (head, d)
-  for (int f0 = lane * 8; f0 < hd; f0 += 64 * 8) {
-    uint4 x[kVGroup];  // x[j]: the values of slot j (token t + j - lo) when new
+  __syncthreads();
+  const int row = __builtin_amdgcn_readfirstlane(task[0]);
+  if (row < 0) return;  // past the last task (uniform over the workgroup)
+  const int pg = __builtin_amdgcn_readfirstlane(task[1]);
+  const int o0 = __builtin_amdgcn_readfirstlane(task[2]);
+  const int o1 = __builtin_amdgcn_readfirstlane(task[3]);
+  const int t0 = __builtin_amdgcn_readfirstlane(task[4]);
+  // the page id is a scalar load; it overlaps the data loads issued below
+  const int blk = bt[(int64_t)row * bt_stride + pg];
+  const int nnew = o1 - o0;
+  const int hd = num_kv_heads * D;            // values of one token's K (or V) row
+  const int ngroups = num_kv_heads * PIECES;  // (head, 8-value group) pairs
+  const int page_bytes = num_kv_heads * PAGE * 2;
+  // byte ranges: the new tokens' rows, and the page (all KV heads)
+  const auto kin = make_page_rsrc(k_new + (int64_t)t0 * hd, nnew * hd * 2);
+  const auto vin = make_page_rsrc(v_new + (int64_t)t0 * hd, nnew * hd * 2);
+  const bool whole = nnew == kBlock;
+
+  // K: pieces e = (group, new slot), slots innermost; V: units u = (half of
+  // the slots that holds a new one, group), groups innermost.  A round loads a
+  // thread's 8 K pieces and its V unit's 8 token rows before any store; an
+  // index past the task loads from / stores to an offset outside its range,
+  // which the hardware turns into a zero load / a dropped store.
+  const int h_lo = o0 / 8, nhalves = (o1 - 1) / 8 - h_lo + 1;
+  const int kn = ngroups * nnew, vn = ngroups * nhalves;
+  for (int k0 = 0, v0 = 0; k0 < kn || v0 < vn; k0 += 8 * T, v0 += T) {
+    uint4 kx[8];
+    uint32_t kdst[8];
 #pragma unroll
-    for (int j = 0; j < kVGroup; ++j) {
-      const bool in = j >= lo && j < lo + nnew;
-      // slots that are not new read token t's row (always in range) and are
-      // then replaced by the cached values
-      x[j] = *reinterpret_cast<const uint4*>(v_new + (int64_t)(t + (in ? j - lo : 0)) * hd + f0);
+    for (int j = 0; j < 8; ++j) {
+      const int e = k0 + j * T + tid;
+      const int i = whole ? (e & (kBlock - 1)) : e % nnew;  // new slot o0 + i
+      const int g = whole ? (e >> 4) : e / nnew;
+      const bool in = e < kn;
+      kx[j] = buffer_load16(kin, in ? (uint32_t)(i * hd + g * 8) * 2 : kOffNone);
+      kdst[j] = in ? (uint32_t)((g * kBlock + o0 + i) * 8) * 2 : kOffNone;
     }
+    const int u = v0 + tid;
+    const bool vin_range = u < vn;
+    const int hg = u % ngroups, half = h_lo + u / ngroups;  // hg = head * PIECES + group
+    const int s0 = max(o0, 8 * half), s1 = min(o1, 8 * half + 8);  // the half's new slots
+    uint4 vx[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int f = f0 + e;  // (head, d) = (f / D, f % D)
-      uint16_t* dst = vpage + (int64_t)(f / D) * PAGE + (f % D) * kBlock;
-      uint32_t w[kVGroup];
+    for (int j = 0; j < 8; ++j) {
+      const int o = 8 * half + j;
+      const bool in = vin_range && o >= s0 && o < s1;
+      vx[j] = buffer_load16(vin, in ? (uint32_t)((o - o0) * hd + hg * 8) * 2 : kOffNone);
+    }
+    // the page id is first used here, after the loads: the empty asm keeps
+    // the compiler from moving that use (and its wait) ahead of them
+    int page = blk;
+    asm volatile("" : "+s"(page));
+    const auto kout = make_page_rsrc(k_cache + (int64_t)page * (num_kv_heads * PAGE), page_bytes);
+    const auto vout = make_page_rsrc(v_cache + (int64_t)page * (num_kv_heads * PAGE), page_bytes);
 #pragma unroll
-      for (int j = 0; j < kVGroup; ++j) {
-        const uint32_t word = e < 2 ? x[j].x : e < 4 ? x[j].y : e < 6 ? x[j].z : x[j].w;
-        w[j] = (word >> (16 * (e & 1))) & 0xFFFFu;
+    for (int j = 0; j < 8; ++j) buffer_store16(kx[j], kout, kdst[j]);
+    // row (head, 8 group + k) of the page, slots 8 half .. 8 half + 7
+    const uint32_t vrow = (uint32_t)(hg * 8 * kBlock + 8 * half) * 2;
+    if (s1 - s0 == 8) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // output dword m holds slots 2m, 2m+1 of value k
+        const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          w[m] = __builtin_amdgcn_perm(dword(vx[2 * m + 1], k >> 1), dword(vx[2 * m], k >> 1), sel);
+        buffer_store16(make_uint4(w[0], w[1], w[2], w[3]), vout,
+                       vin_range ? vrow + k * kBlock * 2 : kOffNone);
       }
-      if (whole) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16),
-                                                    w[4] | (w[5] << 16), w[6] | (w[7] << 16));
-      } else {
+    } else if (vin_range) {
+      // a partly new half: the new slots' 2-byte values alone
 #pragma unroll
-        for (int j = 0; j < kVGroup; ++j)
-          if (j >= lo && j < lo + nnew) dst[j] = (uint16_t)w[j];
+      for (int j = 0; j < 8; ++j) {
+        const int o = 8 * half + j;
+        if (o >= s0 && o < s1) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) buffer_store2((uint16_t)elem16(vx[j], k), vout, vrow + (k * kBlock + j) * 2);
+        }
       }
     }
   }
@@ -237,17 +216,20 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* qs
                          const int32_t* ctx, const int32_t* bt, int bt_stride, int num_seqs,
                          int num_tokens, int num_kv_heads, int head_dim, void* k_cache,
                          void* v_cache, hipStream_t stream) {
-  dim3 grid((num_tokens + kAppendWaves - 1) / kAppendWaves), block(64 * kAppendWaves);
+  // a row of n new tokens touches at most ceil(n / 16) + 1 pages
+  const int64_t tasks = (int64_t)num_tokens / kBlock + 2LL * num_seqs;
+  if (tasks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tasks), block(kAppendThreads);
   const auto* kn = static_cast<const uint16_t*>(k_new);
   const auto* vn = static_cast<const uint16_t*>(v_new);
   auto* kc = static_cast<uint16_t*>(k_cache);
   auto* vc = static_cast<uint16_t*>(v_cache);
   if (head_dim == 128)
     hipLaunchKernelGGL(append_kernel<128>, grid, block, 0, stream, kn, vn, qsl, ctx, bt, bt_stride,
-                       num_seqs, num_tokens, num_kv_heads, kc, vc);
+                       num_seqs, num_kv_heads, kc, vc);
   else
     hipLaunchKernelGGL(append_kernel<64>, grid, block, 0, stream, kn, vn, qsl, ctx, bt, bt_stride,
-                       num_seqs, num_tokens, num_kv_heads, kc, vc);
+                       num_seqs, num_kv_heads, kc, vc);
   return hipGetLastError();
 }
 

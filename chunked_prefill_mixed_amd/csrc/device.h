@@ -11,6 +11,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -61,6 +62,15 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 template <int POLICY = 0>
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
+}
+// Stores of 16 and 2 bytes at byte offset off; a store past the range is
+// dropped by the hardware, so an offset of kOffNone skips it without a branch.
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ void buffer_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store2(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
 // 16 bytes per lane from global memory straight into LDS
