@@ -1,7 +1,7 @@
 """Multi-step replay of a long prompt arriving among streaming requests, on
 one MI355X, attention part only.
 
-Two scenarios from the pages, each run over its own knob:
+Three scenarios from the pages, each run over its own knob:
 
 * ``budget`` -- "Chunked Prefill" (deepconcepts.dev), "Why a chunk can be
   nearly free" and "The budget points in two directions": 32 running decode
@@ -13,6 +13,16 @@ Two scenarios from the pages, each run over its own knob:
   size against time to first token and worst streaming pause): three
   streaming requests and one 8000-token prompt, swept over the chunk size C
   (budget 3 + C, so the prompt gets C tokens a step; 8003 = unchunked).
+
+* ``knee`` -- one step, not a replay: the budget scenario's 32 streams plus
+  one chunk of C tokens after a cached prefix (0, 1024, 4096), C swept from
+  16 to 4096.  It gives the attention-only analogs of two of the pages'
+  figures: the memory-to-compute knee ("How Chunked Prefill Stops Decode
+  Starvation", "Why 512 is the sweet spot": on the A100 a kernel turns from
+  memory- to compute-bound at a few hundred tokens) and the
+  free-ride capacity ("Chunked Prefill", "Why a chunk can be nearly free":
+  the prefill tokens whose compute fits in the time a decode pass spends
+  reading memory).  ``knee_figures`` states how each is derived.
 
 For every knob value the whole sequence of steps runs through the library
 (cpa_build_metadata, cpa_append_kv, cpa_attention on one stream; the
@@ -30,7 +40,7 @@ step), the stall above the undisturbed gap (longest step minus the
 decode-only step), the tokens the streams receive meanwhile (streams x
 steps) and the time to first token against the unchunked run.
 
-    python -m chunked_prefill_mixed_amd.sweep [--scenario budget|chunk]
+    python -m chunked_prefill_mixed_amd.sweep [--scenario budget|chunk|knee]
                                               [--values ...] [--out FILE]
 
 Inputs are seeded and synthetic (workloads.py recipe): stream contexts
@@ -42,6 +52,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import sys
 from dataclasses import dataclass
 
@@ -137,12 +148,14 @@ def replay_figures(times, decode_only, streams, ttft_unchunked=None) -> dict:
 class _Gpu:
     """The run's pool and packed inputs in HBM, and one timed step."""
 
-    def __init__(self, scn: Scenario, contexts, max_steps: int, max_budget: int):
+    def __init__(self, scn: Scenario, contexts, max_steps: int, max_budget: int,
+                 prompt_cached: int = 0):
         import torch
         self.torch = torch
         n = len(contexts)
         reach = [int(c) + max_steps + 1 for c in contexts] + [scn.prompt]
-        reqs = _requests(contexts, 0, 0, scn.prompt)
+        # the prompt's first prompt_cached positions hold values in the pool
+        reqs = _requests(contexts, 0, prompt_cached, scn.prompt)
         st = workloads._streams(scn.seed, 99)
         w = workloads.build(f"replay_{scn.name}", scn.seed, 99, num_q_heads=HQ, num_kv_heads=HKV,
                             head_dim=D, token_budget=max_budget, long_prefill_cap=0,
@@ -248,15 +261,152 @@ def run(scenario: str = "budget", values=None, out_path=None) -> list:
     return rows
 
 
+# ---------------------------------------------------------------------------
+# Knee and free-ride figures: one step of 32 streams plus one chunk of C
+# tokens at a fixed prefix, swept over C.
+# ---------------------------------------------------------------------------
+
+KNEE_SIZES = (16, 32, 64, 128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096)
+KNEE_PREFIXES = (0, 1024, 4096)
+HBM_PEAK = 8.0e12        # B/s, MI355X
+MFMA_BF16_PEAK = 2.5e15  # dense bf16 FLOP/s, MI355X
+FREE_RIDE_SLACK = 0.10   # "free": the step grows by at most this fraction
+
+
+def chunk_flops(c: int, prefix: int, hq: int = HQ, d: int = D) -> float:
+    """Attention flops of a chunk of c queries after `prefix` cached tokens:
+    query j sees prefix + j + 1 keys, 2 d flops each for QK^T and for PV."""
+    return 4.0 * d * hq * (c * prefix + c * (c + 1) / 2)
+
+
+def decode_kv_bytes(contexts, hkv: int = HKV, d: int = D) -> float:
+    """K and V bytes the decode rows read: (context + 1) keys and values each."""
+    return float(sum((int(c) + 1) * hkv * d * 2 * 2 for c in contexts))
+
+
+def tokens_for_flops(flops: float, prefix: int, hq: int = HQ, d: int = D) -> float:
+    """The chunk size c (real) whose chunk_flops(c, prefix) equals flops."""
+    a = 4.0 * d * hq
+    # a (c prefix + c (c + 1) / 2) = flops  ->  c^2 / 2 + c (prefix + 1/2) - flops / a = 0
+    b = prefix + 0.5
+    return -b + math.sqrt(b * b + 2.0 * flops / a)
+
+
+def knee_figures(sizes, step_s, decode_s, prefix: int, decode_bytes: float,
+                 fit_from: int = 1024) -> dict:
+    """Figures of one prefix's sweep.
+
+    step_s[i]: time of the mixed step with a sizes[i]-token chunk; decode_s:
+    the decode-only step at the same contexts.  The chunk's part of the step is
+    x = step - decode.  Above fit_from tokens x is fitted as a + F / R (F the
+    chunk's flops): a is the chunk's fixed cost per step, R its compute rate.
+    The knee is the chunk size where the fitted compute time F / R equals a:
+    below it the step is dominated by fixed costs, above it it grows linearly
+    with the chunk's work.  Free ride, attention only (the pages' free-token
+    estimate with the decode's KV read in place of the weights and the chunk's
+    attention flops in place of 2 x params per token): the chunk tokens whose
+    flops fit in the decode's HBM time decode_bytes / 8 TB/s at the bf16 MFMA
+    peak, the same with the measured rate R and the measured decode-only step,
+    and, as run (decode and chunk back to back), the largest chunk that keeps
+    the step within FREE_RIDE_SLACK of the decode-only step."""
+    sizes = np.asarray(sizes, dtype=np.int64)
+    x = np.asarray(step_s, dtype=np.float64) - decode_s
+    flops = np.array([chunk_flops(int(c), prefix) for c in sizes])
+    sel = sizes >= fit_from
+    if sel.sum() < 2:
+        raise ValueError("need two chunk sizes at or above fit_from")
+    slope, a = np.polyfit(flops[sel], x[sel], 1)
+    rate = 1.0 / slope if slope > 0 else float("nan")  # no rate if time does not grow
+    t_mem = decode_bytes / HBM_PEAK
+    free_peak = tokens_for_flops(t_mem * MFMA_BF16_PEAK, prefix)
+    if rate > 0:
+        knee = tokens_for_flops(max(a, 0.0) * rate, prefix)
+        free_rate = tokens_for_flops(decode_s * rate, prefix)
+    else:
+        knee = free_rate = float("nan")
+    ok = sizes[np.asarray(step_s) <= (1.0 + FREE_RIDE_SLACK) * decode_s]
+    return {"prefix": prefix, "fixed_us": a * 1e6, "rate_tflops": rate * 1e-12,
+            "knee_tokens": knee, "decode_hbm_us": t_mem * 1e6,
+            "free_ride_peak_tokens": free_peak, "free_ride_measured_rate_tokens": free_rate,
+            "free_ride_as_run_tokens": int(ok.max()) if ok.size else 0}
+
+
+def run_knee(sizes=KNEE_SIZES, prefixes=KNEE_PREFIXES, reps: int = 15, out_path=None) -> list:
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("the knee sweep needs a GPU (the HIP library has no CPU path)")
+    cpa.load()
+    sizes = sorted(sizes)
+    prompt = max(prefixes) + max(sizes)
+    scn = Scenario("knee", NUM_STREAMS, prompt, 512, 4096, 1004, tuple(sizes), "chunk")
+    contexts = stream_contexts(scn.seed, scn.streams, scn.ctx_lo, scn.ctx_hi)
+    gpu = _Gpu(scn, contexts, 1, NUM_STREAMS + max(sizes), prompt_cached=max(prefixes))
+    n = scn.streams
+
+    def meta_for(prefix, c):
+        reqs = _requests(contexts, 0, prefix, prefix + c)
+        return cpa.cpa_build_metadata(reqs, token_budget=n + c, long_prefill_cap=0,
+                                      num_q_heads=HQ, num_kv_heads=HKV, head_dim=D)
+
+    def timed(meta):
+        # the same step again: the append rewrites the same slots with the same bits
+        for _ in range(3):
+            gpu.step(meta)
+        return float(np.median([gpu.step(meta) for _ in range(reps)]))
+
+    dec = timed(_decode_only(contexts, 0)[1])
+    dbytes = decode_kv_bytes(contexts)
+    rows, figs = [], []
+    for p in prefixes:
+        times = [timed(meta_for(p, c)) for c in sizes]
+        for c, t in zip(sizes, times):
+            x = t - dec
+            row = {"scenario": "knee", "prefix": p, "chunk_tokens": c, "step_us": t * 1e6,
+                   "decode_only_us": dec * 1e6, "chunk_part_us": x * 1e6,
+                   "chunk_gflop": chunk_flops(c, p) * 1e-9,
+                   "chunk_part_tflops": chunk_flops(c, p) / x * 1e-12 if x > 0 else None}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+        fig = knee_figures(sizes, times, dec, p, dbytes)
+        figs.append(fig)
+        print(json.dumps(fig), flush=True)
+    lines = [f"scenario knee: {n} streams (contexts U[512, 4096], decode K/V read "
+             f"{dbytes / 1e6:.1f} MB) + one chunk of C tokens after a cached prefix; Hq={HQ} "
+             f"Hkv={HKV} D={D} bf16; append + attention per step, median of {reps}",
+             f"decode-only step {dec * 1e6:.1f} us",
+             "prefix  chunk   step_us  chunk_part_us  chunk_GFLOP  chunk_part_TFLOP/s"]
+    for r in rows:
+        tf = f"{r['chunk_part_tflops']:18.1f}" if r["chunk_part_tflops"] else f"{'-':>18}"
+        lines.append(f"{r['prefix']:6d} {r['chunk_tokens']:6d} {r['step_us']:9.1f} "
+                     f"{r['chunk_part_us']:14.1f} {r['chunk_gflop']:12.2f} {tf}")
+    lines.append("")
+    lines.append("prefix  fixed_us  rate_TFLOP/s  knee_tokens  decode_HBM_us  "
+                 "free_ride@peak  free_ride@rate  free_ride_as_run(+10%)")
+    for f in figs:
+        lines.append(f"{f['prefix']:6d} {f['fixed_us']:9.1f} {f['rate_tflops']:13.1f} "
+                     f"{f['knee_tokens']:12.0f} {f['decode_hbm_us']:14.1f} "
+                     f"{f['free_ride_peak_tokens']:15.0f} {f['free_ride_measured_rate_tokens']:15.0f} "
+                     f"{f['free_ride_as_run_tokens']:23d}")
+    text = "\n".join(lines)
+    print(text, file=sys.stderr)
+    if out_path:
+        with open(out_path, "w") as fh:
+            fh.write(text + "\n")
+    return rows + figs
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--scenario", choices=sorted(SCENARIOS), default="budget")
+    ap.add_argument("--scenario", choices=sorted(SCENARIOS) + ["knee"], default="budget")
     ap.add_argument("--values", type=int, nargs="+", default=None,
                     help="budgets (budget scenario) or chunk sizes (chunk scenario)")
     ap.add_argument("--budgets", type=int, nargs="+", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--out", default=None, help="also write the table to this file")
     args = ap.parse_args()
-    run(args.scenario, args.values or args.budgets, args.out)
+    if args.scenario == "knee":
+        run_knee(args.values or KNEE_SIZES, out_path=args.out)
+    else:
+        run(args.scenario, args.values or args.budgets, args.out)
 
 
 if __name__ == "__main__":
