@@ -5,7 +5,7 @@
 // and "The payoff"; tbr8.org deep dive section 1), and the two touch
 // different output rows and partial slots, so nothing orders them inside the
 // step.  Launched as one grid, a CU runs a decode workgroup beside a chunk
-// workgroup (at head_dim 128 both fit two per CU: 230 VGPRs per lane, 64 KB
+// workgroup (at head_dim 128 both fit two per CU: 225 VGPRs per lane, 64 KB
 // of LDS), and the kernel boundary between them goes away.  The caller uses
 // it only when the chunk tiles alone fill a resident round (mixed_slots).
 //
