@@ -13,6 +13,18 @@ Two kinds of record, both written from the CSV files rocprofv3 leaves behind:
   kernel, ``profiles/<kernel>_<workload>_counters.json``, carrying the hash of
   the library sources it was taken on; ``bench.py`` reports the traffic only
   while that hash still matches.
+* ``mfma``: matrix-core and LDS use per kernel from one counter run with
+  ``--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+  SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_ANY SQ_WAVE_CYCLES
+  SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace``, one text section per
+  workload appended to the output file.  Derived per dispatch, then averaged:
+  clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy =
+  SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); issued bf16
+  flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS busy = SQ_LDS_IDX_ACTIVE /
+  (GRBM_GUI_ACTIVE / 8 x 256 CUs); issue wait = SQ_WAIT_INST_ANY /
+  SQ_WAVE_CYCLES (both in 4-cycle units).  The bench's MFMA-only loop
+  (``mfma_kernel``) in the same run is the matrix-core ceiling under the same
+  clock and power limits.
 
 Usage::
 
@@ -20,6 +32,8 @@ Usage::
     python -m chunked_prefill_mixed_amd.counters traffic --workload heavy_mixed \\
         --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv \\
         --out-dir profiles --command "..."
+    python -m chunked_prefill_mixed_amd.counters mfma --workload heavy_mixed \\
+        --csv PMC.csv --out OUT.txt --command "..." [--algorithmic-gflop X]
 """
 
 from __future__ import annotations
@@ -170,6 +184,77 @@ def traffic_record(kernel: str, workload: str, profiles_dir: str) -> dict | None
     return rec
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_IDX_ACTIVE",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+NUM_XCDS, NUM_SIMDS, NUM_CUS = 8, 1024, 256
+
+
+def mfma_summary(path: str) -> dict:
+    """{kernel name: {derived figure: mean over its dispatches}} from one
+    counter run (see the module docstring for the formulas)."""
+    per = defaultdict(lambda: defaultdict(float))
+    meta = {}
+    for r in _rows(path):
+        key = r["Dispatch_Id"]
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        meta[key] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9)
+    acc = defaultdict(lambda: defaultdict(list))
+    for key, c in per.items():
+        name, dur = meta[key]
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / NUM_XCDS
+        if cyc <= 0 or dur <= 0:
+            continue
+        a = acc[name]
+        a["us"].append(dur * 1e6)
+        a["ghz"].append(cyc / dur / 1e9)
+        a["mfma_busy"].append(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * NUM_SIMDS))
+        flops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        a["gflop"].append(flops / 1e9)
+        a["tflops"].append(flops / dur / 1e12)
+        a["lds_busy"].append(c.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cyc * NUM_CUS))
+        a["lds_conflict"].append(c.get("SQ_LDS_BANK_CONFLICT", 0.0))
+        w = c.get("SQ_WAVE_CYCLES", 0.0)
+        a["issue_wait"].append(c.get("SQ_WAIT_INST_ANY", 0.0) / w if w else 0.0)
+    return {name: {k: statistics.fmean(v) for k, v in a.items()} | {"dispatches": len(a["us"])}
+            for name, a in acc.items()}
+
+
+def write_mfma(workload: str, path: str, out: str, command: str,
+               algorithmic_gflop: float | None = None) -> None:
+    """Append the workload's section to out (the file starts with the
+    command and the formulas when it is new)."""
+    summ = mfma_summary(path)
+    lines = []
+    if not os.path.exists(out):
+        lines += [f"command: {command}",
+                  "source: pmc_counter_collection.csv of rocprofv3, counters summed over their "
+                  "instances per dispatch, figures averaged over each kernel's dispatches",
+                  "derived: clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); issued GFLOP = "
+                  "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS busy = SQ_LDS_IDX_ACTIVE / "
+                  "(GRBM_GUI_ACTIVE / 8 x 256 CUs); issue wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; "
+                  "busy x GHz compares matrix-core work per second across kernels at their own "
+                  "clocks; mfma_kernel is the bench's MFMA-only loop on random operands",
+                  ""]
+    alg = f"; algorithmic chunk GFLOP per launch {algorithmic_gflop:.1f}" if algorithmic_gflop else ""
+    lines += [f"workload {workload}{alg}",
+              f"  {'kernel':34s} {'disp':>4s} {'avg_us':>9s} {'GHz':>5s} {'MFMA':>6s} {'busyxGHz':>8s} "
+              f"{'GFLOP':>8s} {'TFLOP/s':>8s} {'LDS':>5s} {'bank_cf':>7s} {'wait':>5s}"]
+    order = sorted(summ.items(), key=lambda kv: -kv[1]["us"] * kv[1]["dispatches"])
+    for name, f in order:
+        if f["us"] < 20:
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")[:34]
+        lines.append(f"  {short:34s} {f['dispatches']:4d} {f['us']:9.1f} {f['ghz']:5.2f} "
+                     f"{100 * f['mfma_busy']:5.1f}% {f['mfma_busy'] * f['ghz']:8.3f} "
+                     f"{f['gflop']:8.1f} {f['tflops']:8.0f} {100 * f['lds_busy']:4.0f}% "
+                     f"{f['lds_conflict']:7.0f} {100 * f['issue_wait']:4.0f}%")
+    lines.append("")
+    with open(out, "a") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -183,9 +268,17 @@ def main():
         c.add_argument("--" + a.replace("_", "-"), required=True, dest=a)
     c.add_argument("--out-dir", required=True)
     c.add_argument("--command", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--workload", required=True)
+    m.add_argument("--csv", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--algorithmic-gflop", type=float, default=None)
     a = ap.parse_args()
     if a.cmd == "trace":
         write_trace(a.csv, a.out, a.command)
+    elif a.cmd == "mfma":
+        write_mfma(a.workload, a.csv, a.out, a.command, a.algorithmic_gflop)
     else:
         for p in write_traffic(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write,
                                a.out_dir, a.command):
