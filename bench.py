@@ -285,9 +285,14 @@ def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, Devi
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
     I = len(insts)
     NEV = len(SPANS) + 2
+    # warm-up: each instance runs its sections once (the first launch of a
+    # kernel on its own pays for loading it, which must not fall into a timed
+    # span), then the one-call steps; a kernel trace of the run thus holds
+    # one untimed launch per instance of each section kernel besides the
+    # timed ones, in the same instance mix
     ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(NEV)]
-    for s in range(warmup):
-        insts[s % I].step(ev_w)
+    for s in range(max(warmup, I)):
+        insts[s % I].step(ev_w if s < I else None)
     torch.cuda.synchronize()
     if graph:
         for inst in insts:
@@ -322,8 +327,11 @@ def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, Devi
 
     def stats(n):
         d = durs[n]
+        by_inst = [[x for x, s in zip(d, sampled) if order[s] == k] for k in range(I)]
         return {"avg_us": sum(d) / len(d), "p10_us": percentile(d, 0.1),
-                "p50_us": percentile(d, 0.5), "p90_us": percentile(d, 0.9)}
+                "p50_us": percentile(d, 0.5), "p90_us": percentile(d, 0.9),
+                # instances in the order of config.instances (their work differs)
+                "per_instance_avg_us": [sum(x) / len(x) if x else None for x in by_inst]}
 
     kernels = {n: stats(n) for n in SPANS}
     for n, unit, scale, peak in (("append_kernel", "GB/s", 1e9, HBM_PEAK_GBS),

@@ -85,25 +85,36 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def trace_summary(path: str) -> dict:
-    """{kernel name: [durations in us]} from a kernel-trace CSV."""
+def trace_summary(path: str, by_grid: bool = False) -> dict:
+    """{kernel name: [durations in us]} from a kernel-trace CSV, or with
+    by_grid {(kernel name, grid size in threads): [durations]}."""
     out = defaultdict(list)
     for r in _rows(path):
         name = r.get("Kernel_Name", "")
         t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        out[name].append((t1 - t0) / 1e3)
+        key = (name, int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)) if by_grid else name
+        out[key].append((t1 - t0) / 1e3)
     return out
 
 
 def write_trace(path: str, out: str, command: str) -> None:
     durs = trace_summary(path)
+    grids = trace_summary(path, by_grid=True)
     lines = [f"command: {command}",
-             "source: rocprofv3 --kernel-trace (csv), durations in microseconds", "",
+             "source: rocprofv3 --kernel-trace (csv), durations in microseconds; a kernel "
+             "launched with several grid sizes (different work) is also listed per grid size, "
+             "in dispatch order", "",
              f"{'kernel':58s} {'calls':>6s} {'mean_us':>10s} {'min_us':>10s} {'median_us':>10s} "
              f"{'max_us':>10s}"]
     for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{name[:58]:58s} {len(d):6d} {statistics.fmean(d):10.2f} {min(d):10.2f} "
                      f"{statistics.median(d):10.2f} {max(d):10.2f}")
+        mine = sorted((g, v) for (n, g), v in grids.items() if n == name)
+        if len(mine) > 1 and short_name(name):
+            for g, v in mine:
+                lines.append(f"  {'grid ' + str(g // 256) + ' workgroups':56s} {len(v):6d} "
+                             f"{statistics.fmean(v):10.2f} {min(v):10.2f} "
+                             f"{statistics.median(v):10.2f} {max(v):10.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
