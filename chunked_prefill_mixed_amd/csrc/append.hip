@@ -12,7 +12,10 @@
 // thread issues all of its loads (up to 8 K pieces and one V unit per round;
 // one round at 8 KV heads of 128) before its first store, and the page id
 // arrives by a scalar load in the meantime, so a task costs about two memory
-// latencies.
+// latencies.  Loads and stores go through buffer resources limited to the
+// task's source rows and to its page: an index past the task reads zero or
+// has its store dropped by the hardware, so the copy has no branches around
+// its memory operations and its waits count exactly the loads it needs.
 //
 // K pages hold their keys in 8-value pieces ([Hkv][D/8][16][8]), so piece c
 // of slot o of head h is 16 bytes at ((h * D/8 + c) * 16 + o) * 16: with the
