@@ -235,7 +235,9 @@ __device__ __forceinline__ void chunk_body(
   // regrouping all MFMAs ahead of all vector work.
   constexpr int kUnitsPerSlot = 16 / (2 * KS);
   static_assert(kUnitsPerSlot * 2 * KS == 16, "16 probability units over the MFMA slots");
-  auto qk_and_probs = [&](f32x16_t (&sn)[2], int kstage, const f32x16_t (&s)[2], float msc) {
+  static_assert(2 * PER_THREAD <= 2 * KS, "a tile's K and V loads fit in the slots");
+  auto qk_and_probs = [&](f32x16_t (&sn)[2], int kstage, const f32x16_t (&s)[2], float msc,
+                          auto&& dma) {
     uint4 ka[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) ka[i] = kfrag(kstage, i);
@@ -250,6 +252,7 @@ __device__ __forceinline__ void chunk_body(
       sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                           __builtin_bit_cast(bf16x8_t, qf[i >> 1]),
                                                           i < 2 ? zero : sn[i & 1], 0, 0, 0);
+      dma(i);
 #pragma unroll
       for (int uu = 0; uu < kUnitsPerSlot; ++uu) {
         const int u = i * kUnitsPerSlot + uu;
@@ -375,12 +378,22 @@ __device__ __forceinline__ void chunk_body(
   auto step = [&](const f32x16_t (&s)[2], f32x16_t (&sn)[2], int64_t (&off_next)[PER_THREAD],
                   int64_t (&off_after)[PER_THREAD], int kt) {
     const int st = (kt - kt0) & 1;
-    if (kt + 2 < n_kv) {
-      page_offsets(kt + 2, off_after);
-      issue_k(off_after, st);  // K(kt) was read in the previous iteration
-    }
-    issue_v(off_next, st ^ 1);  // V(kt-1) likewise
-    qk_and_probs(sn, st ^ 1, s, m * scale_log2);
+    // K(kt+2) into the stage K(kt) used and V(kt+1) into the stage V(kt-1)
+    // used, one 16-byte load per lane in each of the first 2 PER_THREAD
+    // slots, K first: issued all at once after the barrier, the loads of a
+    // CU's 8 waves queued at its address unit and held each wave there for a
+    // fifth of the tile.  Past the piece's last tile the K offsets are those
+    // of page 0, so the spare loads stay inside the pool.
+    page_offsets(kt + 2, off_after);
+    auto dma = [&](int i) {
+      if (i < PER_THREAD)
+        load_lds16(k_head + off_after[i], k_lane_bytes,
+                   lds_address(&k_lds_buf[st][(wave_u * 64 + 256 * i) * 8]));
+      else if (i < 2 * PER_THREAD)
+        load_lds16(v_head + off_next[i - PER_THREAD], v_lane_bytes,
+                   lds_address(&v_lds_buf[st ^ 1][(wave_u * 64 + 256 * (i - PER_THREAD)) * 8]));
+    };
+    qk_and_probs(sn, st ^ 1, s, m * scale_log2, dma);
     rescale_if_needed(s);
     pv(st, false, kt);
     if (kt + 1 >= kt_mask) mask(sn, kt + 1);
