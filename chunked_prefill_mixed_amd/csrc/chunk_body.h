@@ -236,6 +236,9 @@ __device__ __forceinline__ void chunk_body(
   constexpr int kUnitsPerSlot = 16 / (2 * KS);
   static_assert(kUnitsPerSlot * 2 * KS == 16, "16 probability units over the MFMA slots");
   static_assert(2 * PER_THREAD <= 2 * KS, "a tile's K and V loads fit in the slots");
+  // at head_dim 64 the loads stay ahead of the slots: issued from the slots
+  // they cost 2 more VGPRs (170), one workgroup per CU fewer
+  constexpr bool kLoadsInSlots = D > 64;
   auto qk_and_probs = [&](f32x16_t (&sn)[2], int kstage, const f32x16_t (&s)[2], float msc,
                           auto&& dma) {
     uint4 ka[kAhead];
@@ -379,13 +382,23 @@ __device__ __forceinline__ void chunk_body(
                   int64_t (&off_after)[PER_THREAD], int kt) {
     const int st = (kt - kt0) & 1;
     // K(kt+2) into the stage K(kt) used and V(kt+1) into the stage V(kt-1)
-    // used, one 16-byte load per lane in each of the first 2 PER_THREAD
-    // slots, K first: issued all at once after the barrier, the loads of a
-    // CU's 8 waves queued at its address unit and held each wave there for a
-    // fifth of the tile.  Past the piece's last tile the K offsets are those
-    // of page 0, so the spare loads stay inside the pool.
-    page_offsets(kt + 2, off_after);
+    // used.  At head_dim 128 one 16-byte load per lane goes out in each of
+    // the first 2 PER_THREAD slots, K first: issued together right after the
+    // barrier, the 8 loads held the wave for about a fifth of its tile, and
+    // from the slots that time overlaps other waves' matrix work.  Past the
+    // piece's last tile the K offsets are those of page 0, so the spare loads
+    // stay inside the pool.
+    if constexpr (kLoadsInSlots) {
+      page_offsets(kt + 2, off_after);
+    } else {
+      if (kt + 2 < n_kv) {
+        page_offsets(kt + 2, off_after);
+        issue_k(off_after, st);
+      }
+      issue_v(off_next, st ^ 1);
+    }
     auto dma = [&](int i) {
+      if (!kLoadsInSlots) return;
       if (i < PER_THREAD)
         load_lds16(k_head + off_after[i], k_lane_bytes,
                    lds_address(&k_lds_buf[st][(wave_u * 64 + 256 * i) * 8]));
