@@ -25,7 +25,10 @@ whole rounds of instances (the first step of every instance, every
 ``--kernel-event-stride``-th round), which run each plan section as its own
 launch (append, decode, chunk, decode merge, chunk merge) so each kernel has
 its own span; the other steps make the one cpa_attention call and carry no
-events (a marker costs a few microseconds of GPU time between two launches).
+events (a marker costs a few microseconds of GPU time between two launches;
+``empty_span_us`` is the span between two markers with no launch between, the
+part of every kernel span that is not the kernel).  A plan section with no
+entries launches nothing and is reported as ``{"launched": false}``.
 The step rate is the wall clock over all timed steps.
 """
 
@@ -179,14 +182,17 @@ class Instance:
                 P(ds.context_lens))
         zero = dict(num_decode_splits=0, num_decode_merges=0, num_chunk_tiles=0,
                     num_chunk_merges=0)
-        # one plan section per call, so HIP events can bracket each launch
+        # one plan section per call, so HIP events can bracket each launch; a
+        # section with no entries launches nothing and has no span
         self.section_args = {}
+        self.launches = {"append_kernel": ds.num_tokens > 0}
         self._keep = []
         for name, field, sec in (("decode_kernel", "num_decode_splits", "decode_splits"),
                                  ("chunk_kernel", "num_chunk_tiles", "chunk_tiles"),
                                  ("decode_merge", "num_decode_merges", "decode_merges"),
                                  ("chunk_merge", "num_chunk_merges", "chunk_merges")):
             counts = c.copy(**{**zero, field: getattr(c, field)})
+            self.launches[name] = getattr(c, field) > 0
             self._keep.append(counts)
             self.section_args[name] = head + (vp(plan_base + 4 * off[sec]),
                                               ctypes.byref(counts)) + tail
@@ -215,11 +221,13 @@ class Instance:
         self.graph = g
 
     def step(self, events=None):
-        """One full step.  With ``events`` (len(SPANS) + 2 HIP events) every
+        """One full step.  With ``events`` (len(SPANS) + 3 HIP events) every
         launch runs on its own between two of them: events[0] before the
-        metadata copy, events[1 + i] before span i, events[-1] after the
-        last; without, the step is one cpa_attention call (or the replay of
-        the captured graph) and carries no events."""
+        metadata copy, events[1 + i] before span i, events[-2] after the
+        last, and events[-1] right after events[-2] with nothing between
+        (the cost of the markers themselves, which every span also holds);
+        without, the step is one cpa_attention call (or the replay of the
+        captured graph) and carries no events."""
         self.copy_done.synchronize()  # the previous copy out of the pinned buffer is done
         t0 = time.perf_counter()
         self.build_host()
@@ -244,10 +252,13 @@ class Instance:
         st = 0
         for i, name in enumerate(SPANS):
             events[1 + i].record(main)
+            if not self.launches[name]:
+                continue
             if name == "append_kernel":
                 st |= lib.cpa_append_kv(*self.append_args)
             else:
                 st |= lib.cpa_attention(*self.section_args[name])
+        events[-2].record(main)
         events[-1].record(main)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
@@ -284,7 +295,7 @@ def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, Devi
     log(f"config {config} setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
     I = len(insts)
-    NEV = len(SPANS) + 2
+    NEV = len(SPANS) + 3
     # warm-up: each instance runs its sections once (the first launch of a
     # kernel on its own pays for loading it, which must not fall into a timed
     # span), then the one-call steps; a kernel trace of the run thus holds
@@ -316,18 +327,25 @@ def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, Devi
     work = {n: [] for n in SPANS}
     wkey = {"append_kernel": "append_bytes", "decode_kernel": "decode_bytes",
             "chunk_kernel": "chunk_flops", "decode_merge": None, "chunk_merge": None}
-    gpu_step, copy_us = [], []
+    gpu_step, copy_us, gap_us = [], [], []
+    span_steps = {n: [] for n in SPANS}  # the sampled steps in which span n launched
     for s in sampled:
         ev = events[s]
         copy_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
-        gpu_step.append(ev[1].elapsed_time(ev[-1]) * 1e3)
+        gpu_step.append(ev[1].elapsed_time(ev[-2]) * 1e3)
+        gap_us.append(ev[-2].elapsed_time(ev[-1]) * 1e3)
         for i, n in enumerate(SPANS):
+            if not insts[order[s]].launches[n]:
+                continue
+            span_steps[n].append(s)
             durs[n].append(ev[1 + i].elapsed_time(ev[2 + i]) * 1e3)  # us
             work[n].append(insts[order[s]].work[wkey[n]] if wkey[n] else 0)
 
     def stats(n):
         d = durs[n]
-        by_inst = [[x for x, s in zip(d, sampled) if order[s] == k] for k in range(I)]
+        if not d:
+            return {"launched": False}
+        by_inst = [[x for x, s in zip(d, span_steps[n]) if order[s] == k] for k in range(I)]
         return {"avg_us": sum(d) / len(d), "p10_us": percentile(d, 0.1),
                 "p50_us": percentile(d, 0.5), "p90_us": percentile(d, 0.9),
                 # instances in the order of config.instances (their work differs)
@@ -359,6 +377,9 @@ def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, Devi
         "instances": [i.w.name for i in insts],
         "kernels": kernels,
         "gpu_step_us": sum(gpu_step) / len(gpu_step),
+        # two markers back to back with no launch between: what every span
+        # holds besides its kernel
+        "empty_span_us": {"avg": sum(gap_us) / len(gap_us), "p50": percentile(gap_us, 0.5)},
         "metadata_upload_us": sum(copy_us) / len(copy_us),
         "host_build_us": host_us,
         "kernel_events": {"round_stride": stride, "sampled_steps": len(sampled),
@@ -543,7 +564,7 @@ def main():
     kernels = head["kernels"]
     # the dominant kernel of the step: the one with the largest time
     dominant = max(("decode_kernel", "chunk_kernel", "append_kernel"),
-                   key=lambda n: kernels[n]["avg_us"])
+                   key=lambda n: kernels[n].get("avg_us", 0.0))
     if dominant == "chunk_kernel":
         ach = kernels[dominant]["TFLOP/s"]
         roofline = {"bound": "mfma", "kernel": dominant, "achieved": ach,
@@ -571,6 +592,7 @@ def main():
             "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
             "tokens_per_step": r["tokens_per_step"],
             "kernels": {n: {k: v for k, v in d.items()} for n, d in r["kernels"].items()},
+            "empty_span_us": r["empty_span_us"],
         }
 
     peaks = measured_peaks(torch, build_lib)
@@ -604,6 +626,7 @@ def main():
         "kernels": kernels,
         "graph": bool(args.graph),
         "gpu_step_us": head["gpu_step_us"],
+        "empty_span_us": head["empty_span_us"],
         "metadata_upload_us": head["metadata_upload_us"],
         "host_build_us": head["host_build_us"],
         "kernel_events": head["kernel_events"],

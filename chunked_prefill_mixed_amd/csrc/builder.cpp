@@ -12,7 +12,7 @@
 // every wave is resident at once and none reads more pages than needed
 // (lognormal context lengths then balance over the GPU); rows with several
 // pieces get a log-sum-exp merge entry.  Chunk rows are cut into query tiles of
-// kChunkRows/(Hq/Hkv) tokens, ordered longest key range first.
+// chunk_rows(head_dim)/(Hq/Hkv) tokens, ordered longest key range first.
 //
 // Pure host code: no HIP call, safe to run on a machine without a GPU.
 
@@ -98,12 +98,14 @@ int pick_piece_pages(const std::vector<int64_t>& row_pages, int num_kv_heads, in
 // otherwise each tile's keys are cut into ceil(L / S) equal pieces, with S
 // the smallest size (at least kChunkMinSplit) for which all pieces of all KV
 // heads fit one round, so no short tail pieces spill into a second round.
-std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, int num_kv_heads) {
+std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, int num_kv_heads,
+                                       int head_dim) {
+  const int target = cpa::chunk_wg_target(head_dim);
   std::vector<int32_t> n(tile_keys.size(), 1);
-  if ((int64_t)tile_keys.size() * num_kv_heads >= cpa::kChunkWgTarget) return n;
+  if ((int64_t)tile_keys.size() * num_kv_heads >= target) return n;
   int64_t total_keys = 0;
   for (int64_t L : tile_keys) total_keys += L;
-  int64_t S = ceil_div(total_keys * num_kv_heads, cpa::kChunkWgTarget);
+  int64_t S = ceil_div(total_keys * num_kv_heads, target);
   S = std::max<int64_t>(ceil_div(S, cpa::kKvTile) * cpa::kKvTile, cpa::kChunkMinSplit);
   for (;;) {
     int64_t pieces = 0;
@@ -111,7 +113,7 @@ std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, in
       n[t] = (int32_t)std::max<int64_t>(1, ceil_div(tile_keys[t], S));
       pieces += n[t];
     }
-    if (pieces * num_kv_heads <= cpa::kChunkWgTarget) return n;
+    if (pieces * num_kv_heads <= target) return n;
     S += std::max<int64_t>(cpa::kKvTile, S / 16);
   }
 }
@@ -275,11 +277,11 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
                    [](const DPiece& x, const DPiece& y) { return x.ke - x.kb > y.ke - y.kb; });
   for (const DPiece& p : dp) dsplits.insert(dsplits.end(), {p.row, p.kb, p.ke, p.slot});
 
-  // chunk tiles: 128 (token, head) rows of one KV head each.  Keys below
+  // chunk tiles: chunk_rows(head_dim) (token, head) rows of one KV head each.  Keys below
   // context + q_begin are visible to every row of the tile, so a long prefix
   // may be cut into pieces there; the last piece holds the rest, including
   // the causal diagonal.
-  const int tile_tokens = cpa::chunk_tile_tokens(group);
+  const int tile_tokens = cpa::chunk_tile_tokens(group, params->head_dim);
   struct Tile { int32_t row, qb, qe; int64_t prefix, keys; };
   std::vector<Tile> tl;
   for (int s = n_dec; s < nseq; ++s) {
@@ -298,7 +300,7 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   if (!params->chunk_split_tokens) {
     std::vector<int64_t> keys(tl.size());
     for (size_t i = 0; i < tl.size(); ++i) keys[i] = tl[i].keys;
-    auto_n = pick_chunk_pieces(keys, params->num_kv_heads);
+    auto_n = pick_chunk_pieces(keys, params->num_kv_heads, params->head_dim);
   }
   struct Piece { int32_t row, qb, qe, kb, ke, slot; };
   std::vector<Piece> pieces;

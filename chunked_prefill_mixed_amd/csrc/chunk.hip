@@ -1,13 +1,15 @@
-// Prefill-chunk flash attention kernel: one workgroup of 4 waves per work item
-// (128 query rows of one KV head, one piece of its keys).  The body and its
-// design are in chunk_body.h.
+// Prefill-chunk flash attention kernel: one workgroup of chunk_waves(D) waves
+// per work item (32 query rows per wave, all of one KV head, one piece of its
+// keys).  The body and its design are in chunk_body.h.
 
 #include "chunk_body.h"
 
 namespace cpa {
 
+// launch bounds: at least two waves per SIMD (one 8-wave or two 4-wave
+// workgroups per CU), so at most 256 registers per lane
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void chunk_kernel(
+__global__ __launch_bounds__(64 * chunk_waves(D), 8 / chunk_waves(D)) void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
@@ -22,8 +24,8 @@ static void launch_chunk_t(const void* q, const void* kc, const void* vc, const 
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
                            const int32_t* tiles, int num_tiles, int hq, int hkv, float sl2,
                            void* out, float* lse, Partials part, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_kernel<D, G>), dim3(num_tiles * hkv), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+  hipLaunchKernelGGL((chunk_kernel<D, G>), dim3(num_tiles * hkv), dim3(64 * chunk_waves(D)), 0,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), bt, bt_stride, qsl, ctx, tiles, num_tiles,
                      hq, hkv, sl2, static_cast<uint16_t*>(out), lse, part);
 }

@@ -10,9 +10,10 @@
 // ("How Chunked Prefill Stops Decode Starvation", "The payoff"), so with a
 // long prefix this kernel is bound by matrix-core throughput.
 //
-// Workgroup = 4 waves = 128 query rows of one KV head: 128/G tokens times the
-// G query heads that share the KV head (their rows share every K/V tile).
-// Each wave owns 32 rows, one per lane column n = lane % 32.
+// Workgroup = W = chunk_waves(D) waves = 32 W query rows of one KV head (256
+// at head_dim 128, 128 at 64): 32 W / G tokens times the G query heads that
+// share the KV head; all its rows share every K/V tile it loads.  Each wave
+// owns 32 rows, one per lane column n = lane % 32.
 //   S^T[64 keys][32 rows] = K Q^T    v_mfma_f32_32x32x16_bf16, K from LDS (A),
 //                                    Q^T kept in registers (B)
 //   online softmax per row (column) in fp32, P^T rounded to bf16
@@ -31,7 +32,7 @@
 // is doing.  K runs two tiles ahead of its use and V one, in two LDS stages
 // each: iteration t loads K(t+2) into the stage K(t) used and V(t+1) into
 // the stage V(t-1) used, with one barrier per tile.  The loads go straight
-// from memory into LDS (global_load_lds_dwordx4, by all 256 threads, issued
+// from memory into LDS (global_load_lds_dwordx4, by all the threads, issued
 // as inline assembly so the compiler does not make the current tile's LDS
 // reads wait for them).  The lane-to-LDS-slot order of those loads is fixed,
 // so the LDS layout is chosen by which 16 bytes each lane fetches.  K pages
@@ -79,8 +80,11 @@ __device__ __forceinline__ void chunk_body(
   constexpr int DB = D / 32;               // 32-row d blocks of O^T
   constexpr int PAGE = kBlock * D;         // elements of one (page, KV head)
   constexpr int CHUNKS = 4 * PAGE / 8;     // 16-byte pieces per 64-key tile (K or V)
-  constexpr int PER_THREAD = CHUNKS / 256;
-  static_assert(CHUNKS % 256 == 0, "tile must split evenly over 256 threads");
+  constexpr int NT = 64 * chunk_waves(D);  // threads of the workgroup
+  constexpr int ROWS = chunk_rows(D);      // query rows of the workgroup
+  constexpr int PER_THREAD = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
+  static_assert(NT % (PAGE / 8) == 0, "a thread's load slots sit at one place in every page");
 
   // two stages each: K(t+1) is read while K(t+2) is written, V(t) while V(t+1)
   __shared__ __align__(16) uint16_t k_lds_buf[2][kKvTile * D];
@@ -139,7 +143,7 @@ __device__ __forceinline__ void chunk_body(
   };
   int win = kt0 / 16;
   int id_cur = load_window(win), id_next = load_window(win + 1);
-  // Load slot i of this wave covers 16-byte slot p = tid + 256 i of a stage:
+  // Load slot i of this wave covers 16-byte slot p = tid + NT i of a stage:
   // page p / (PAGE / 8) of the tile (the same page for the whole wave) at the
   // same place inside it for every i.  K slot s = p % (PAGE / 8) is the
   // page's own slot s (piece s / 16 of key s % 16); V slot s holds row
@@ -161,7 +165,7 @@ __device__ __forceinline__ void chunk_body(
     }
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
-      const int pg = kt * 4 + (wave_u * 64 + 256 * i) / (PAGE / 8);
+      const int pg = kt * 4 + (wave_u * 64 + NT * i) / (PAGE / 8);
       // page ids are non-negative: an unsigned 32 x 32 -> 64-bit product
       off[i] = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readlane(id_cur, pg & 63) *
                          page_bytes);
@@ -171,13 +175,13 @@ __device__ __forceinline__ void chunk_body(
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i)
       load_lds16(k_head + off[i], k_lane_bytes,
-                 lds_address(&k_lds_buf[stage][(wave_u * 64 + 256 * i) * 8]));
+                 lds_address(&k_lds_buf[stage][(wave_u * 64 + NT * i) * 8]));
   };
   auto issue_v = [&](const int64_t (&off)[PER_THREAD], int stage) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i)
       load_lds16(v_head + off[i], v_lane_bytes,
-                 lds_address(&v_lds_buf[stage][(wave_u * 64 + 256 * i) * 8]));
+                 lds_address(&v_lds_buf[stage][(wave_u * 64 + NT * i) * 8]));
   };
 
   // S^T = K Q^T of the tile in K stage `stage`: two 32-key blocks, their
@@ -384,8 +388,9 @@ __device__ __forceinline__ void chunk_body(
     // K(kt+2) into the stage K(kt) used and V(kt+1) into the stage V(kt-1)
     // used.  At head_dim 128 one 16-byte load per lane goes out in each of
     // the first 2 PER_THREAD slots, K first: issued together right after the
-    // barrier, the 8 loads held the wave for about a fifth of its tile, and
-    // from the slots that time overlaps other waves' matrix work.  Past the
+    // barrier, a tile's loads held the wave for about a fifth of its tile (8
+    // per lane in a 4-wave workgroup), and from the slots that time overlaps
+    // other waves' matrix work.  Past the
     // piece's last tile the K offsets are those of page 0, so the spare loads
     // stay inside the pool.
     if constexpr (kLoadsInSlots) {
@@ -401,10 +406,10 @@ __device__ __forceinline__ void chunk_body(
       if (!kLoadsInSlots) return;
       if (i < PER_THREAD)
         load_lds16(k_head + off_after[i], k_lane_bytes,
-                   lds_address(&k_lds_buf[st][(wave_u * 64 + 256 * i) * 8]));
+                   lds_address(&k_lds_buf[st][(wave_u * 64 + NT * i) * 8]));
       else if (i < 2 * PER_THREAD)
         load_lds16(v_head + off_next[i - PER_THREAD], v_lane_bytes,
-                   lds_address(&v_lds_buf[st ^ 1][(wave_u * 64 + 256 * (i - PER_THREAD)) * 8]));
+                   lds_address(&v_lds_buf[st ^ 1][(wave_u * 64 + NT * (i - PER_THREAD)) * 8]));
     };
     qk_and_probs(sn, st ^ 1, s, m * scale_log2, dma);
     rescale_if_needed(s);
@@ -444,7 +449,7 @@ __device__ __forceinline__ void chunk_body(
   const int hq_out = g * G + (r % G);
   if (row_ok && slot >= 0) {
     // one piece of a split tile: unnormalised partial for merge_kernel
-    const int64_t pr = ((int64_t)slot * num_kv_heads + g) * kChunkRows + r;
+    const int64_t pr = ((int64_t)slot * num_kv_heads + g) * ROWS + r;
     float* acc = part.acc + pr * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

@@ -12,7 +12,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(
     const int32_t* __restrict__ splits, int num_q_heads, int num_kv_heads, int num_items,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials ws) {
   decode_body<D, G>(q, k_cache, v_cache, bt, bt_stride, splits, num_q_heads, num_kv_heads,
-                    num_items, scale_log2, out, lse, ws, blockIdx.x);
+                    num_items, scale_log2, out, lse, ws, blockIdx.x * kDecodeWaves);
 }
 
 template <int D, int G>

@@ -57,14 +57,15 @@ __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ splits, int num_q_heads, int num_kv_heads, int num_items,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials ws, int wg) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials ws,
+    int first_item) {
   constexpr int KK = D / 32;  // S^T steps over d
   constexpr int MB = D / 16;  // O^T blocks of 16 d rows
   constexpr int PAGE_BYTES = kBlock * D * 2;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int item = wg * kDecodeWaves + wave;
+  const int item = first_item + wave;  // wave w of the workgroup takes item first_item + w
   if (item >= num_items) return;  // whole wave; no workgroup barrier below
   const int g = item % num_kv_heads;
   const int4 e = reinterpret_cast<const int4*>(splits)[item / num_kv_heads];

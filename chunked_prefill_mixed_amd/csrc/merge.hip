@@ -91,7 +91,8 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
                                                  float* __restrict__ lse) {
   constexpr int LPR = D / 4;             // lanes per row
   constexpr int RPW = 256 / LPR;         // rows per workgroup
-  constexpr int RG = kChunkRows / RPW;   // workgroups per (merge entry, KV head)
+  constexpr int ROWS = chunk_rows(D);    // rows of a chunk tile and partial slot
+  constexpr int RG = ROWS / RPW;         // workgroups per (merge entry, KV head)
   const int rg = block % RG;
   const int g = (block / RG) % num_kv_heads;
   const int4* ep = reinterpret_cast<const int4*>(merges) + 2 * (block / (RG * num_kv_heads));
@@ -101,8 +102,8 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
   const int r = rg * RPW + threadIdx.x / LPR;
   const int j = qb + r / G;
   if (j >= qe) return;  // past the chunk end
-  const int64_t stride = (int64_t)num_kv_heads * kChunkRows;  // rows between consecutive slots
-  const int64_t base = ((int64_t)first * num_kv_heads + g) * kChunkRows + r;
+  const int64_t stride = (int64_t)num_kv_heads * ROWS;  // rows between consecutive slots
+  const int64_t base = ((int64_t)first * num_kv_heads + g) * ROWS + r;
   const int d = 4 * li;
 
   float M = neg_inf(), L = 0.f;
@@ -163,7 +164,8 @@ hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const in
                          int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
                          float* lse, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
-  const int chunk_blocks = num_chunk_merges * num_kv_heads * (kChunkRows / (256 / (head_dim / 4)));
+  const int chunk_blocks =
+      num_chunk_merges * num_kv_heads * (chunk_rows(head_dim) / (256 / (head_dim / 4)));
   const int pairs = num_decode_merges * num_q_heads;
   const dim3 grid(chunk_blocks + (pairs + 3) / 4), block(256);
   auto* o = static_cast<uint16_t*>(out);

@@ -68,7 +68,7 @@ def test_builder_matches_oracle_on_configs(lib, config):
         got = same_as_oracle(w.requests, w.token_budget, w.long_prefill_cap,
                              Hq=w.num_q_heads, Hkv=w.num_kv_heads, D=w.head_dim,
                              host_block_table=w.block_table, num_blocks=w.num_blocks)
-        check_plan(got, w.num_q_heads // w.num_kv_heads)
+        check_plan(got, w.num_q_heads // w.num_kv_heads, w.head_dim)
         # slot mapping: page * 16 + slot of every scheduled token (checked here
         # with the test's own indexing)
         sm = got["slot_mapping"]
@@ -82,10 +82,15 @@ def test_builder_matches_oracle_on_configs(lib, config):
             break
 
 
-def check_plan(m, group):
+def chunk_rows(head_dim):
+    """(token, head) rows of a chunk tile, as include/cpa.h states them."""
+    return 256 if head_dim == 128 else 128
+
+
+def check_plan(m, group, head_dim):
     """Every decode row's keys are covered exactly once by page-aligned splits;
     merges list exactly the rows with several splits.  Every chunk row's
-    tokens are covered by tiles of 128/G tokens; each tile's keys
+    tokens are covered by tiles of R/G tokens (R rows per tile); each tile's keys
     [0, context + q_end) are covered exactly once by pieces whose inner
     boundaries are 64-key aligned and lie in the fully visible prefix
     (<= context + q_begin); split tiles have a merge entry; pieces come
@@ -114,7 +119,7 @@ def check_plan(m, group):
             assert sorted(p[2] for p in pieces) == list(range(first, first + n))
     assert sorted(slots) == list(range(m["counts"].num_decode_partials))
 
-    tt = 128 // group
+    tt = chunk_rows(head_dim) // group
     tiles = {}
     cslots = []
     for row, qb, qe, kb, ke, slot, z0, z1 in sec["chunk_tiles"]:
@@ -204,7 +209,7 @@ def test_builder_random_mixes_match_oracle(lib):
         csplit = int(rng.choice([0, 0, 64, 256, 1024]))
         m = same_as_oracle(reqs, budget, cap, Hq=G * Hkv, Hkv=Hkv, D=D, decode_split_tokens=split,
                            chunk_split_tokens=csplit)
-        check_plan(m, G)
+        check_plan(m, G, D)
 
 
 @pytest.mark.parametrize("policy", ["truncate", "defer", "quota"])
@@ -236,7 +241,7 @@ def test_builder_policies_match_oracle(lib, policy, adaptive, block_aligned):
             kw["max_prefill_tokens"] = int(rng.choice([1, 64, 1000, 6000]))
         G = int(rng.choice([1, 4, 8]))
         m = same_as_oracle(reqs, budget, cap, Hq=G * 2, Hkv=2, D=128, **kw)
-        check_plan(m, G)
+        check_plan(m, G, 128)
         if policy != "quota":
             assert m["num_tokens"] <= budget
         else:
@@ -385,9 +390,13 @@ def test_builder_valid_block_table_accepted(lib):
 def test_workspace_size(lib):
     up = lambda b: math.ceil(b / 256) * 256
     c = cpa.cpa_plan_counts_t(5, 2, 3, 1, 7, 3)
+    # chunk slots: 8 KV heads x R rows (256 at head_dim 128, 128 at 64)
     want = (up(7 * 32 * 128 * 4) + 2 * up(7 * 32 * 4)
-            + up(3 * 8 * 128 * 128 * 4) + 2 * up(3 * 8 * 128 * 4))
+            + up(3 * 8 * 256 * 128 * 4) + 2 * up(3 * 8 * 256 * 4))
     assert cpa.cpa_workspace_size(c, 32, 8, 128) == want
+    want64 = (up(7 * 32 * 64 * 4) + 2 * up(7 * 32 * 4)
+              + up(3 * 8 * 128 * 64 * 4) + 2 * up(3 * 8 * 128 * 4))
+    assert cpa.cpa_workspace_size(c, 32, 8, 64) == want64
     c0 = cpa.cpa_plan_counts_t(5, 0, 3, 0, 0, 0)
     assert cpa.cpa_workspace_size(c0, 32, 8, 128) == 0
 
@@ -396,10 +405,14 @@ def test_chunk_split_sizes(lib):
     """A small chunk beside a long prefix is cut into pieces (enough work for
     the GPU); a large chunk is not."""
     R = oracle.Request
+    # Hq=32, Hkv=8, D=128: 256-row tiles of 64 tokens
     m = build([R(0, 7680, 8192, False)], 480)
-    assert m["counts"].num_chunk_merges == 15 and m["counts"].num_chunk_tiles > 15
+    assert m["counts"].num_chunk_merges == 8 and m["counts"].num_chunk_tiles > 8
     m = build([R(0, 0, 8192, False)], 8192)
-    assert m["counts"].num_chunk_merges == 0 and m["counts"].num_chunk_tiles == 256
+    assert m["counts"].num_chunk_merges == 0 and m["counts"].num_chunk_tiles == 128
+    # D=64: 128-row tiles of 32 tokens
+    m = build([R(0, 7680, 8192, False)], 480, D=64)
+    assert m["counts"].num_chunk_merges == 15 and m["counts"].num_chunk_tiles > 15
     m = build([R(0, 7680, 8192, False)], 480, chunk_split_tokens=1 << 30)
     assert m["counts"].num_chunk_merges == 0
 
