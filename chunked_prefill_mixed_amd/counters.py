@@ -87,12 +87,14 @@ def _rows(path):
 
 def trace_summary(path: str, by_grid: bool = False) -> dict:
     """{kernel name: [durations in us]} from a kernel-trace CSV, or with
-    by_grid {(kernel name, grid size in threads): [durations]}."""
+    by_grid {(kernel name, grid size in workgroups): [durations]}."""
     out = defaultdict(list)
     for r in _rows(path):
         name = r.get("Kernel_Name", "")
         t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        key = (name, int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)) if by_grid else name
+        threads = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+        wg = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 1)
+        key = (name, threads // max(1, wg)) if by_grid else name
         out[key].append((t1 - t0) / 1e3)
     return out
 
@@ -102,8 +104,8 @@ def write_trace(path: str, out: str, command: str) -> None:
     grids = trace_summary(path, by_grid=True)
     lines = [f"command: {command}",
              "source: rocprofv3 --kernel-trace (csv), durations in microseconds; a kernel "
-             "launched with several grid sizes (different work) is also listed per grid size, "
-             "in dispatch order", "",
+             "launched with several grid sizes (different work) is also listed per grid size "
+             "(workgroups)", "",
              f"{'kernel':58s} {'calls':>6s} {'mean_us':>10s} {'min_us':>10s} {'median_us':>10s} "
              f"{'max_us':>10s}"]
     for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
@@ -112,7 +114,7 @@ def write_trace(path: str, out: str, command: str) -> None:
         mine = sorted((g, v) for (n, g), v in grids.items() if n == name)
         if len(mine) > 1 and short_name(name):
             for g, v in mine:
-                lines.append(f"  {'grid ' + str(g // 256) + ' workgroups':56s} {len(v):6d} "
+                lines.append(f"  {'grid ' + str(g) + ' workgroups':56s} {len(v):6d} "
                              f"{statistics.fmean(v):10.2f} {min(v):10.2f} "
                              f"{statistics.median(v):10.2f} {max(v):10.2f}")
     with open(out, "w") as f:
