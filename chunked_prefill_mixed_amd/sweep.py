@@ -213,8 +213,12 @@ def run(scenario: str = "budget", values=None, out_path=None) -> list:
     max_steps = max(len(p) for p in plans.values())
     gpu = _Gpu(scn, contexts, max_steps, max(scn.budget(v) for v in values))
     n = scn.streams
-    for _, meta in plans[values[0]][:3]:  # warm-up, then reset the pool
-        gpu.step(meta)
+    # warm-up: the first steps of every run and a decode-only step, so each
+    # kernel the runs launch is loaded before a timed step; then reset the pool
+    for v in values:
+        for _, meta in plans[v][:3]:
+            gpu.step(meta)
+    gpu.step(_decode_only(contexts, 0)[1])
     runs = {}
     for v in values:
         gpu.reset()
