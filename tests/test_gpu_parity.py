@@ -124,6 +124,23 @@ def test_wide_head_counts(case):
     check_step(w, decode_split_tokens=split, label=f"wide{case}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_chunk_tile_edges(G, D):
+    """Chunks one token short of, exactly at and one past the query tile of
+    256 (token, head) rows at head_dim 128 (128 at 64), i.e. 256/G tokens,
+    and one of two tiles plus a token, at every head grouping; one chunk
+    after a 3000-token prefix, so the few tiles of the step are cut into key
+    pieces and merged.  Every token of every row matches the oracle."""
+    rows = 256 if D == 128 else 128
+    T = rows // G
+    chunks = [(0, max(1, T - 1)), (0, T), (3000, 3000 + T + 1), (5, 5 + 2 * T + 1)]
+    w = workloads.random_workload(1500 + 10 * G + D, num_q_heads=2 * G, num_kv_heads=2,
+                                  head_dim=D, decode_ctx=[10, 700], chunks=chunks)
+    ds, _ = check_step(w, label=f"tile edges G{G} D{D}")
+    assert ds.counts.num_chunk_merges > 0  # the prefixed chunk's tiles were split
+
+
 def test_empty_step_touches_nothing():
     """num_tokens = 0: both device calls return CPA_OK without a launch, and
     the cache and the output buffer keep their bits."""
