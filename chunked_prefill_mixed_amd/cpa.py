@@ -66,8 +66,7 @@ POLICY_NAMES = {"truncate": CPA_POLICY_TRUNCATE, "defer": CPA_POLICY_DEFER,
 class cpa_plan_counts_t(ctypes.Structure):
     _fields_ = [("num_decode_splits", ctypes.c_int32), ("num_decode_merges", ctypes.c_int32),
                 ("num_chunk_tiles", ctypes.c_int32), ("num_chunk_merges", ctypes.c_int32),
-                ("num_decode_partials", ctypes.c_int32), ("num_chunk_partials", ctypes.c_int32),
-                ("chunk_tile_rows", ctypes.c_int32)]
+                ("num_decode_partials", ctypes.c_int32), ("num_chunk_partials", ctypes.c_int32)]
 
     def copy(self, **changes):
         vals = {f: getattr(self, f) for f, _ in self._fields_}

@@ -60,8 +60,6 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
   if (n.num_decode_splits < 0 || n.num_decode_merges < 0 || n.num_chunk_tiles < 0 ||
       n.num_chunk_merges < 0 || n.num_decode_partials < 0 || n.num_chunk_partials < 0)
     return CPA_ERR_INVALID;
-  const int rows = cpa::plan_chunk_rows(n.chunk_tile_rows, head_dim);
-  if (rows == 0) return CPA_ERR_INVALID;
   if (num_tokens == 0) return CPA_OK;
   if (!q || !k_cache || !v_cache || !d_block_table || !d_query_start_loc || !d_context_lens ||
       !d_plan || !out)
@@ -69,7 +67,7 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
   if (!(softmax_scale > 0.f)) return CPA_ERR_INVALID;
   const cpa::WorkspaceLayout wl =
       cpa::workspace_layout(n.num_decode_partials, n.num_chunk_partials, num_q_heads, num_kv_heads,
-                            head_dim, rows);
+                            head_dim);
   if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total)) return CPA_ERR_CAPACITY;
 
   hipStream_t s = (hipStream_t)stream;
@@ -91,12 +89,12 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
   // present and the chunk tiles fill a resident round); the merges (one
   // launch) follow them
   const bool mixed = n.num_decode_splits > 0 &&
-                     (int64_t)n.num_chunk_tiles * num_kv_heads >= cpa::mixed_slots(head_dim, rows);
+                     (int64_t)n.num_chunk_tiles * num_kv_heads >= cpa::mixed_slots(head_dim);
   if (mixed) {
     st = status_of(cpa::launch_mixed(q, k_cache, v_cache, d_block_table, bt_stride,
                                      d_query_start_loc, d_context_lens, tiles, n.num_chunk_tiles,
                                      splits, n.num_decode_splits, num_q_heads, num_kv_heads,
-                                     head_dim, rows, sl2, out, lse, cws, dws, s));
+                                     head_dim, sl2, out, lse, cws, dws, s));
     if (st != CPA_OK) return st;
   } else if (n.num_decode_splits > 0) {
     st = status_of(cpa::launch_decode(q, k_cache, v_cache, d_block_table, bt_stride,
@@ -107,14 +105,13 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
   if (!mixed && n.num_chunk_tiles > 0) {
     st = status_of(cpa::launch_chunk(q, k_cache, v_cache, d_block_table, bt_stride,
                                      d_query_start_loc, d_context_lens, tiles, n.num_chunk_tiles,
-                                     num_q_heads, num_kv_heads, head_dim, rows, sl2, out, lse, cws,
-                                     s));
+                                     num_q_heads, num_kv_heads, head_dim, sl2, out, lse, cws, s));
     if (st != CPA_OK) return st;
   }
   if (n.num_decode_merges > 0 || n.num_chunk_merges > 0) {
     st = status_of(cpa::launch_merges(dmerges, n.num_decode_merges, cmerges, n.num_chunk_merges,
-                                      d_query_start_loc, num_q_heads, num_kv_heads, head_dim,
-                                      rows, dws, cws, out, lse, s));
+                                      d_query_start_loc, num_q_heads, num_kv_heads, head_dim, dws,
+                                      cws, out, lse, s));
     if (st != CPA_OK) return st;
   }
   return CPA_OK;
@@ -166,11 +163,9 @@ extern "C" int cpa_attention_noalloc(const void* q, const void* k_cache, const v
   if (st != CPA_OK) return st;
   if (!counts || counts->num_decode_partials < 0 || counts->num_chunk_partials < 0)
     return CPA_ERR_INVALID;
-  const int rows = cpa::plan_chunk_rows(counts->chunk_tile_rows, head_dim);
-  if (rows == 0) return CPA_ERR_INVALID;
   const cpa::WorkspaceLayout wl =
       cpa::workspace_layout(counts->num_decode_partials, counts->num_chunk_partials, num_q_heads,
-                            num_kv_heads, head_dim, rows);
+                            num_kv_heads, head_dim);
   if (wl.total > kScratchBytes) return CPA_ERR_CAPACITY;
   void* ws = nullptr;
   if (wl.total > 0 && num_tokens > 0) {

@@ -12,8 +12,7 @@
 // every wave is resident at once and none reads more pages than needed
 // (lognormal context lengths then balance over the GPU); rows with several
 // pieces get a log-sum-exp merge entry.  Chunk rows are cut into query tiles of
-// R/(Hq/Hkv) tokens (R the tile rows the step uses), ordered longest key range
-// first.
+// chunk_rows(head_dim)/(Hq/Hkv) tokens, ordered longest key range first.
 //
 // Pure host code: no HIP call, safe to run on a machine without a GPU.
 
@@ -100,8 +99,8 @@ int pick_piece_pages(const std::vector<int64_t>& row_pages, int num_kv_heads, in
 // the smallest size (at least kChunkMinSplit) for which all pieces of all KV
 // heads fit one round, so no short tail pieces spill into a second round.
 std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, int num_kv_heads,
-                                       int rows) {
-  const int target = cpa::chunk_wg_target(rows);
+                                       int head_dim) {
+  const int target = cpa::chunk_wg_target(head_dim);
   std::vector<int32_t> n(tile_keys.size(), 1);
   if ((int64_t)tile_keys.size() * num_kv_heads >= target) return n;
   int64_t total_keys = 0;
@@ -278,26 +277,11 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
                    [](const DPiece& x, const DPiece& y) { return x.ke - x.kb > y.ke - y.kb; });
   for (const DPiece& p : dp) dsplits.insert(dsplits.end(), {p.row, p.kb, p.ke, p.slot});
 
-  // Rows of a chunk tile: 256 at head_dim 128 (one 8-wave workgroup per CU,
-  // all its rows sharing each K/V tile load) unless the step's 256-row tiles
-  // would make at least one and fewer than two resident rounds with no key
-  // split: there a CU whose one tile ends early idles until the round's
-  // longest tile ends, and 128-row tiles, two workgroups per CU (a long tile
-  // beside a shorter one), balance the round better.  128 at head_dim 64.
-  int rows = cpa::default_chunk_rows(params->head_dim);
-  if (rows == 256) {
-    int64_t t256 = 0;
-    for (int s = n_dec; s < nseq; ++s) t256 += ceil_div(out->num_scheduled[s], 256 / group);
-    t256 *= params->num_kv_heads;
-    const int round = cpa::chunk_wg_target(256);
-    if (t256 >= round && t256 < 2 * round) rows = 128;
-  }
-  out->counts.chunk_tile_rows = rows;
-  // chunk tiles: `rows` (token, head) rows of one KV head each.  Keys below
+  // chunk tiles: chunk_rows(head_dim) (token, head) rows of one KV head each.  Keys below
   // context + q_begin are visible to every row of the tile, so a long prefix
   // may be cut into pieces there; the last piece holds the rest, including
   // the causal diagonal.
-  const int tile_tokens = cpa::chunk_tile_tokens(group, rows);
+  const int tile_tokens = cpa::chunk_tile_tokens(group, params->head_dim);
   struct Tile { int32_t row, qb, qe; int64_t prefix, keys; };
   std::vector<Tile> tl;
   for (int s = n_dec; s < nseq; ++s) {
@@ -316,7 +300,7 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   if (!params->chunk_split_tokens) {
     std::vector<int64_t> keys(tl.size());
     for (size_t i = 0; i < tl.size(); ++i) keys[i] = tl[i].keys;
-    auto_n = pick_chunk_pieces(keys, params->num_kv_heads, rows);
+    auto_n = pick_chunk_pieces(keys, params->num_kv_heads, params->head_dim);
   }
   struct Piece { int32_t row, qb, qe, kb, ke, slot; };
   std::vector<Piece> pieces;
@@ -377,11 +361,9 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
 extern "C" size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads,
                                      int num_kv_heads, int head_dim) {
   if (!counts || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-  const int rows = cpa::plan_chunk_rows(counts->chunk_tile_rows, head_dim);
-  if (rows == 0) return 0;
   const cpa::WorkspaceLayout w =
       cpa::workspace_layout(counts->num_decode_partials, counts->num_chunk_partials, num_q_heads,
-                            num_kv_heads, head_dim, rows);
+                            num_kv_heads, head_dim);
   return w.total;
 }
 

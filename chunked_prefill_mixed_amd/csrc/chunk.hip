@@ -1,5 +1,5 @@
-// Prefill-chunk flash attention kernel: one workgroup of ROWS / 32 waves per
-// work item (32 query rows per wave, all of one KV head, one piece of its
+// Prefill-chunk flash attention kernel: one workgroup of chunk_waves(D) waves
+// per work item (32 query rows per wave, all of one KV head, one piece of its
 // keys).  The body and its design are in chunk_body.h.
 
 #include "chunk_body.h"
@@ -8,23 +8,23 @@ namespace cpa {
 
 // launch bounds: at least two waves per SIMD (one 8-wave or two 4-wave
 // workgroups per CU), so at most 256 registers per lane
-template <int D, int G, int ROWS>
-__global__ __launch_bounds__(2 * ROWS, 256 / ROWS) void chunk_kernel(
+template <int D, int G>
+__global__ __launch_bounds__(64 * chunk_waves(D), 8 / chunk_waves(D)) void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ tiles, int num_tiles, int num_q_heads, int num_kv_heads,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials part) {
-  chunk_body<D, G, ROWS>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,
-                         num_q_heads, num_kv_heads, scale_log2, out, lse, part, blockIdx.x);
+  chunk_body<D, G>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles, num_q_heads,
+                   num_kv_heads, scale_log2, out, lse, part, blockIdx.x);
 }
 
-template <int D, int G, int ROWS>
+template <int D, int G>
 static void launch_chunk_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
                            const int32_t* tiles, int num_tiles, int hq, int hkv, float sl2,
                            void* out, float* lse, Partials part, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_kernel<D, G, ROWS>), dim3(num_tiles * hkv), dim3(2 * ROWS), 0,
+  hipLaunchKernelGGL((chunk_kernel<D, G>), dim3(num_tiles * hkv), dim3(64 * chunk_waves(D)), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), bt, bt_stride, qsl, ctx, tiles, num_tiles,
                      hq, hkv, sl2, static_cast<uint16_t*>(out), lse, part);
@@ -33,18 +33,17 @@ static void launch_chunk_t(const void* q, const void* kc, const void* vc, const 
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-                        int head_dim, int rows, float scale_log2, void* out, float* lse,
-                        Partials part, hipStream_t stream) {
+                        int head_dim, float scale_log2, void* out, float* lse, Partials part,
+                        hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
-#define CPA_CHK(DD, GG, RR)                                                                    \
-  if (head_dim == DD && G == GG && rows == RR) {                                                \
-    launch_chunk_t<DD, GG, RR>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,  \
-                               num_q_heads, num_kv_heads, scale_log2, out, lse, part, stream);  \
+#define CPA_CHK(DD, GG)                                                                        \
+  if (head_dim == DD && G == GG) {                                                              \
+    launch_chunk_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,      \
+                           num_q_heads, num_kv_heads, scale_log2, out, lse, part, stream);      \
     return hipGetLastError();                                                                   \
   }
-  CPA_CHK(128, 1, 256) CPA_CHK(128, 2, 256) CPA_CHK(128, 4, 256) CPA_CHK(128, 8, 256)
-  CPA_CHK(128, 1, 128) CPA_CHK(128, 2, 128) CPA_CHK(128, 4, 128) CPA_CHK(128, 8, 128)
-  CPA_CHK(64, 1, 128) CPA_CHK(64, 2, 128) CPA_CHK(64, 4, 128) CPA_CHK(64, 8, 128)
+  CPA_CHK(128, 1) CPA_CHK(128, 2) CPA_CHK(128, 4) CPA_CHK(128, 8)
+  CPA_CHK(64, 1) CPA_CHK(64, 2) CPA_CHK(64, 4) CPA_CHK(64, 8)
 #undef CPA_CHK
   return hipErrorInvalidValue;
 }

@@ -10,10 +10,10 @@
 // ("How Chunked Prefill Stops Decode Starvation", "The payoff"), so with a
 // long prefix this kernel is bound by matrix-core throughput.
 //
-// Workgroup = ROWS / 32 waves = ROWS query rows of one KV head (ROWS = 256 or
-// 128 at head_dim 128, 128 at 64): ROWS / G tokens times the G query heads
-// that share the KV head; all its rows share every K/V tile it loads.  Each
-// wave owns 32 rows, one per lane column n = lane % 32.
+// Workgroup = W = chunk_waves(D) waves = 32 W query rows of one KV head (256
+// at head_dim 128, 128 at 64): 32 W / G tokens times the G query heads that
+// share the KV head; all its rows share every K/V tile it loads.  Each wave
+// owns 32 rows, one per lane column n = lane % 32.
 //   S^T[64 keys][32 rows] = K Q^T    v_mfma_f32_32x32x16_bf16, K from LDS (A),
 //                                    Q^T kept in registers (B)
 //   online softmax per row (column) in fp32, P^T rounded to bf16
@@ -69,7 +69,7 @@
 namespace cpa {
 
 // The work of chunk workgroup wg (one work item of the XCD-remapped order).
-template <int D, int G, int ROWS>
+template <int D, int G>
 __device__ __forceinline__ void chunk_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
@@ -80,7 +80,8 @@ __device__ __forceinline__ void chunk_body(
   constexpr int DB = D / 32;               // 32-row d blocks of O^T
   constexpr int PAGE = kBlock * D;         // elements of one (page, KV head)
   constexpr int CHUNKS = 4 * PAGE / 8;     // 16-byte pieces per 64-key tile (K or V)
-  constexpr int NT = 64 * chunk_waves(ROWS);  // threads of the workgroup
+  constexpr int NT = 64 * chunk_waves(D);  // threads of the workgroup
+  constexpr int ROWS = chunk_rows(D);      // query rows of the workgroup
   constexpr int PER_THREAD = CHUNKS / NT;
   static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
   static_assert(NT % (PAGE / 8) == 0, "a thread's load slots sit at one place in every page");

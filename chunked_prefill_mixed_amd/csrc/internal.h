@@ -25,26 +25,25 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
                          int head_dim, float scale_log2, void* out, float* lse, Partials ws,
                          hipStream_t stream);
 
-// rows: (token, head) rows of the plan's chunk tiles (128 or 256)
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-                        int head_dim, int rows, float scale_log2, void* out, float* lse,
-                        Partials part, hipStream_t stream);
+                        int head_dim, float scale_log2, void* out, float* lse, Partials part,
+                        hipStream_t stream);
 
 // Decode pieces and chunk tiles of one step in one launch (mixed.hip); both
 // counts > 0.
 hipError_t launch_mixed(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, const int32_t* splits, int num_splits,
-                        int num_q_heads, int num_kv_heads, int head_dim, int rows,
-                        float scale_log2, void* out, float* lse, Partials cpart, Partials dpart,
+                        int num_q_heads, int num_kv_heads, int head_dim, float scale_log2,
+                        void* out, float* lse, Partials cpart, Partials dpart,
                         hipStream_t stream);
 
 // Both merges of a step in one launch (either count may be 0).
 hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const int32_t* cmerges,
                          int num_chunk_merges, const int32_t* qsl, int num_q_heads,
-                         int num_kv_heads, int head_dim, int rows, Partials dws, Partials cws,
-                         void* out, float* lse, hipStream_t stream);
+                         int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
+                         float* lse, hipStream_t stream);
 
 }  // namespace cpa

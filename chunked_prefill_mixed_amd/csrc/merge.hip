@@ -83,7 +83,7 @@ __device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ me
 // a running max, sum and output as in the decode merge.
 constexpr int kChunkMergeBatch = 8;
 
-template <int D, int G, int ROWS>
+template <int D, int G>
 __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ merges, int block,
                                                  const int32_t* __restrict__ qsl, int num_q_heads,
                                                  int num_kv_heads, const Partials& part,
@@ -91,8 +91,8 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
                                                  float* __restrict__ lse) {
   constexpr int LPR = D / 4;             // lanes per row
   constexpr int RPW = 256 / LPR;         // rows per workgroup
-  constexpr int RG = ROWS / RPW;         // workgroups per (merge entry, KV head); ROWS:
-                                         // rows of a chunk tile and partial slot
+  constexpr int ROWS = chunk_rows(D);    // rows of a chunk tile and partial slot
+  constexpr int RG = ROWS / RPW;         // workgroups per (merge entry, KV head)
   const int rg = block % RG;
   const int g = (block / RG) % num_kv_heads;
   const int4* ep = reinterpret_cast<const int4*>(merges) + 2 * (block / (RG * num_kv_heads));
@@ -143,14 +143,13 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
   if (lse && li == 0) lse[(int64_t)(t0 + j) * num_q_heads + hq] = (M + __log2f(L)) * kLn2;
 }
 
-template <int D, int G, int ROWS>
+template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(
     const int32_t* __restrict__ dmerges, int num_decode_pairs, const int32_t* __restrict__ cmerges,
     int chunk_blocks, const int32_t* __restrict__ qsl, int num_q_heads, int num_kv_heads,
     Partials dws, Partials cws, uint16_t* __restrict__ out, float* __restrict__ lse) {
   if ((int)blockIdx.x < chunk_blocks) {
-    merge_chunk_rows<D, G, ROWS>(cmerges, blockIdx.x, qsl, num_q_heads, num_kv_heads, cws, out,
-                                 lse);
+    merge_chunk_rows<D, G>(cmerges, blockIdx.x, qsl, num_q_heads, num_kv_heads, cws, out, lse);
     return;
   }
   // four (decode row, query head) pairs per workgroup, one per wave
@@ -162,23 +161,22 @@ __global__ __launch_bounds__(256) void merge_kernel(
 
 hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const int32_t* cmerges,
                          int num_chunk_merges, const int32_t* qsl, int num_q_heads,
-                         int num_kv_heads, int head_dim, int rows, Partials dws, Partials cws,
-                         void* out, float* lse, hipStream_t stream) {
+                         int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
+                         float* lse, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
-  const int chunk_blocks = num_chunk_merges * num_kv_heads * (rows / (256 / (head_dim / 4)));
+  const int chunk_blocks =
+      num_chunk_merges * num_kv_heads * (chunk_rows(head_dim) / (256 / (head_dim / 4)));
   const int pairs = num_decode_merges * num_q_heads;
   const dim3 grid(chunk_blocks + (pairs + 3) / 4), block(256);
   auto* o = static_cast<uint16_t*>(out);
-#define CPA_MRG(DD, GG, RR)                                                                    \
-  if (head_dim == DD && G == GG && rows == RR) {                                                \
-    hipLaunchKernelGGL((merge_kernel<DD, GG, RR>), grid, block, 0, stream, dmerges, pairs,      \
-                       cmerges, chunk_blocks, qsl, num_q_heads, num_kv_heads, dws, cws, o,      \
-                       lse);                                                                    \
+#define CPA_MRG(DD, GG)                                                                        \
+  if (head_dim == DD && G == GG) {                                                              \
+    hipLaunchKernelGGL((merge_kernel<DD, GG>), grid, block, 0, stream, dmerges, pairs, cmerges, \
+                       chunk_blocks, qsl, num_q_heads, num_kv_heads, dws, cws, o, lse);         \
     return hipGetLastError();                                                                   \
   }
-  CPA_MRG(128, 1, 256) CPA_MRG(128, 2, 256) CPA_MRG(128, 4, 256) CPA_MRG(128, 8, 256)
-  CPA_MRG(128, 1, 128) CPA_MRG(128, 2, 128) CPA_MRG(128, 4, 128) CPA_MRG(128, 8, 128)
-  CPA_MRG(64, 1, 128) CPA_MRG(64, 2, 128) CPA_MRG(64, 4, 128) CPA_MRG(64, 8, 128)
+  CPA_MRG(128, 1) CPA_MRG(128, 2) CPA_MRG(128, 4) CPA_MRG(128, 8)
+  CPA_MRG(64, 1) CPA_MRG(64, 2) CPA_MRG(64, 4) CPA_MRG(64, 8)
 #undef CPA_MRG
   return hipErrorInvalidValue;
 }

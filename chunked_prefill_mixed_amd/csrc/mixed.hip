@@ -5,15 +5,14 @@
 // and "The payoff"; tbr8.org deep dive section 1), and the two touch
 // different output rows and partial slots, so nothing orders them inside the
 // step.  Launched as one grid, the kernel boundary between them goes away.
-// Every workgroup has the chunk workgroup's ROWS / 32 waves; a decode
+// Every workgroup has the chunk workgroup's chunk_waves(D) waves; a decode
 // workgroup runs one (piece, KV head) item per wave, as the decode kernel's
 // do.  The caller uses it only when the chunk tiles alone fill a resident
 // round (mixed_slots).
 //
 // Which part comes first in the grid (workgroups are dispatched in order):
-// when the decode workgroups fit one resident round of this kernel
-// (mixed_slots: one or two workgroups per CU at head_dim 128, by the tile
-// rows, three at 64), they go first and start
+// when the decode workgroups fit one resident round of this kernel (one
+// workgroup per CU at head_dim 128, three at 64), they go first and start
 // together while the chunk tiles take the other slots and then the slots the
 // decode frees; otherwise the chunk tiles go first and the decode pieces fill
 // the slots that the chunk's last round leaves idle.  The decode count is
@@ -25,8 +24,8 @@
 
 namespace cpa {
 
-template <int D, int G, int ROWS>
-__global__ __launch_bounds__(2 * ROWS, 256 / ROWS) void mixed_kernel(
+template <int D, int G>
+__global__ __launch_bounds__(64 * chunk_waves(D), 8 / chunk_waves(D)) void mixed_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
@@ -41,25 +40,24 @@ __global__ __launch_bounds__(2 * ROWS, 256 / ROWS) void mixed_kernel(
   if (is_decode)
     decode_body<D, G>(q, k_cache, v_cache, bt, bt_stride, splits, num_q_heads, num_kv_heads,
                       num_items, scale_log2, out, lse, dpart,
-                      (decode_lead ? w : w - chunk_wgs) * chunk_waves(ROWS));
+                      (decode_lead ? w : w - chunk_wgs) * chunk_waves(D));
   else
-    chunk_body<D, G, ROWS>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,
-                           num_q_heads, num_kv_heads, scale_log2, out, lse, cpart,
-                           w - decode_lead);
+    chunk_body<D, G>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles, num_q_heads,
+                     num_kv_heads, scale_log2, out, lse, cpart, w - decode_lead);
 }
 
-template <int D, int G, int ROWS>
+template <int D, int G>
 static void launch_mixed_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
                            const int32_t* tiles, int num_tiles, const int32_t* splits,
                            int num_splits, int hq, int hkv, float sl2, void* out, float* lse,
                            Partials cpart, Partials dpart, hipStream_t stream) {
   const int items = num_splits * hkv;
-  constexpr int W = chunk_waves(ROWS);  // decode items per workgroup
+  constexpr int W = chunk_waves(D);  // decode items per workgroup
   const int decode_wgs = (items + W - 1) / W;
-  const int decode_lead = decode_wgs <= mixed_slots(D, ROWS) ? (decode_wgs + 7) / 8 * 8 : 0;
+  const int decode_lead = decode_wgs <= mixed_slots(D) ? (decode_wgs + 7) / 8 * 8 : 0;
   const int wgs = num_tiles * hkv + (decode_lead ? decode_lead : decode_wgs);
-  hipLaunchKernelGGL((mixed_kernel<D, G, ROWS>), dim3(wgs), dim3(64 * W), 0, stream,
+  hipLaunchKernelGGL((mixed_kernel<D, G>), dim3(wgs), dim3(64 * W), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), bt, bt_stride, qsl, ctx, tiles, num_tiles,
                      splits, items, hq, hkv, sl2, static_cast<uint16_t*>(out), lse, cpart, dpart,
@@ -69,20 +67,19 @@ static void launch_mixed_t(const void* q, const void* kc, const void* vc, const 
 hipError_t launch_mixed(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, const int32_t* splits, int num_splits,
-                        int num_q_heads, int num_kv_heads, int head_dim, int rows,
-                        float scale_log2, void* out, float* lse, Partials cpart, Partials dpart,
+                        int num_q_heads, int num_kv_heads, int head_dim, float scale_log2,
+                        void* out, float* lse, Partials cpart, Partials dpart,
                         hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
-#define CPA_MIX(DD, GG, RR)                                                                    \
-  if (head_dim == DD && G == GG && rows == RR) {                                                \
-    launch_mixed_t<DD, GG, RR>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,  \
-                               splits, num_splits, num_q_heads, num_kv_heads, scale_log2, out,  \
-                               lse, cpart, dpart, stream);                                      \
+#define CPA_MIX(DD, GG)                                                                        \
+  if (head_dim == DD && G == GG) {                                                              \
+    launch_mixed_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,      \
+                           splits, num_splits, num_q_heads, num_kv_heads, scale_log2, out, lse, \
+                           cpart, dpart, stream);                                               \
     return hipGetLastError();                                                                   \
   }
-  CPA_MIX(128, 1, 256) CPA_MIX(128, 2, 256) CPA_MIX(128, 4, 256) CPA_MIX(128, 8, 256)
-  CPA_MIX(128, 1, 128) CPA_MIX(128, 2, 128) CPA_MIX(128, 4, 128) CPA_MIX(128, 8, 128)
-  CPA_MIX(64, 1, 128) CPA_MIX(64, 2, 128) CPA_MIX(64, 4, 128) CPA_MIX(64, 8, 128)
+  CPA_MIX(128, 1) CPA_MIX(128, 2) CPA_MIX(128, 4) CPA_MIX(128, 8)
+  CPA_MIX(64, 1) CPA_MIX(64, 2) CPA_MIX(64, 4) CPA_MIX(64, 8)
 #undef CPA_MIX
   return hipErrorInvalidValue;
 }

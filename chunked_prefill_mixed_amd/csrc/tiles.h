@@ -6,21 +6,15 @@ namespace cpa {
 constexpr int kBlock = 16;          // tokens per KV page
 constexpr int kKvTile = 64;         // keys per LDS-staged K/V tile in the chunk kernel (4 pages)
 
-// (token, head) query rows of a chunk tile, workgroup and partial slot: 32
-// per wave, all sharing every K/V tile the workgroup loads into LDS.  At
-// head_dim 128 the kernel's registers allow two waves per SIMD: 256 rows (8
-// waves) fill a CU with one workgroup and share each tile load (half the
-// loads per matrix operation), or 128 rows (4 waves) put two workgroups on a
-// CU.  At 64 they allow three, and three 128-row workgroups per CU fill it.
-constexpr int default_chunk_rows(int head_dim) { return head_dim > 64 ? 256 : 128; }
-// The rows a plan's chunk_tile_rows field selects (0: the head_dim's
-// default); 0 when the head_dim does not allow the value.
-inline int plan_chunk_rows(int field, int head_dim) {
-  if (field == 0) return default_chunk_rows(head_dim);
-  if (field == 128 || (field == 256 && head_dim > 64)) return field;
-  return 0;
-}
-constexpr int chunk_waves(int rows) { return rows / 32; }
+// Waves of one chunk workgroup, each owning 32 (token, head) query rows; all
+// of them share every K/V tile the workgroup loads into LDS.  At head_dim 128
+// the kernel's registers allow two waves per SIMD, so 8 waves fill a CU with
+// one workgroup, whose 256 rows then share each tile load (half the loads per
+// matrix operation of two 4-wave workgroups).  At 64 they allow three, and
+// three 4-wave workgroups per CU fill it.
+constexpr int chunk_waves(int head_dim) { return head_dim > 64 ? 8 : 4; }
+// (token, head) query rows of one chunk workgroup, tile and partial slot
+constexpr int chunk_rows(int head_dim) { return 32 * chunk_waves(head_dim); }
 // Decode waves per launch round: one per SIMD of the 256 CUs.  The kernel's
 // registers would allow 3 waves per SIMD at head_dim 128 and 5 at 64, but
 // longer pieces at one wave per SIMD read as fast or faster (less start-up
@@ -35,22 +29,19 @@ constexpr int kDecodeMaxSplit = 64 * kBlock;  // a decode split spans at most 64
 constexpr int kChunkMinSplit = 256;       // fewest prefix keys worth a separate chunk piece
 
 // Chunk workgroups the planner aims at when it cuts tiles into key pieces:
-// one resident round of 256-row workgroups (one per CU); 512 of 128 rows.
-inline int chunk_wg_target(int rows) { return rows == 256 ? 256 : 512; }
+// one resident round at head_dim 128 (one workgroup per CU); 512 at 64.
+inline int chunk_wg_target(int head_dim) { return head_dim > 64 ? 256 : 512; }
 
-// Resident workgroups of the chunk kernel and of the mixed launch on 256 CUs:
-// one per CU with 256-row tiles, two with 128-row tiles at head_dim 128,
-// three at 64.  A step runs its decode pieces and chunk tiles as one launch
-// only when the chunk tiles alone fill a round: then decode workgroups either
-// run beside them or fill the slots their last round leaves idle.  With fewer
-// chunk tiles the two run as separate launches, which measured as fast or
-// faster there.
-inline int mixed_slots(int head_dim, int rows) {
-  return 256 * (rows == 256 ? 1 : head_dim > 64 ? 2 : 3);
-}
+// Resident workgroups of the chunk kernel and of the mixed launch (one per CU
+// at head_dim 128, three at 64, on 256 CUs).  A step runs its decode pieces
+// and chunk tiles as one launch only when the chunk tiles alone fill a round:
+// then decode workgroups either run beside them or fill the slots their last
+// round leaves idle.  With fewer chunk tiles the two run as separate
+// launches, which measured as fast or faster there.
+inline int mixed_slots(int head_dim) { return 256 * (head_dim > 64 ? 1 : 3); }
 
 // Query tokens one chunk workgroup covers when G query heads share a KV head.
-inline int chunk_tile_tokens(int group, int rows) { return rows / group; }
+inline int chunk_tile_tokens(int group, int head_dim) { return chunk_rows(head_dim) / group; }
 
 inline bool supported_group(int group) {
   return group == 1 || group == 2 || group == 4 || group == 8;
@@ -70,19 +61,19 @@ namespace cpa {
 
 // Byte offsets of the fp32 partial-result regions inside the caller's
 // workspace.  Decode slot: acc [Hq][D], m [Hq], l [Hq].  Chunk slot: acc
-// [Hkv][R rows][D], m and l [Hkv][R], R the plan's chunk tile rows.  Max
-// values are stored in log2 units of the scaled score.
+// [Hkv][R rows][D], m and l [Hkv][R], R = chunk_rows(D).  Max values are
+// stored in log2 units of the scaled score.
 struct WorkspaceLayout {
   size_t dec_acc, dec_m, dec_l, chk_acc, chk_m, chk_l, total;
 };
 
 inline WorkspaceLayout workspace_layout(int64_t dec_slots, int64_t chk_slots, int num_q_heads,
-                                        int num_kv_heads, int head_dim, int rows) {
+                                        int num_kv_heads, int head_dim) {
   auto up = [](int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); };
   WorkspaceLayout w;
   size_t at = 0;
   const int64_t dr = dec_slots * num_q_heads;
-  const int64_t cr = chk_slots * num_kv_heads * rows;
+  const int64_t cr = chk_slots * num_kv_heads * chunk_rows(head_dim);
   w.dec_acc = at; at += up(dr * head_dim * 4);
   w.dec_m = at;   at += up(dr * 4);
   w.dec_l = at;   at += up(dr * 4);

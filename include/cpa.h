@@ -146,13 +146,9 @@ typedef struct {
  * int32 array of four sections, in this order: num_decode_splits entries of
  * CPA_DECODE_SPLIT_WORDS, num_chunk_tiles of CPA_CHUNK_TILE_WORDS,
  * num_decode_merges of CPA_DECODE_MERGE_WORDS, num_chunk_merges of
- * CPA_CHUNK_MERGE_WORDS (the two merge sections run as one launch).  A chunk tile covers R =
- * chunk_tile_rows (token, query head) rows of one KV head: R / (num_q_heads /
- * num_kv_heads) tokens.  R is 128 at head_dim 64; at head_dim 128 the planner
- * takes 256 (one 8-wave workgroup per CU, its rows sharing every K/V tile
- * load) unless 256-row tiles would make at least one and fewer than two
- * resident rounds of 256 workgroups unsplit, where 128 (two 4-wave
- * workgroups per CU) balances unequal tiles better. */
+ * CPA_CHUNK_MERGE_WORDS (the two merge sections run as one launch).  A chunk tile covers R
+ * (token, query head) rows of one KV head, R = 256 at head_dim 128 and 128 at
+ * head_dim 64: R / (num_q_heads / num_kv_heads) tokens. */
 typedef struct {
   int32_t num_decode_splits;   /* one wave per (split, KV head) */
   int32_t num_decode_merges;   /* decode rows whose keys were split in several pieces */
@@ -160,8 +156,6 @@ typedef struct {
   int32_t num_chunk_merges;    /* chunk tiles whose prefix keys were split in several pieces */
   int32_t num_decode_partials; /* decode partial slots: num_q_heads x (head_dim + 2) fp32 each */
   int32_t num_chunk_partials;  /* chunk partial slots: num_kv_heads x R x (head_dim + 2) fp32 */
-  int32_t chunk_tile_rows;     /* R: 128 or 256 (256 only at head_dim 128); 0 = 256 at
-                                  head_dim 128, 128 at 64 */
 } cpa_plan_counts_t;
 
 /* Host arrays filled by cpa_build_metadata; the caller provides them with the
@@ -247,9 +241,8 @@ int cpa_append_kv(const void* k_new, const void* v_new, const int32_t* d_query_s
  * plan with these counts: fp32 partial sums plus the running max and sum of
  * every split piece, i.e. (num_decode_partials * num_q_heads +
  * num_chunk_partials * num_kv_heads * R) * (head_dim + 2) * 4 bytes (R, the
- * rows of a chunk tile, from counts->chunk_tile_rows), each region rounded up
- * to 256 bytes.  0 when nothing is split, or when chunk_tile_rows is not one
- * the head_dim allows.
+ * rows of a chunk tile: 256 at head_dim 128, 128 at 64), each region rounded
+ * up to 256 bytes.  0 when nothing is split.
  */
 size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int num_kv_heads,
                           int head_dim);

@@ -281,19 +281,17 @@ def _mixed_case(case):
 
 @pytest.mark.parametrize("case", [3, 4, 5, "d64"])
 def test_one_launch_matches_separate_sections(case):
-    """When the chunk tiles fill a resident round (256 8-wave workgroups or
-    512 4-wave ones at head_dim 128, by the plan's tile rows; 768 4-wave ones
-    at 64), a step runs its decode pieces and chunk tiles as one launch:
-    decode workgroups first when they fit one round (budget-8192,
-    long-context and the head_dim-64 steps), chunk tiles first otherwise
-    (heavy mixed).  The same plan run section by section, one launch each,
-    gives the same bits."""
+    """When the chunk tiles fill a resident round (256 8-wave workgroups at
+    head_dim 128, 768 4-wave ones at 64), a step runs its decode pieces and
+    chunk tiles as one launch: decode workgroups first when they fit one
+    round (budget-8192, long-context and the head_dim-64 steps), chunk tiles
+    first otherwise (heavy mixed).  The same plan run section by section, one
+    launch each, gives the same bits."""
     import torch
     w = _mixed_case(case)
     a = DeviceStep(w, validate=False)
     c = a.counts
-    rows = c.chunk_tile_rows
-    slots = 256 * (1 if rows == 256 else 2 if w.head_dim > 64 else 3)
+    slots = 256 * (1 if w.head_dim > 64 else 3)
     assert c.num_decode_splits > 0 and c.num_chunk_tiles * w.num_kv_heads >= slots
     a.run()
     b = DeviceStep(w, validate=False)

@@ -4,7 +4,6 @@ oracle's scheduler element for element, reproduces the pages' worked
 numbers, reports every error path, and emits a work plan that covers each
 row exactly once."""
 
-import ctypes
 import math
 import os
 import re
@@ -69,7 +68,7 @@ def test_builder_matches_oracle_on_configs(lib, config):
         got = same_as_oracle(w.requests, w.token_budget, w.long_prefill_cap,
                              Hq=w.num_q_heads, Hkv=w.num_kv_heads, D=w.head_dim,
                              host_block_table=w.block_table, num_blocks=w.num_blocks)
-        check_plan(got, w.num_q_heads // w.num_kv_heads, w.head_dim, w.num_kv_heads)
+        check_plan(got, w.num_q_heads // w.num_kv_heads, w.head_dim)
         # slot mapping: page * 16 + slot of every scheduled token (checked here
         # with the test's own indexing)
         sm = got["slot_mapping"]
@@ -83,24 +82,15 @@ def test_builder_matches_oracle_on_configs(lib, config):
             break
 
 
-def expected_chunk_rows(m, group, head_dim, hkv):
-    """The chunk tile rows include/cpa.h says the planner picks: 128 at
-    head_dim 64; at 128, 256 unless the step's 256-row tiles (one per 256/G
-    tokens of each chunk row, per KV head) number at least 256 and fewer than
-    512."""
-    if head_dim == 64:
-        return 128
-    nd = m["num_decodes"]
-    t256 = hkv * sum(-(-int(m["num_scheduled"][s]) // (256 // group))
-                     for s in range(nd, m["num_seqs"]))
-    return 128 if 256 <= t256 < 512 else 256
+def chunk_rows(head_dim):
+    """(token, head) rows of a chunk tile, as include/cpa.h states them."""
+    return 256 if head_dim == 128 else 128
 
 
-def check_plan(m, group, head_dim, hkv):
+def check_plan(m, group, head_dim):
     """Every decode row's keys are covered exactly once by page-aligned splits;
     merges list exactly the rows with several splits.  Every chunk row's
-    tokens are covered by tiles of R/G tokens (R rows per tile, as the header's
-    rule picks them); each tile's keys
+    tokens are covered by tiles of R/G tokens (R rows per tile); each tile's keys
     [0, context + q_end) are covered exactly once by pieces whose inner
     boundaries are 64-key aligned and lie in the fully visible prefix
     (<= context + q_begin); split tiles have a merge entry; pieces come
@@ -129,9 +119,7 @@ def check_plan(m, group, head_dim, hkv):
             assert sorted(p[2] for p in pieces) == list(range(first, first + n))
     assert sorted(slots) == list(range(m["counts"].num_decode_partials))
 
-    rows = m["counts"].chunk_tile_rows
-    assert rows == expected_chunk_rows(m, group, head_dim, hkv)
-    tt = rows // group
+    tt = chunk_rows(head_dim) // group
     tiles = {}
     cslots = []
     for row, qb, qe, kb, ke, slot, z0, z1 in sec["chunk_tiles"]:
@@ -221,7 +209,7 @@ def test_builder_random_mixes_match_oracle(lib):
         csplit = int(rng.choice([0, 0, 64, 256, 1024]))
         m = same_as_oracle(reqs, budget, cap, Hq=G * Hkv, Hkv=Hkv, D=D, decode_split_tokens=split,
                            chunk_split_tokens=csplit)
-        check_plan(m, G, D, Hkv)
+        check_plan(m, G, D)
 
 
 @pytest.mark.parametrize("policy", ["truncate", "defer", "quota"])
@@ -253,7 +241,7 @@ def test_builder_policies_match_oracle(lib, policy, adaptive, block_aligned):
             kw["max_prefill_tokens"] = int(rng.choice([1, 64, 1000, 6000]))
         G = int(rng.choice([1, 4, 8]))
         m = same_as_oracle(reqs, budget, cap, Hq=G * 2, Hkv=2, D=128, **kw)
-        check_plan(m, G, 128, 2)
+        check_plan(m, G, 128)
         if policy != "quota":
             assert m["num_tokens"] <= budget
         else:
@@ -402,21 +390,13 @@ def test_builder_valid_block_table_accepted(lib):
 def test_workspace_size(lib):
     up = lambda b: math.ceil(b / 256) * 256
     c = cpa.cpa_plan_counts_t(5, 2, 3, 1, 7, 3)
-    # chunk slots: 8 KV heads x R rows; chunk_tile_rows 0 = 256 at head_dim 128,
-    # 128 at 64
+    # chunk slots: 8 KV heads x R rows (256 at head_dim 128, 128 at 64)
     want = (up(7 * 32 * 128 * 4) + 2 * up(7 * 32 * 4)
             + up(3 * 8 * 256 * 128 * 4) + 2 * up(3 * 8 * 256 * 4))
     assert cpa.cpa_workspace_size(c, 32, 8, 128) == want
-    assert cpa.cpa_workspace_size(c.copy(chunk_tile_rows=256), 32, 8, 128) == want
-    want128 = (up(7 * 32 * 128 * 4) + 2 * up(7 * 32 * 4)
-               + up(3 * 8 * 128 * 128 * 4) + 2 * up(3 * 8 * 128 * 4))
-    assert cpa.cpa_workspace_size(c.copy(chunk_tile_rows=128), 32, 8, 128) == want128
     want64 = (up(7 * 32 * 64 * 4) + 2 * up(7 * 32 * 4)
               + up(3 * 8 * 128 * 64 * 4) + 2 * up(3 * 8 * 128 * 4))
     assert cpa.cpa_workspace_size(c, 32, 8, 64) == want64
-    # rows the head_dim does not allow: no size
-    assert cpa.cpa_workspace_size(c.copy(chunk_tile_rows=256), 32, 8, 64) == 0
-    assert cpa.cpa_workspace_size(c.copy(chunk_tile_rows=64), 32, 8, 128) == 0
     c0 = cpa.cpa_plan_counts_t(5, 0, 3, 0, 0, 0)
     assert cpa.cpa_workspace_size(c0, 32, 8, 128) == 0
 
@@ -433,35 +413,6 @@ def test_chunk_split_sizes(lib):
     # D=64: 128-row tiles of 32 tokens
     m = build([R(0, 7680, 8192, False)], 480, D=64)
     assert m["counts"].num_chunk_merges == 15 and m["counts"].num_chunk_tiles > 15
-    assert m["counts"].chunk_tile_rows == 128
-
-
-@pytest.mark.parametrize("rows,head_dim,status", [
-    (0, 128, 0), (128, 128, 0), (256, 128, 0), (0, 64, 0), (128, 64, 0),
-    (256, 64, -1), (64, 128, -1), (512, 128, -1), (-128, 128, -1)])
-def test_attention_checks_chunk_tile_rows(lib, rows, head_dim, status):
-    """cpa_attention and its no-allocation variant accept only the tile rows
-    the head_dim allows (CPA_ERR_INVALID otherwise), before anything reaches
-    the GPU: with no tokens a valid call returns CPA_OK without a launch."""
-    assert cpa.CPA_OK == 0 and cpa.CPA_ERR_INVALID == -1
-    counts = cpa.cpa_plan_counts_t(chunk_tile_rows=rows)
-    args = (None, None, None, None, 1, None, None, None, None, ctypes.byref(counts), 0, 0, 0, 8, 2,
-            head_dim, 16, ctypes.c_float(0.125), None, None)
-    assert lib.cpa_attention(*args, None, ctypes.c_size_t(0), None) == status
-    assert lib.cpa_attention_noalloc(*args, None) == status
-
-
-def test_chunk_tile_rows_follow_the_round_rule(lib):
-    """At head_dim 128 a step whose 256-row tiles fill one round but not two
-    (2048 tokens at G=4: 32 tiles x 8 KV heads = 256) gets 128-row tiles; one
-    with two rounds or more (4096 tokens: 512) and one below a round (480
-    tokens: 64, split into pieces) get 256-row tiles."""
-    R = oracle.Request
-    for n, rows, tiles in ((2048, 128, 64), (2047, 128, 64), (4096, 256, 64), (480, 256, None)):
-        m = build([R(0, 0, n, False)], n)
-        assert m["counts"].chunk_tile_rows == rows, n
-        if tiles is not None:
-            assert m["counts"].num_chunk_tiles == tiles and m["counts"].num_chunk_merges == 0, n
     m = build([R(0, 7680, 8192, False)], 480, chunk_split_tokens=1 << 30)
     assert m["counts"].num_chunk_merges == 0
 
