@@ -12,6 +12,8 @@
 // Workgroups [0, chunk_blocks) merge chunk tiles, the rest decode rows, so
 // both merges of a step cost one launch.  Neither part uses a barrier.
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 #include "tiles.h"
@@ -19,11 +21,46 @@
 namespace cpa {
 
 // One wave per (decode row, query head), each lane owning D/64 output
-// dimensions.  Splits are taken kDecodeMergeBatch at a time, every load of a
-// batch (the splits' max and sum, broadcast to all lanes, and this lane's
-// partial values) issued before any is used, so a batch costs one memory
-// round trip; batches fold into a running max, sum and output.
-constexpr int kDecodeMergeBatch = 16;
+// dimensions.  Splits are taken B at a time, every load of a batch (the
+// splits' max and sum, broadcast to all lanes, and this lane's partial
+// values) issued before any is used, so a batch costs one memory round trip;
+// batches fold into a running max, sum and output.  B (4, 8 or 16) is the
+// smallest that takes the row's splits in one batch, so few loads go to the
+// padding entries of a batch.
+template <int D, int B>
+__device__ __forceinline__ void merge_decode_batches(int first, int n, int h, int num_q_heads,
+                                                     const Partials& ws, float& M, float& L,
+                                                     float (&o)[D / 64]) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  for (int i0 = 0; i0 < n; i0 += B) {
+    float mi[B], lv[B], a[B][PER];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const bool in = i0 + i < n;
+      const int64_t ph = (int64_t)(first + (in ? i0 + i : i0)) * num_q_heads + h;
+      mi[i] = in ? ws.m[ph] : neg_inf();
+      lv[i] = ws.l[ph];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) a[i][k] = ws.acc[ph * D + lane + 64 * k];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < B; ++i) Mb = fmaxf(Mb, mi[i]);
+    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
+    L *= alpha;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] *= alpha;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
+      L += w * lv[i];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] += w * a[i][k];
+    }
+    M = Mb;
+  }
+}
 
 template <int D>
 __device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ merges, int entry,
@@ -39,33 +76,12 @@ __device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ me
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kDecodeMergeBatch) {
-    float mi[kDecodeMergeBatch], lv[kDecodeMergeBatch], a[kDecodeMergeBatch][PER];
-#pragma unroll
-    for (int i = 0; i < kDecodeMergeBatch; ++i) {
-      const bool in = i0 + i < n;
-      const int64_t ph = (int64_t)(first + (in ? i0 + i : i0)) * num_q_heads + h;
-      mi[i] = in ? ws.m[ph] : neg_inf();
-      lv[i] = ws.l[ph];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) a[i][k] = ws.acc[ph * D + lane + 64 * k];
-    }
-    float Mb = M;
-#pragma unroll
-    for (int i = 0; i < kDecodeMergeBatch; ++i) Mb = fmaxf(Mb, mi[i]);
-    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
-    L *= alpha;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] *= alpha;
-#pragma unroll
-    for (int i = 0; i < kDecodeMergeBatch; ++i) {
-      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
-      L += w * lv[i];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] += w * a[i][k];
-    }
-    M = Mb;
-  }
+  if (n <= 4)
+    merge_decode_batches<D, 4>(first, n, h, num_q_heads, ws, M, L, o);
+  else if (n <= 8)
+    merge_decode_batches<D, 8>(first, n, h, num_q_heads, ws, M, L, o);
+  else
+    merge_decode_batches<D, 16>(first, n, h, num_q_heads, ws, M, L, o);
   const int t = qsl[row];
   const float inv = 1.f / L;
 #pragma unroll
@@ -76,12 +92,13 @@ __device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ me
 
 // RPW rows of one (chunk merge entry, KV head) per workgroup; each row is
 // handled by LPR = D/4 lanes, each owning 4 consecutive d values, so a partial
-// row is one contiguous sweep.  Pieces are taken kChunkMergeBatch at a time:
-// every lane issues all loads of a batch (each piece's max and sum, the same
-// address for the row's lanes, and its 16 bytes of the piece's partial)
-// before using any, so a batch costs one memory round trip; batches fold into
-// a running max, sum and output as in the decode merge.
-constexpr int kChunkMergeBatch = 8;
+// row is one contiguous sweep.  Pieces are taken B at a time (2, 4 or 8, the
+// smallest that takes the tile's pieces in one batch, up to 8): every lane
+// issues all loads of a batch (each piece's max and sum, the same address for
+// the row's lanes, and its 16 bytes of the piece's partial) before using any,
+// so a batch costs one memory round trip; batches fold into a running max,
+// sum and output as in the decode merge.
+constexpr int kChunkMergeBatch = 8;  // the largest chunk-merge batch
 
 template <int D, int G>
 __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ merges, int block,
@@ -108,31 +125,41 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
 
   float M = neg_inf(), L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < n; i0 += kChunkMergeBatch) {
-    float mi[kChunkMergeBatch], lv[kChunkMergeBatch];
-    float4 a[kChunkMergeBatch];
+  auto batches = [&](auto bsz) {
+    constexpr int B = decltype(bsz)::value;
+    for (int i0 = 0; i0 < n; i0 += B) {
+      float mi[B], lv[B];
+      float4 a[B];
 #pragma unroll
-    for (int i = 0; i < kChunkMergeBatch; ++i) {
-      const bool in = i0 + i < n;
-      const int64_t pr = base + (int64_t)(in ? i0 + i : i0) * stride;
-      mi[i] = in ? part.m[pr] : neg_inf();
-      lv[i] = part.l[pr];
-      a[i] = *reinterpret_cast<const float4*>(part.acc + pr * D + d);
+      for (int i = 0; i < B; ++i) {
+        const bool in = i0 + i < n;
+        const int64_t pr = base + (int64_t)(in ? i0 + i : i0) * stride;
+        mi[i] = in ? part.m[pr] : neg_inf();
+        lv[i] = part.l[pr];
+        a[i] = *reinterpret_cast<const float4*>(part.acc + pr * D + d);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int i = 0; i < B; ++i) Mb = fmaxf(Mb, mi[i]);
+      const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
+      L *= alpha;
+      o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
+        L += w * lv[i];
+        o.x += w * a[i].x; o.y += w * a[i].y; o.z += w * a[i].z; o.w += w * a[i].w;
+      }
+      M = Mb;
     }
-    float Mb = M;
-#pragma unroll
-    for (int i = 0; i < kChunkMergeBatch; ++i) Mb = fmaxf(Mb, mi[i]);
-    const float alpha = fast_exp2(M - Mb);  // 0 on the first batch (M = -inf)
-    L *= alpha;
-    o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
-#pragma unroll
-    for (int i = 0; i < kChunkMergeBatch; ++i) {
-      const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
-      L += w * lv[i];
-      o.x += w * a[i].x; o.y += w * a[i].y; o.z += w * a[i].z; o.w += w * a[i].w;
-    }
-    M = Mb;
-  }
+  };
+  // batch size from the piece count, uniform over the workgroup
+  if (n <= 2)
+    batches(std::integral_constant<int, 2>{});
+  else if (n <= 4)
+    batches(std::integral_constant<int, 4>{});
+  else
+    batches(std::integral_constant<int, kChunkMergeBatch>{});
   const float inv = 1.f / L;
   const int hq = g * G + (r % G);
   const int t0 = qsl[row];
