@@ -43,6 +43,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 from collections import defaultdict
 
@@ -60,16 +61,25 @@ KERNELS = {
 COPY_BYTES = 1 << 30  # bytes bench.py --copy-calibration copies per launch
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments, trailing blanks and empty lines (the
+    library's sources hold no string literal with a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def library_source_hash() -> str:
-    """Hash of every source that shapes what the library's kernels do: the
-    kernels, their launchers and the host work planner (which decides the
-    splits and with them the partial-result traffic).  The bench's own
-    ceiling probes are left out."""
+    """Hash of the code of every source that shapes what the library's
+    kernels do: the kernels, their launchers and the host work planner (which
+    decides the splits and with them the partial-result traffic).  Comments
+    and blank lines are left out, so a record stays valid across changes to
+    them alone; the bench's own ceiling probes are left out."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".h", ".cpp")) and f != "peaks.hip":
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+                h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -51,7 +51,9 @@ constexpr int kStages = CPA_DECODE_STAGES;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// The work of decode workgroup wg (4 waves, items 4 wg .. 4 wg + 3).
+// The work of one decode wave: wave w of the workgroup takes item
+// first_item + w (kDecodeWaves waves per decode-kernel workgroup; the mixed
+// launch's decode workgroups have the chunk workgroup's waves).
 template <int D, int G>
 __device__ __forceinline__ void decode_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,

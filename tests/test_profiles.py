@@ -32,6 +32,14 @@ def test_every_counter_record_matches_the_current_sources():
         assert rec["dispatches"] > 0 and rec["read_bytes_per_launch"] > 0
 
 
+def test_source_hash_sees_code_not_comments():
+    a = "int x = 1;  // one\n/* a block\n   comment */\nint y = 2;\n"
+    b = "int x = 1;\n\n// another comment\nint y = 2;   \n"
+    c = "int x = 1;\nint y = 3;\n"
+    assert counters._code_only(a) == counters._code_only(b)
+    assert counters._code_only(a) != counters._code_only(c)
+
+
 @pytest.mark.parametrize("kernel", ["append_kernel", "decode_kernel", "chunk_kernel",
                                     "merge_kernel"])
 @pytest.mark.parametrize("workload", WORKLOADS)
