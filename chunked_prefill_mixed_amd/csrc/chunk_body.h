@@ -388,11 +388,11 @@ __device__ __forceinline__ void chunk_body(
     // K(kt+2) into the stage K(kt) used and V(kt+1) into the stage V(kt-1)
     // used.  At head_dim 128 one 16-byte load per lane goes out in each of
     // the first 2 PER_THREAD slots, K first: issued together right after the
-    // barrier, a tile's loads held the wave for about a fifth of its tile (8
-    // per lane in a 4-wave workgroup), and from the slots that time overlaps
-    // other waves' matrix work.  Past the
-    // piece's last tile the K offsets are those of page 0, so the spare loads
-    // stay inside the pool.
+    // barrier, a tile's loads held the wave for about a fifth of its tile
+    // (measured at 8 loads per lane, with 4-wave workgroups), and from the
+    // slots that time overlaps other waves' matrix work.  Past the piece's
+    // last tile the K offsets are those of page 0, so the spare loads stay
+    // inside the pool.
     if constexpr (kLoadsInSlots) {
       page_offsets(kt + 2, off_after);
     } else {
