@@ -13,8 +13,8 @@ int check_heads(int num_q_heads, int num_kv_heads, int head_dim, int block_size)
   if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return CPA_ERR_INVALID;
   if (block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
   if (num_q_heads % num_kv_heads) return CPA_ERR_UNSUPPORTED;
-  if (!cpa::supported_group(num_q_heads / num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_head_dim(head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_group(num_q_heads / num_kv_heads, head_dim)) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_kv_heads(num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   return CPA_OK;
 }

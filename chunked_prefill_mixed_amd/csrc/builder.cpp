@@ -35,8 +35,9 @@ int check_params(const cpa_build_params_t* p) {
   if (p->decode_split_tokens < 0 || p->chunk_split_tokens < 0) return CPA_ERR_INVALID;
   if (p->block_size != cpa::kBlock) return CPA_ERR_UNSUPPORTED;
   if (p->num_q_heads % p->num_kv_heads) return CPA_ERR_UNSUPPORTED;
-  if (!cpa::supported_group(p->num_q_heads / p->num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_head_dim(p->head_dim)) return CPA_ERR_UNSUPPORTED;
+  if (!cpa::supported_group(p->num_q_heads / p->num_kv_heads, p->head_dim))
+    return CPA_ERR_UNSUPPORTED;
   if (!cpa::supported_kv_heads(p->num_kv_heads)) return CPA_ERR_UNSUPPORTED;
   if (p->decode_split_tokens % cpa::kBlock || p->decode_split_tokens > cpa::kDecodeMaxSplit)
     return CPA_ERR_INVALID;
@@ -72,16 +73,17 @@ int adaptive_cap(int base_chunk, int num_decodes) {
 // longest wave: pick the fewest rounds k of R waves (R = decode_waves_target,
 // one per SIMD) for which pieces of at most 64 pages exist, then the
 // smallest page count p such that the rows, each cut into ceil(pages/p)
-// pieces, give at most k * R waves (piece x KV head).  Every wave then
+// pieces, give at most k * R waves (piece x KV head x block of 16 query heads
+// of the group, one block for G <= 16).  Every wave then
 // starts in pass 1..k and no wave reads more than p pages.  p is kept at 8 pages or
 // more: a shorter piece is mostly start-up latency and lengthens the merge.
-int pick_piece_pages(const std::vector<int64_t>& row_pages, int num_kv_heads, int head_dim) {
+int pick_piece_pages(const std::vector<int64_t>& row_pages, int waves_per_piece, int head_dim) {
   constexpr int64_t kMinPages = 8;
   const int64_t max_pages = cpa::kDecodeMaxSplit / cpa::kBlock;
   auto waves = [&](int64_t p) {
     int64_t n = 0;
     for (int64_t pg : row_pages) n += ceil_div(pg, p);
-    return n * num_kv_heads;
+    return n * waves_per_piece;
   };
   const int64_t target = cpa::decode_waves_target(head_dim);
   const int64_t budget = ceil_div(std::max<int64_t>(waves(max_pages), 1), target) * target;
@@ -252,7 +254,11 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   std::vector<int64_t> row_pages(n_dec);
   for (int s = 0; s < n_dec; ++s) row_pages[s] = ceil_div(out->seq_lens[s], cpa::kBlock);
   const int split = params->decode_split_tokens;
-  const int piece_pages = split ? 0 : pick_piece_pages(row_pages, params->num_kv_heads, params->head_dim);
+  const int piece_pages =
+      split ? 0
+            : pick_piece_pages(row_pages,
+                               params->num_kv_heads * cpa::decode_column_blocks(group),
+                               params->head_dim);
   std::vector<int32_t> dsplits, dmerges, tiles;
   int partials = 0;
   struct DPiece { int32_t row, kb, ke, slot; };

@@ -36,14 +36,15 @@ hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache,
                         int head_dim, float scale_log2, void* out, float* lse, Partials part,
                         hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
+  // G = 0 instances: any other group, read at run time
 #define CPA_CHK(DD, GG)                                                                        \
-  if (head_dim == DD && G == GG) {                                                              \
+  if (head_dim == DD && (G == GG || GG == 0)) {                                               \
     launch_chunk_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,      \
                            num_q_heads, num_kv_heads, scale_log2, out, lse, part, stream);      \
     return hipGetLastError();                                                                   \
   }
-  CPA_CHK(128, 1) CPA_CHK(128, 2) CPA_CHK(128, 4) CPA_CHK(128, 8)
-  CPA_CHK(64, 1) CPA_CHK(64, 2) CPA_CHK(64, 4) CPA_CHK(64, 8)
+  CPA_CHK(128, 1) CPA_CHK(128, 2) CPA_CHK(128, 4) CPA_CHK(128, 8) CPA_CHK(128, 0)
+  CPA_CHK(64, 1) CPA_CHK(64, 2) CPA_CHK(64, 4) CPA_CHK(64, 8) CPA_CHK(64, 0)
 #undef CPA_CHK
   return hipErrorInvalidValue;
 }

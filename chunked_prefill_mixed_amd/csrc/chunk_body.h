@@ -11,8 +11,8 @@
 // long prefix this kernel is bound by matrix-core throughput.
 //
 // Workgroup = W = chunk_waves(D) waves = 32 W query rows of one KV head (256
-// at head_dim 128, 128 at 64): 32 W / G tokens times the G query heads that
-// share the KV head; all its rows share every K/V tile it loads.  Each wave
+// at head_dim 128, 128 at 64): floor(32 W / G) tokens times the G query heads
+// that share the KV head; all its rows share every K/V tile it loads.  Each wave
 // owns 32 rows, one per lane column n = lane % 32.
 //   S^T[64 keys][32 rows] = K Q^T    v_mfma_f32_32x32x16_bf16, K from LDS (A),
 //                                    Q^T kept in registers (B)
@@ -102,11 +102,13 @@ __device__ __forceinline__ void chunk_body(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ncol = lane & 31, half = lane >> 5;
+  // query heads per KV head: compiled in, or (G = 0) read at run time
+  const int grp = G > 0 ? G : num_q_heads / num_kv_heads;
   int r = wave * 32 + ncol;  // the wave's row, one per lane column
-  int j = qb + r / G;
+  int j = qb + r / grp;
   const bool row_ok = j < qe;
   if (!row_ok) j = qe - 1;  // ragged tail: recompute the last query, store nothing
-  const int hq = g * G + (r % G);
+  const int hq = g * grp + (r % grp);
   const int qlimit = c + j;
 
   // B operand of S^T: Q[j][hq][16ks + 8half .. +8]
@@ -446,7 +448,7 @@ __device__ __forceinline__ void chunk_body(
   // the output addresses are derived again here rather than kept in
   // registers through the loop
   asm volatile("" : "+v"(j), "+v"(r));
-  const int hq_out = g * G + (r % G);
+  const int hq_out = g * grp + (r % grp);
   if (row_ok && slot >= 0) {
     // one piece of a split tile: unnormalised partial for merge_kernel
     const int64_t pr = ((int64_t)slot * num_kv_heads + g) * ROWS + r;

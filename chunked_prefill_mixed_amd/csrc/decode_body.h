@@ -16,8 +16,10 @@
 //                                      pieces ([D/8][16][8]), so the A operand
 //                                      of step kk (pieces 4kk..4kk+3 of all 16
 //                                      keys) is one contiguous 1 KB load;
-//                                      column n of Q^T holds query head n % G
-//                                      (columns n >= G repeat heads and are
+//                                      column n of Q^T holds query head n of
+//                                      the group (16 per wave: a group of more
+//                                      takes one wave per 16 heads; columns
+//                                      past the group repeat a head and are
 //                                      never stored)
 //   O^T[D][16 cols] += V^T P^T         v_mfma_f32_16x16x16_bf16, D/16 blocks;
 //                                      V pages are stored transposed ([D][16])
@@ -69,14 +71,25 @@ __device__ __forceinline__ void decode_body(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int item = first_item + wave;  // wave w of the workgroup takes item first_item + w
   if (item >= num_items) return;  // whole wave; no workgroup barrier below
-  const int g = item % num_kv_heads;
-  const int4 e = reinterpret_cast<const int4*>(splits)[item / num_kv_heads];
+  // query heads per KV head: compiled in (at most 8, one block of columns), or
+  // (G = 0) read at run time, in ceil(G / 16) blocks of 16 columns, each block
+  // its own item: item = (piece x KV head) x blocks + block
+  static_assert(G >= 0 && G <= kDecodeCols, "compiled groups fit one block of columns");
+  const int grp = G > 0 ? G : num_q_heads / num_kv_heads;
+  const int ncb = G > 0 ? 1 : decode_column_blocks(grp);
+  const int cb = G > 0 ? 0 : item % ncb;
+  const int pk = G > 0 ? item : item / ncb;
+  const int g = pk % num_kv_heads;
+  const int4 e = reinterpret_cast<const int4*>(splits)[pk / num_kv_heads];
   const int row = e.x, kv_begin = e.y, kv_end = e.z, slot = e.w;
   // decode rows come first and hold one token each, so row s is packed token s
   const int t = row;
-  const int n = lane & 15;   // column: query head n % G of the group
+  const int n = lane & 15;                 // column of S^T and O^T
+  const int col = kDecodeCols * cb + n;    // the column's query head within the group
   const int g4 = lane >> 4;  // lane group: d pieces of S^T, keys 4*g4..+4 of P^T and O^T
-  const int hq = g * G + n % G;
+  // columns past the group repeat a head of it and are never stored
+  constexpr int kGroup = G > 0 ? G : 1;  // the compiled group (a divisor in the G > 0 path)
+  const int hq = g * grp + (G > 0 ? n % kGroup : min(col, grp - 1));
 
   // B operand of S^T: Q[hq][32 kk + 8 g4 .. +8]
   uint4 qf[KK];
@@ -185,7 +198,7 @@ __device__ __forceinline__ void decode_body(
   // column sums over the 4 lane groups (each summed its own keys)
   lsum += xor_lane(lsum, 16);
   lsum += xor_lane(lsum, 32);
-  if (n >= G) return;
+  if (col >= grp) return;
   const int d0 = 4 * g4;  // this lane's O^T rows inside each 16-row block
   if (slot < 0) {
     const float inv = 1.f / lsum;

@@ -117,7 +117,8 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
   const int row = e0.x, qb = e0.y, qe = e0.z, first = e0.w, n = e1.x;
   const int li = threadIdx.x % LPR;
   const int r = rg * RPW + threadIdx.x / LPR;
-  const int j = qb + r / G;
+  const int grp = G > 0 ? G : num_q_heads / num_kv_heads;  // G = 0: read at run time
+  const int j = qb + r / grp;
   if (j >= qe) return;  // past the chunk end
   const int64_t stride = (int64_t)num_kv_heads * ROWS;  // rows between consecutive slots
   const int64_t base = ((int64_t)first * num_kv_heads + g) * ROWS + r;
@@ -161,7 +162,7 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
   else
     batches(std::integral_constant<int, kChunkMergeBatch>{});
   const float inv = 1.f / L;
-  const int hq = g * G + (r % G);
+  const int hq = g * grp + (r % grp);
   const int t0 = qsl[row];
   uint2 v;
   v.x = pack_bf16x2(o.x * inv, o.y * inv);
@@ -196,14 +197,15 @@ hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const in
   const int pairs = num_decode_merges * num_q_heads;
   const dim3 grid(chunk_blocks + (pairs + 3) / 4), block(256);
   auto* o = static_cast<uint16_t*>(out);
+  // G = 0 instances: any other group, read at run time
 #define CPA_MRG(DD, GG)                                                                        \
-  if (head_dim == DD && G == GG) {                                                              \
+  if (head_dim == DD && (G == GG || GG == 0)) {                                               \
     hipLaunchKernelGGL((merge_kernel<DD, GG>), grid, block, 0, stream, dmerges, pairs, cmerges, \
                        chunk_blocks, qsl, num_q_heads, num_kv_heads, dws, cws, o, lse);         \
     return hipGetLastError();                                                                   \
   }
-  CPA_MRG(128, 1) CPA_MRG(128, 2) CPA_MRG(128, 4) CPA_MRG(128, 8)
-  CPA_MRG(64, 1) CPA_MRG(64, 2) CPA_MRG(64, 4) CPA_MRG(64, 8)
+  CPA_MRG(128, 1) CPA_MRG(128, 2) CPA_MRG(128, 4) CPA_MRG(128, 8) CPA_MRG(128, 0)
+  CPA_MRG(64, 1) CPA_MRG(64, 2) CPA_MRG(64, 4) CPA_MRG(64, 8) CPA_MRG(64, 0)
 #undef CPA_MRG
   return hipErrorInvalidValue;
 }

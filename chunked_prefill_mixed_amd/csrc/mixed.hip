@@ -52,7 +52,8 @@ static void launch_mixed_t(const void* q, const void* kc, const void* vc, const 
                            const int32_t* tiles, int num_tiles, const int32_t* splits,
                            int num_splits, int hq, int hkv, float sl2, void* out, float* lse,
                            Partials cpart, Partials dpart, hipStream_t stream) {
-  const int items = num_splits * hkv;
+  // a run-time group (G = 0) of more than 16 heads takes a wave per 16 heads
+  const int items = num_splits * hkv * (G > 0 ? 1 : decode_column_blocks(hq / hkv));
   constexpr int W = chunk_waves(D);  // decode items per workgroup
   const int decode_wgs = (items + W - 1) / W;
   const int decode_lead = decode_wgs <= mixed_slots(D) ? (decode_wgs + 7) / 8 * 8 : 0;
@@ -71,15 +72,16 @@ hipError_t launch_mixed(const void* q, const void* k_cache, const void* v_cache,
                         void* out, float* lse, Partials cpart, Partials dpart,
                         hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
+  // G = 0 instances: any other group, read at run time
 #define CPA_MIX(DD, GG)                                                                        \
-  if (head_dim == DD && G == GG) {                                                              \
+  if (head_dim == DD && (G == GG || GG == 0)) {                                               \
     launch_mixed_t<DD, GG>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles,      \
                            splits, num_splits, num_q_heads, num_kv_heads, scale_log2, out, lse, \
                            cpart, dpart, stream);                                               \
     return hipGetLastError();                                                                   \
   }
-  CPA_MIX(128, 1) CPA_MIX(128, 2) CPA_MIX(128, 4) CPA_MIX(128, 8)
-  CPA_MIX(64, 1) CPA_MIX(64, 2) CPA_MIX(64, 4) CPA_MIX(64, 8)
+  CPA_MIX(128, 1) CPA_MIX(128, 2) CPA_MIX(128, 4) CPA_MIX(128, 8) CPA_MIX(128, 0)
+  CPA_MIX(64, 1) CPA_MIX(64, 2) CPA_MIX(64, 4) CPA_MIX(64, 8) CPA_MIX(64, 0)
 #undef CPA_MIX
   return hipErrorInvalidValue;
 }

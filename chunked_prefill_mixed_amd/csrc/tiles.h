@@ -40,11 +40,22 @@ inline int chunk_wg_target(int head_dim) { return head_dim > 64 ? 256 : 512; }
 // launches, which measured as fast or faster there.
 inline int mixed_slots(int head_dim) { return 256 * (head_dim > 64 ? 1 : 3); }
 
-// Query tokens one chunk workgroup covers when G query heads share a KV head.
+// Query tokens one chunk workgroup covers when G query heads share a KV head
+// (its last chunk_rows % G rows, if any, hold no query and store nothing).
 inline int chunk_tile_tokens(int group, int head_dim) { return chunk_rows(head_dim) / group; }
 
-inline bool supported_group(int group) {
-  return group == 1 || group == 2 || group == 4 || group == 8;
+// Query heads one decode wave serves: the 16 columns of its S^T product.  A
+// larger group takes ceil(G / 16) waves per (piece, KV head), one per block
+// of 16 heads.
+constexpr int kDecodeCols = 16;
+constexpr int decode_column_blocks(int group) { return (group + kDecodeCols - 1) / kDecodeCols; }
+
+// Any number of query heads per KV head up to one chunk tile's rows, so that
+// a tile holds at least one token.  G = 1, 2, 4 and 8 have kernels compiled
+// for them; any other G runs the same kernels with G read at run time, which
+// only changes the row -> (token, head) index arithmetic.
+inline bool supported_group(int group, int head_dim) {
+  return group >= 1 && group <= chunk_rows(head_dim);
 }
 inline bool supported_head_dim(int d) { return d == 64 || d == 128; }
 // at most 256 KV heads: one page of all KV heads then spans under 2^21 bytes,

@@ -36,8 +36,12 @@
  *   - Status: CPA_OK (0) or a negative CPA_ERR_*; the library never aborts and
  *     never throws across the ABI.  CPA_ERR_DEVICE carries a launch failure
  *     reported by hipGetLastError.
- *   - Supported shapes: head_dim in {64, 128}; num_q_heads / num_kv_heads in
- *     {1, 2, 4, 8}; num_kv_heads at most 256; block_size 16; bf16 only.
+ *   - Supported shapes: head_dim in {64, 128}; num_q_heads a multiple of
+ *     num_kv_heads, with G = num_q_heads / num_kv_heads from 1 to one chunk
+ *     tile's rows R (256 at head_dim 128, 128 at 64); num_kv_heads at most
+ *     256; block_size 16; bf16 only.  G = 1, 2, 4 and 8 run kernels compiled
+ *     for them, any other G the same kernels with G read at run time; a
+ *     decode piece takes one wave per 16 query heads of its group.
  *
  * KV cache layout (one tensor each for K and V; the same page id in both)
  *   k_cache [num_blocks][num_kv_heads][head_dim/8][16][8]
@@ -148,9 +152,10 @@ typedef struct {
  * num_decode_merges of CPA_DECODE_MERGE_WORDS, num_chunk_merges of
  * CPA_CHUNK_MERGE_WORDS (the two merge sections run as one launch).  A chunk tile covers R
  * (token, query head) rows of one KV head, R = 256 at head_dim 128 and 128 at
- * head_dim 64: R / (num_q_heads / num_kv_heads) tokens. */
+ * head_dim 64: floor(R / G) tokens, G = num_q_heads / num_kv_heads (when G does
+ * not divide R, a tile's last R mod G rows hold no query). */
 typedef struct {
-  int32_t num_decode_splits;   /* one wave per (split, KV head) */
+  int32_t num_decode_splits;   /* one wave per (split, KV head, 16 query heads of the group) */
   int32_t num_decode_merges;   /* decode rows whose keys were split in several pieces */
   int32_t num_chunk_tiles;     /* one workgroup per (tile, KV head) */
   int32_t num_chunk_merges;    /* chunk tiles whose prefix keys were split in several pieces */

@@ -125,11 +125,13 @@ def test_wide_head_counts(case):
 
 
 @pytest.mark.parametrize("D", [128, 64])
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 3, 7, 29])
 def test_chunk_tile_edges(G, D):
     """Chunks one token short of, exactly at and one past the query tile of
-    256 (token, head) rows at head_dim 128 (128 at 64), i.e. 256/G tokens,
-    and one of two tiles plus a token, at every head grouping; one chunk
+    256 (token, head) rows at head_dim 128 (128 at 64), i.e. floor(256/G)
+    tokens, and one of two tiles plus a token, at the compiled head groupings
+    and at three read at run time (3, 7, 29: tiles whose last rows hold no
+    query; 29 also takes two decode waves per piece and KV head); one chunk
     after a 3000-token prefix, so the few tiles of the step are cut into key
     pieces and merged.  Every token of every row matches the oracle."""
     rows = 256 if D == 128 else 128
@@ -303,6 +305,56 @@ def test_one_launch_matches_separate_sections(case):
         x, y = getattr(a, name), getattr(b, name)
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y), name
+
+
+# (Hq, Hkv, D, decode contexts, chunks): groups the kernels read at run time.
+# Decode pieces of up to 64 pages; a group above 16 takes ceil(G / 16) decode
+# waves per piece and KV head.  The largest groups are one chunk tile's rows
+# (one token per tile: 256 at head_dim 128, 128 at 64).
+ANY_GROUP = [
+    (6, 2, 128, [0, 15, 1500], [(0, 200), (2000, 2100)]),
+    (10, 2, 64, [700, 5000], [(300, 420), (0, 1)]),
+    (16, 1, 128, [64, 2047], [(900, 1000)]),
+    (17, 1, 64, [3000, 1], [(0, 50), (600, 641)]),
+    (96, 2, 128, [1200, 33], [(100, 140)]),
+    (128, 1, 64, [2500], [(0, 9), (400, 403)]),
+    (256, 1, 128, [900, 4100], [(1000, 1006)]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ANY_GROUP)))
+def test_any_group_size(case):
+    """Query heads per KV head outside the compiled 1, 2, 4 and 8: every
+    token of every row against the oracle, at default and at fine splits."""
+    Hq, Hkv, D, dec, chunks = ANY_GROUP[case]
+    w = workloads.random_workload(2600 + case, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  decode_ctx=dec, chunks=chunks)
+    check_step(w, label=f"G{Hq // Hkv} D{D}")
+    check_step(w, decode_split_tokens=128, chunk_split_tokens=64, label=f"G{Hq // Hkv} D{D} split")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,tokens", [(58, 2, 128, 1024), (28, 4, 64, 3456),
+                                             (48, 1, 128, 1280)])
+def test_any_group_one_launch(Hq, Hkv, D, tokens):
+    """Run-time groups (29, 7, 48) with enough chunk tiles for the one-launch
+    kernel: it matches the oracle on every token and gives the same bits as
+    the plan run section by section."""
+    import torch
+    rng = np.random.default_rng(Hq + D)
+    ctx = rng.integers(100, 3000, size=12).tolist()
+    w = workloads.random_workload(2700 + Hq + D, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  decode_ctx=ctx, chunks=[(300, 300 + tokens)])
+    a, _ = check_step(w, label=f"G{Hq // Hkv} D{D} one launch")
+    c = a.counts
+    assert c.num_decode_splits > 0
+    assert c.num_chunk_tiles * Hkv >= 256 * (1 if D > 64 else 3)  # the one-launch path ran
+    b = DeviceStep(w, validate=False)
+    b.append()
+    for sec in ("decode_splits", "chunk_tiles", "decode_merges", "chunk_merges"):
+        b._section_call(sec, None)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.lse, b.lse)
 
 
 @pytest.mark.parametrize("rows", [449, 511, 512, 700])

@@ -212,6 +212,42 @@ def test_builder_random_mixes_match_oracle(lib):
         check_plan(m, G, D)
 
 
+@pytest.mark.parametrize("G,D", [(3, 128), (5, 64), (7, 128), (12, 64), (16, 128), (17, 128),
+                                 (29, 64), (48, 128), (128, 64), (256, 128)])
+def test_builder_plans_any_group(lib, G, D):
+    """Groups outside 1, 2, 4, 8, up to one tile's rows: the schedule is the
+    oracle's and the plan covers every key and query once, with tiles of
+    floor(R / G) tokens."""
+    rng = np.random.default_rng(9100 + G + D)
+    for _ in range(20):
+        reqs = []
+        for i in range(int(rng.integers(1, 30))):
+            if rng.random() < 0.5:
+                c = int(rng.integers(0, 6000))
+                reqs.append(oracle.Request(i, c, c + 1, True))
+            else:
+                L = int(rng.integers(1, 3000))
+                c = int(rng.integers(0, L + 1))
+                reqs.append(oracle.Request(i, c, L, False))
+        ndec = sum(r.is_decode for r in reqs)
+        budget = int(rng.integers(max(1, ndec), ndec + 4000))
+        Hkv = int(rng.choice([1, 2]))
+        m = same_as_oracle(reqs, budget, 0, Hq=G * Hkv, Hkv=Hkv, D=D)
+        check_plan(m, G, D)
+
+
+def test_decode_pieces_count_the_waves_of_wide_groups(lib):
+    """A group of more than 16 heads takes one decode wave per 16 heads, so
+    the planner cuts the rows into fewer pieces for the same wave budget."""
+    reqs = [oracle.Request(i, 3000 + 37 * i, 3001 + 37 * i, True) for i in range(40)]
+    pieces = {}
+    for G in (16, 32, 64):
+        m = cpa.cpa_build_metadata(reqs, token_budget=64, long_prefill_cap=0, num_q_heads=G,
+                                   num_kv_heads=1, head_dim=128)
+        pieces[G] = m["counts"].num_decode_splits
+    assert pieces[16] > pieces[32] > pieces[64] >= len(reqs)
+
+
 @pytest.mark.parametrize("policy", ["truncate", "defer", "quota"])
 @pytest.mark.parametrize("adaptive", [False, True])
 @pytest.mark.parametrize("block_aligned", [False, True])
@@ -307,7 +343,8 @@ def test_builder_rejects_unknown_policy_value(lib):
     ("target_below_computed", cpa.CPA_ERR_INVALID),
     ("decodes_over_budget", cpa.CPA_ERR_BUDGET),
     ("head_dim_96", cpa.CPA_ERR_UNSUPPORTED),
-    ("group_3", cpa.CPA_ERR_UNSUPPORTED),
+    ("group_over_tile_rows", cpa.CPA_ERR_UNSUPPORTED),
+    ("group_over_tile_rows_d64", cpa.CPA_ERR_UNSUPPORTED),
     ("heads_not_multiple", cpa.CPA_ERR_UNSUPPORTED),
     ("block_size_32", cpa.CPA_ERR_UNSUPPORTED),
     ("kv_heads_over_256", cpa.CPA_ERR_UNSUPPORTED),
@@ -338,8 +375,10 @@ def test_builder_error_paths(lib, case, status):
         kw["budget"] = 9
     elif case == "head_dim_96":
         args["D"] = 96
-    elif case == "group_3":
-        args.update(Hq=6, Hkv=2)
+    elif case == "group_over_tile_rows":  # a tile of 256 rows holds no token of 257 heads
+        args.update(Hq=257, Hkv=1)
+    elif case == "group_over_tile_rows_d64":
+        args.update(Hq=129, Hkv=1, D=64)
     elif case == "heads_not_multiple":
         args.update(Hq=7, Hkv=2)
     elif case == "block_size_32":
