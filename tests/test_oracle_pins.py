@@ -111,7 +111,7 @@ def run_oracle_chunk(q, K, V, ids, nb, c, Hkv, scale):
 
 BRUTE_CASES = [
     (Hq, G, D, c, n)
-    for (Hq, G) in [(1, 1), (4, 1), (4, 2)]
+    for (Hq, G) in [(1, 1), (4, 1), (4, 2), (6, 3), (14, 7)]
     for D in (8, 16)
     for c in (0, 1, 15, 16, 17)
     for n in (1, 2, 5, 16)
