@@ -286,11 +286,13 @@ def percentile(xs, q):
     return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
 
-def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, DeviceStep):
+def run_config(config, steps, warmup, stride, graph, torch, cpa, workloads, DeviceStep,
+               kv_shard=1):
     """Warm up, then time ``steps`` steps of the configuration's instances,
     rotated; returns the measurements (see main)."""
     t_setup = time.perf_counter()
-    ws = [workloads.make_workload(config, i) for i in range(workloads.num_instances(config))]
+    ws = [workloads.make_workload(config, i, kv_shard)
+          for i in range(workloads.num_instances(config))]
     insts = [Instance(w, torch, cpa, DeviceStep) for w in ws]
     log(f"config {config} setup {time.perf_counter() - t_setup:.1f}s: {len(insts)} instance(s), "
         f"{[i.ds.num_tokens for i in insts]} tokens/step")
@@ -528,6 +530,10 @@ def main():
     ap.add_argument("--kernel-event-stride", type=int, default=3,
                     help="record per-kernel HIP events on every n-th round of instances (each "
                          "instance's step of that round); the other steps carry no event")
+    ap.add_argument("--kv-shard", type=int, default=1, choices=[1, 2, 4, 8],
+                    help="time one GPU's share of each step split N ways by KV head (32/N query "
+                         "heads on 8/N KV heads, the same rows and tokens); the default 1 is the "
+                         "whole step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -559,7 +565,7 @@ def main():
 
     K, W = args.steps, args.warmup
     head = run_config(args.config, K, W, args.kernel_event_stride, args.graph, torch, cpa,
-                      workloads, DeviceStep)
+                      workloads, DeviceStep, args.kv_shard)
     ws = head.pop("workloads")
     kernels = head["kernels"]
     # the dominant kernel of the step: the one with the largest time
@@ -574,7 +580,8 @@ def main():
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s"}
     roofline["frac"] = ach / roofline["peak"]
-    roofline["traffic"] = traffic_for(dominant, args.config)
+    # the counter records are of the whole steps
+    roofline["traffic"] = traffic_for(dominant, args.config) if args.kv_shard == 1 else None
     wk = {"chunk_kernel": "chunk_flops", "decode_kernel": "decode_bytes",
           "append_kernel": "append_bytes"}[dominant]
     roofline["algorithmic_per_launch"] = (sum(head["work_per_step"][wk])
@@ -586,7 +593,7 @@ def main():
         if c == args.config:
             continue
         r = run_config(c, args.other_steps, 4, args.kernel_event_stride, False, torch, cpa,
-                       workloads, DeviceStep)
+                       workloads, DeviceStep, args.kv_shard)
         r.pop("workloads")
         others[config_key(c)] = {
             "value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
@@ -606,6 +613,12 @@ def main():
                                       else "hbm_copy_GB/s"]
     roofline["frac_of_measured"] = roofline["achieved"] / roofline["measured_peak"]
 
+    config = {"workload": WORKLOAD_TEXT[args.config], "config": config_key(args.config),
+              "tokens_per_step": head["tokens_per_step"], "instances": head["instances"]}
+    if args.kv_shard != 1:
+        config["workload"] += (f"; one GPU's share of a {args.kv_shard}-way split by KV head: "
+                               f"Hq={32 // args.kv_shard} Hkv={8 // args.kv_shard}")
+        config["kv_shard"] = args.kv_shard
     result = {
         "metric": METRIC,
         "value": head["value"],
@@ -619,9 +632,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "config": config_key(args.config),
-                   "tokens_per_step": head["tokens_per_step"],
-                   "instances": head["instances"]},
+        "config": config,
         "roofline": roofline,
         "kernels": kernels,
         "graph": bool(args.graph),

@@ -19,6 +19,8 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <vector>
 
 #include "../../include/cpa.h"
@@ -95,14 +97,12 @@ int pick_piece_pages(const std::vector<int64_t>& row_pages, int waves_per_piece,
   return (int)lo;
 }
 
-// Pieces per chunk tile when the caller leaves the split size to the library:
-// none split when the tiles alone give a resident round of workgroups;
-// otherwise each tile's keys are cut into ceil(L / S) equal pieces, with S
-// the smallest size (at least kChunkMinSplit) for which all pieces of all KV
-// heads fit one round, so no short tail pieces spill into a second round.
-std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, int num_kv_heads,
-                                       int head_dim) {
-  const int target = cpa::chunk_wg_target(head_dim);
+// Pieces per tile for a grid of at most `target` workgroups: none when the
+// tiles alone reach it; otherwise each tile's keys are cut into ceil(L / S)
+// equal pieces, with S the smallest size (a multiple of the KV tile, at
+// least kChunkMinSplit) for which all pieces of all KV heads fit the target.
+std::vector<int32_t> pieces_within(const std::vector<int64_t>& tile_keys, int num_kv_heads,
+                                   int64_t target) {
   std::vector<int32_t> n(tile_keys.size(), 1);
   if ((int64_t)tile_keys.size() * num_kv_heads >= target) return n;
   int64_t total_keys = 0;
@@ -118,6 +118,68 @@ std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, in
     if (pieces * num_kv_heads <= target) return n;
     S += std::max<int64_t>(cpa::kKvTile, S / 16);
   }
+}
+
+// Keys' worth of time a piece of a split tile costs beyond its own keys (its
+// fp32 partial write and the merge's read of it), and what a plan with any
+// split tile costs once more for the merging.  Both were fitted to same-box
+// timings: a one-round step whose causal tiles run up to twice the mean (a
+// 2048-token chunk at prefix 0) gains less from splitting than its merges
+// cost, and stays unsplit.
+constexpr int64_t kPieceCost = 128;
+constexpr int64_t kMergeCost = 512;
+
+// Finish time of the chunk launch, in keys, estimated as list scheduling:
+// the pieces' workgroups (one per KV head) taken longest first by `slots`
+// resident workgroups, each starting the next one when it frees (the order
+// the grid is dispatched in).
+int64_t estimated_finish(const std::vector<int64_t>& tile_keys, const std::vector<int32_t>& n,
+                         int num_kv_heads, int slots) {
+  std::vector<int64_t> work;
+  for (size_t t = 0; t < tile_keys.size(); ++t)
+    for (int32_t k = 0; k < n[t]; ++k)
+      work.push_back(ceil_div(tile_keys[t], n[t]) + (n[t] > 1 ? kPieceCost : 0));
+  std::sort(work.begin(), work.end(), std::greater<int64_t>());
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int i = 0; i < slots; ++i) free_at.push(0);
+  int64_t end = 0;
+  for (int64_t w : work)
+    for (int h = 0; h < num_kv_heads; ++h) {
+      const int64_t t = free_at.top() + w;
+      free_at.pop();
+      free_at.push(t);
+      end = std::max(end, t);
+    }
+  const bool split = std::any_of(n.begin(), n.end(), [](int32_t k) { return k > 1; });
+  return end + (split ? kMergeCost : 0);
+}
+
+// Pieces per chunk tile when the caller leaves the split size to the library.
+// The base plan fills one resident round (pieces_within the resident slots;
+// nothing is split when the tiles alone fill it).  With tiles of very
+// different lengths that round waits for its longest piece, so plans of two
+// and three rounds of smaller pieces are estimated too, and one replaces the
+// base plan when it is estimated to finish in under kSplitGain of the base
+// plan's time.  Steps of three rounds of tiles or more are left unsplit
+// without estimating (list scheduling balances them).
+constexpr double kSplitGain = 0.85;
+
+std::vector<int32_t> pick_chunk_pieces(const std::vector<int64_t>& tile_keys, int num_kv_heads,
+                                       int head_dim) {
+  const int slots = cpa::chunk_wg_target(head_dim);
+  std::vector<int32_t> best = pieces_within(tile_keys, num_kv_heads, slots);
+  if ((int64_t)tile_keys.size() * num_kv_heads >= 3LL * slots) return best;
+  const int64_t base = estimated_finish(tile_keys, best, num_kv_heads, slots);
+  int64_t best_time = base;
+  for (int rounds = 2; rounds <= 3; ++rounds) {
+    std::vector<int32_t> n = pieces_within(tile_keys, num_kv_heads, (int64_t)rounds * slots);
+    const int64_t t = estimated_finish(tile_keys, n, num_kv_heads, slots);
+    if (t < kSplitGain * base && t < best_time) {
+      best = n;
+      best_time = t;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -342,6 +404,21 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   // longest key range first, so the last workgroups to start are short ones
   std::stable_sort(pieces.begin(), pieces.end(),
                    [](const Piece& x, const Piece& y) { return x.ke - x.kb > y.ke - y.kb; });
+  // The chunk grid is (KV head, piece) items, head-major, and each of the 8
+  // XCDs runs one contiguous range of them (xcd_remap).  With 8 KV heads an
+  // XCD's range is one head's whole list; with fewer, 8 / Hkv XCDs split a
+  // head's list into consecutive ranges, and the longest-first order would
+  // give the first of them all the long pieces.  Deal the pieces round-robin
+  // over those ranges instead (each range stays longest first).
+  const int hkv = params->num_kv_heads;
+  if (hkv < 8 && 8 % hkv == 0 && pieces.size() > 1) {
+    const size_t f = (size_t)(8 / hkv);
+    std::vector<Piece> dealt;
+    dealt.reserve(pieces.size());
+    for (size_t r = 0; r < f; ++r)
+      for (size_t j = r; j < pieces.size(); j += f) dealt.push_back(pieces[j]);
+    pieces.swap(dealt);
+  }
   for (const Piece& p : pieces) tiles.insert(tiles.end(), {p.row, p.qb, p.qe, p.kb, p.ke, p.slot, 0, 0});
 
   out->counts.num_decode_splits = (int32_t)(dsplits.size() / CPA_DECODE_SPLIT_WORDS);

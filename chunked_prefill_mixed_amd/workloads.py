@@ -209,17 +209,33 @@ def num_instances(config: int) -> int:
     return {1: 4, 2: 3, 3: 4, 4: 2, 5: 2}[config]
 
 
-def make_workload(config: int, instance: int = 0) -> Workload:
+def make_workload(config: int, instance: int = 0, kv_shard: int = 1) -> Workload:
     """Instance ``instance`` of measured configuration ``config`` (1..5).
 
     Config 1 instance i is step i of the tiny multi-step run with a fresh
     pool; use :func:`tiny_run` to carry the pool across steps.
+
+    ``kv_shard`` = N (configs 2..5) gives one GPU's share of the step split N
+    ways by KV head: the same rows, tokens and page ids, with 32/N query heads
+    on 8/N KV heads (the pool's pages then hold 8/N heads each).
     """
     seed = 1000 + config
     st = _streams(seed, instance)
     if config == 1:
+        if kv_shard != 1:
+            raise ValueError("the tiny run is not split by KV head")
         run = tiny_run()
         return run.step_workload(instance, run.k_pool, run.v_pool)
+    if kv_shard not in (1, 2, 4, 8):
+        raise ValueError("kv_shard must divide the 8 KV heads")
+    w = _measured_workload(config, instance, seed, st, 32 // kv_shard, 8 // kv_shard)
+    if kv_shard != 1:
+        w.name += f"/kvshard{kv_shard}"
+    return w
+
+
+def _measured_workload(config, instance, seed, st, hq, hkv):
+    """Configurations 2..5 with hq query heads on hkv KV heads."""
     if config == 2:
         rng = np.random.Generator(np.random.PCG64(st["ctx"]))
         ctx = rng.integers(512, 4096, size=32, endpoint=True)
@@ -227,24 +243,24 @@ def make_workload(config: int, instance: int = 0) -> Workload:
         reqs = [Req(i, int(c), int(c) + 1, True) for i, c in enumerate(ctx)]
         reqs.append(Req(32, prefix, 8192, False))
         reach = [int(c) + 1 for c in ctx] + [8192]
-        return build(f"page1_defaults/prefix{prefix}", seed, instance, num_q_heads=32,
-                     num_kv_heads=8, head_dim=128, token_budget=512, long_prefill_cap=0,
+        return build(f"page1_defaults/prefix{prefix}", seed, instance, num_q_heads=hq,
+                     num_kv_heads=hkv, head_dim=128, token_budget=512, long_prefill_cap=0,
                      requests=reqs, reach=reach, pool_blocks=None, streams=st)
     if config == 3:
         prefix = PREFIXES[3][instance]
         ctx = [1000, 3000]
         reqs = [Req(0, 1000, 1001, True), Req(1, 3000, 3001, True), Req(2, prefix, 8192, False)]
         reach = [c + 1 for c in ctx] + [8192]
-        return build(f"budget8192/prefix{prefix}", seed, instance, num_q_heads=32,
-                     num_kv_heads=8, head_dim=128, token_budget=8192, long_prefill_cap=2048,
+        return build(f"budget8192/prefix{prefix}", seed, instance, num_q_heads=hq,
+                     num_kv_heads=hkv, head_dim=128, token_budget=8192, long_prefill_cap=2048,
                      requests=reqs, reach=reach, pool_blocks=None, streams=st)
     if config == 4:
         ctx = _lognormal_lengths(st["ctx"], 64, 2048, 0.75, 32768)
         reqs = [Req(i, int(c), int(c) + 1, True) for i, c in enumerate(ctx)]
         reqs.append(Req(64, 31744, 32768, False))
         reach = [int(c) + 1 for c in ctx] + [32768]
-        return build(f"long_context/prefix31744/seed{instance}", seed, instance, num_q_heads=32,
-                     num_kv_heads=8, head_dim=128, token_budget=8192, long_prefill_cap=0,
+        return build(f"long_context/prefix31744/seed{instance}", seed, instance, num_q_heads=hq,
+                     num_kv_heads=hkv, head_dim=128, token_budget=8192, long_prefill_cap=0,
                      requests=reqs, reach=reach, pool_blocks=None, streams=st)
     if config == 5:
         ctx = _lognormal_lengths(st["ctx"], 256, 1024, 0.75, 16384)
@@ -258,7 +274,7 @@ def make_workload(config: int, instance: int = 0) -> Workload:
             reqs.append(Req(256 + k, int(offs[k]), int(offs[k]) + lefts[k], False))
         reach = [int(c) + 1 for c in ctx] + [int(offs[k]) + lefts[k] for k in range(3)]
         # 2 GiB of K+V: 32768 pages of 64 KiB (32 KiB K + 32 KiB V)
-        return build(f"heavy_mixed/seed{instance}", seed, instance, num_q_heads=32, num_kv_heads=8,
+        return build(f"heavy_mixed/seed{instance}", seed, instance, num_q_heads=hq, num_kv_heads=hkv,
                      head_dim=128, token_budget=8192, long_prefill_cap=0, requests=reqs,
                      reach=reach, pool_blocks=32768, streams=st)
     raise ValueError(f"unknown config {config}")

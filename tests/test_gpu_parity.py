@@ -530,6 +530,30 @@ def test_config_end_to_end(config):
         del ds
 
 
+@pytest.mark.parametrize("config", [4, 5])
+def test_kv_shard_end_to_end(config):
+    """One GPU's share of the long-context and heavy-mixed steps split 8 ways
+    by KV head (4 query heads on 1 KV head: the planner cuts the few chunk
+    tiles into key pieces to fill the GPU), every instance: the pool
+    bit-exact and every token against the oracle."""
+    import torch
+    for inst in range(workloads.num_instances(config)):
+        w = workloads.make_workload(config, inst, kv_shard=8)
+        ds = DeviceStep(w)
+        print(f"config {config} instance {inst}: {w.name}, {ds.num_tokens} tokens", flush=True)
+        ds.run()
+        torch.cuda.synchronize()
+        kp, vp, out, lse = oracle_step_parallel(w, ds.meta)
+        gk, gv = ds.pools_bits()
+        assert np.array_equal(gk, kp) and np.array_equal(gv, vp), w.name
+        del gk, gv, kp, vp
+        err = np.max(np.abs(ds.out_f64() - out))
+        assert err <= OUT_TOL, f"{w.name}: max |err| {err}"
+        lerr = np.max(np.abs(ds.lse_f64() - lse))
+        assert lerr <= LSE_TOL, f"{w.name}: lse err {lerr}"
+        del ds
+
+
 # (Hq, Hkv, D, decode contexts, chunks, decode split tokens, chunk split tokens)
 STAIRCASES = [
     (32, 8, 128, [3000, 777, 64, 15], [(1000, 1300), (0, 200)], 0, 0),

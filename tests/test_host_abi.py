@@ -68,7 +68,7 @@ def test_builder_matches_oracle_on_configs(lib, config):
         got = same_as_oracle(w.requests, w.token_budget, w.long_prefill_cap,
                              Hq=w.num_q_heads, Hkv=w.num_kv_heads, D=w.head_dim,
                              host_block_table=w.block_table, num_blocks=w.num_blocks)
-        check_plan(got, w.num_q_heads // w.num_kv_heads, w.head_dim)
+        check_plan(got, w.num_q_heads // w.num_kv_heads, w.head_dim, w.num_kv_heads)
         # slot mapping: page * 16 + slot of every scheduled token (checked here
         # with the test's own indexing)
         sm = got["slot_mapping"]
@@ -87,7 +87,7 @@ def chunk_rows(head_dim):
     return 256 if head_dim == 128 else 128
 
 
-def check_plan(m, group, head_dim):
+def check_plan(m, group, head_dim, num_kv_heads=8):
     """Every decode row's keys are covered exactly once by page-aligned splits;
     merges list exactly the rows with several splits.  Every chunk row's
     tokens are covered by tiles of R/G tokens (R rows per tile); each tile's keys
@@ -148,8 +148,18 @@ def check_plan(m, group, head_dim):
             assert n == len(pcs)
             assert sorted(p[2] for p in pcs) == list(range(first, first + n))
     assert sorted(cslots) == list(range(m["counts"].num_chunk_partials))
+    # longest first; with fewer than 8 KV heads the list is dealt round-robin
+    # into 8 / Hkv consecutive runs (one per XCD range of a head), each
+    # longest first: interleaving the runs back gives the sorted list
     lens = [ke - kb for _, _, _, kb, ke, *_ in sec["chunk_tiles"]]
-    assert lens == sorted(lens, reverse=True)
+    f = 8 // num_kv_heads if num_kv_heads < 8 and 8 % num_kv_heads == 0 else 1
+    P = len(lens)
+    runs, at = [], 0
+    for r in range(f):
+        n = (P - r + f - 1) // f
+        runs.append(lens[at:at + n])
+        at += n
+    assert [runs[j % f][j // f] for j in range(P)] == sorted(lens, reverse=True)
 
 
 def users_and_prompt(running, prompt):
@@ -209,7 +219,7 @@ def test_builder_random_mixes_match_oracle(lib):
         csplit = int(rng.choice([0, 0, 64, 256, 1024]))
         m = same_as_oracle(reqs, budget, cap, Hq=G * Hkv, Hkv=Hkv, D=D, decode_split_tokens=split,
                            chunk_split_tokens=csplit)
-        check_plan(m, G, D)
+        check_plan(m, G, D, Hkv)
 
 
 @pytest.mark.parametrize("G,D", [(3, 128), (5, 64), (7, 128), (12, 64), (16, 128), (17, 128),
@@ -233,7 +243,7 @@ def test_builder_plans_any_group(lib, G, D):
         budget = int(rng.integers(max(1, ndec), ndec + 4000))
         Hkv = int(rng.choice([1, 2]))
         m = same_as_oracle(reqs, budget, 0, Hq=G * Hkv, Hkv=Hkv, D=D)
-        check_plan(m, G, D)
+        check_plan(m, G, D, Hkv)
 
 
 def test_decode_pieces_count_the_waves_of_wide_groups(lib):
@@ -277,7 +287,7 @@ def test_builder_policies_match_oracle(lib, policy, adaptive, block_aligned):
             kw["max_prefill_tokens"] = int(rng.choice([1, 64, 1000, 6000]))
         G = int(rng.choice([1, 4, 8]))
         m = same_as_oracle(reqs, budget, cap, Hq=G * 2, Hkv=2, D=128, **kw)
-        check_plan(m, G, 128)
+        check_plan(m, G, 128, 2)
         if policy != "quota":
             assert m["num_tokens"] <= budget
         else:
@@ -532,3 +542,36 @@ def test_c_program_uses_the_abi(lib, tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "ok"
+
+
+@pytest.mark.parametrize("config", [2, 3])
+def test_kv_shard_workload_is_one_gpus_share(config):
+    """One GPU's share of a step split 8 ways by KV head: the same requests,
+    pages and token count, with 4 query heads on 1 KV head."""
+    full = workloads.make_workload(config, 1)
+    part = workloads.make_workload(config, 1, kv_shard=8)
+    assert (part.num_q_heads, part.num_kv_heads) == (4, 1)
+    assert part.requests == full.requests and part.token_budget == full.token_budget
+    assert np.array_equal(part.block_table, full.block_table)
+    assert part.q.shape[1:] == (4, 128) and part.k_pool.shape[1] == 1
+    with pytest.raises(ValueError):
+        workloads.make_workload(config, 1, kv_shard=3)
+
+
+def test_chunk_split_balances_uneven_tiles(lib):
+    """Tiles of very different lengths that fill about one round of
+    workgroups (one GPU's share of the heavy-mixed step at 2 KV heads) are
+    cut into two or three rounds of pieces, so the round no longer waits for
+    its longest tile; the causal tiles of a 2048-token chunk at prefix 0 at 8
+    KV heads (one round, up to twice the mean) stay unsplit."""
+    uneven = workloads.make_workload(5, 0, kv_shard=4)
+    m = cpa.cpa_build_metadata(uneven.requests, token_budget=uneven.token_budget,
+                               long_prefill_cap=0, num_q_heads=8, num_kv_heads=2, head_dim=128)
+    wgs = m["counts"].num_chunk_tiles * 2
+    assert 256 < wgs <= 3 * 256 and m["counts"].num_chunk_merges > 0
+    check_plan(m, 4, 128, 2)
+    causal = workloads.make_workload(3, 0)
+    m = cpa.cpa_build_metadata(causal.requests, token_budget=causal.token_budget,
+                               long_prefill_cap=causal.long_prefill_cap, num_q_heads=32,
+                               num_kv_heads=8, head_dim=128)
+    assert m["counts"].num_chunk_tiles * 8 == 256 and m["counts"].num_chunk_merges == 0
