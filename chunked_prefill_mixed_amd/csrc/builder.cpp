@@ -12,7 +12,9 @@
 // every wave is resident at once and none reads more pages than needed
 // (lognormal context lengths then balance over the GPU); rows with several
 // pieces get a log-sum-exp merge entry.  Chunk rows are cut into query tiles of
-// chunk_rows(head_dim)/(Hq/Hkv) tokens, ordered longest key range first.
+// floor(chunk_rows(head_dim) / (Hq/Hkv)) tokens whose visible prefix may be cut
+// into key pieces, ordered longest key range first (dealt over the XCD ranges
+// of a KV head when there are fewer than 8 KV heads).
 //
 // Pure host code: no HIP call, safe to run on a machine without a GPU.
 
