@@ -72,13 +72,14 @@ extern "C" int cpa_attention(const void* q, const void* k_cache, const void* v_c
 
   hipStream_t s = (hipStream_t)stream;
   const float sl2 = softmax_scale * 1.4426950408889634f;
-  cpa::Partials dws{nullptr, nullptr, nullptr}, cws{nullptr, nullptr, nullptr};
+  cpa::Partials dws{nullptr, nullptr, nullptr};
+  cpa::ChunkPartials cws{nullptr, nullptr, nullptr};
   if (wl.total > 0) {
     char* base = static_cast<char*>(workspace);
     dws = {reinterpret_cast<float*>(base + wl.dec_acc), reinterpret_cast<float*>(base + wl.dec_m),
            reinterpret_cast<float*>(base + wl.dec_l)};
-    cws = {reinterpret_cast<float*>(base + wl.chk_acc), reinterpret_cast<float*>(base + wl.chk_m),
-           reinterpret_cast<float*>(base + wl.chk_l)};
+    cws = {reinterpret_cast<uint16_t*>(base + wl.chk_acc),
+           reinterpret_cast<float*>(base + wl.chk_m), reinterpret_cast<float*>(base + wl.chk_l)};
   }
   const int32_t* splits = d_plan;
   const int32_t* tiles = splits + (size_t)n.num_decode_splits * CPA_DECODE_SPLIT_WORDS;

@@ -14,7 +14,7 @@ __global__ __launch_bounds__(64 * chunk_waves(D), 8 / chunk_waves(D)) void chunk
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials part) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, ChunkPartials part) {
   chunk_body<D, G>(q, k_cache, v_cache, bt, bt_stride, qsl, ctx, tiles, num_tiles, num_q_heads,
                    num_kv_heads, scale_log2, out, lse, part, blockIdx.x);
 }
@@ -23,7 +23,7 @@ template <int D, int G>
 static void launch_chunk_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
                            const int32_t* tiles, int num_tiles, int hq, int hkv, float sl2,
-                           void* out, float* lse, Partials part, hipStream_t stream) {
+                           void* out, float* lse, ChunkPartials part, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_kernel<D, G>), dim3(num_tiles * hkv), dim3(64 * chunk_waves(D)), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), bt, bt_stride, qsl, ctx, tiles, num_tiles,
@@ -33,7 +33,7 @@ static void launch_chunk_t(const void* q, const void* kc, const void* vc, const 
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-                        int head_dim, float scale_log2, void* out, float* lse, Partials part,
+                        int head_dim, float scale_log2, void* out, float* lse, ChunkPartials part,
                         hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   // G = 0 instances: any other group, read at run time

@@ -51,9 +51,10 @@
 //
 // A work item may cover only a piece [kv_begin, kv_end) of its tile's keys
 // (a long, fully visible prefix is cut into pieces so small chunks still fill
-// the GPU); such a piece writes its unnormalised fp32 output, running max and
-// sum, and merge_kernel (merge.hip) combines the pieces:
-//   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum acc_i 2^(m_i - M) / L.
+// the GPU); such a piece writes its output over its own keys o_i (normalised
+// by its own sum, in bf16), its running max m_i and sum l_i, and merge_kernel
+// (merge.hip) combines the pieces:
+//   M = max m_i,  L = sum l_i 2^(m_i - M),  out = sum l_i 2^(m_i - M) o_i / L.
 // The running max used as the exponent reference is the first tile's row max
 // and moves only when a later tile's max exceeds it by more than 8 (log2
 // units of the scaled score), so the 16-64 accumulator rescale almost never
@@ -75,7 +76,7 @@ __device__ __forceinline__ void chunk_body(
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt, int bt_stride,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, Partials part, int wg) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse, ChunkPartials part, int wg) {
   constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;               // 32-row d blocks of O^T
   constexpr int PAGE = kBlock * D;         // elements of one (page, KV head)
@@ -450,16 +451,20 @@ __device__ __forceinline__ void chunk_body(
   asm volatile("" : "+v"(j), "+v"(r));
   const int hq_out = g * grp + (r % grp);
   if (row_ok && slot >= 0) {
-    // one piece of a split tile: unnormalised partial for merge_kernel
+    // one piece of a split tile, for merge_kernel: its output over its own
+    // keys (normalised by its own sum) in bf16, the sum and max in fp32
     const int64_t pr = ((int64_t)slot * num_kv_heads + g) * ROWS + r;
-    float* acc = part.acc + pr * D;
+    const float inv = 1.f / lsum;
+    uint16_t* prow = part.out + pr * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * db + 8 * g4 + 4 * half;
-        *reinterpret_cast<float4*>(acc + d) =
-            make_float4(o[db][4 * g4 + 0], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
+        uint2 v;
+        v.x = pack_bf16x2(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv);
+        v.y = pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
+        *reinterpret_cast<uint2*>(prow + d) = v;
       }
     if (half == 0) {
       part.m[pr] = m * scale_log2;

@@ -29,6 +29,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+// The two bf16 values of a dword (low half first) as fp32, exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
 // acc + sum_i a_i * b_i over 8 bf16 pairs held in 4 dwords, fp32 accumulate
 // (v_dot2_f32_bf16: two products per instruction).

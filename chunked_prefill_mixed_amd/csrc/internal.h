@@ -19,6 +19,15 @@ struct Partials {
   float* l;
 };
 
+// A split chunk tile's pieces: each piece's output divided by its own sum, in
+// bf16 (a weighted mean of V rows, so within V's range), with that sum and
+// the running max in fp32.
+struct ChunkPartials {
+  uint16_t* out;
+  float* m;
+  float* l;
+};
+
 hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* bt, int bt_stride, const int32_t* qsl,
                          const int32_t* splits, int num_splits, int num_q_heads, int num_kv_heads,
@@ -28,7 +37,7 @@ hipError_t launch_decode(const void* q, const void* k_cache, const void* v_cache
 hipError_t launch_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, int num_q_heads, int num_kv_heads,
-                        int head_dim, float scale_log2, void* out, float* lse, Partials part,
+                        int head_dim, float scale_log2, void* out, float* lse, ChunkPartials part,
                         hipStream_t stream);
 
 // Decode pieces and chunk tiles of one step in one launch (mixed.hip); both
@@ -37,13 +46,13 @@ hipError_t launch_mixed(const void* q, const void* k_cache, const void* v_cache,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, const int32_t* splits, int num_splits,
                         int num_q_heads, int num_kv_heads, int head_dim, float scale_log2,
-                        void* out, float* lse, Partials cpart, Partials dpart,
+                        void* out, float* lse, ChunkPartials cpart, Partials dpart,
                         hipStream_t stream);
 
 // Both merges of a step in one launch (either count may be 0).
 hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const int32_t* cmerges,
                          int num_chunk_merges, const int32_t* qsl, int num_q_heads,
-                         int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
+                         int num_kv_heads, int head_dim, Partials dws, ChunkPartials cws, void* out,
                          float* lse, hipStream_t stream);
 
 }  // namespace cpa

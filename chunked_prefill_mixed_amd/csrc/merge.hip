@@ -92,18 +92,20 @@ __device__ __forceinline__ void merge_decode_head(const int32_t* __restrict__ me
 
 // RPW rows of one (chunk merge entry, KV head) per workgroup; each row is
 // handled by LPR = D/4 lanes, each owning 4 consecutive d values, so a partial
-// row is one contiguous sweep.  Pieces are taken B at a time (2, 4 or 8, the
-// smallest that takes the tile's pieces in one batch, up to 8): every lane
-// issues all loads of a batch (each piece's max and sum, the same address for
-// the row's lanes, and its 16 bytes of the piece's partial) before using any,
-// so a batch costs one memory round trip; batches fold into a running max,
-// sum and output as in the decode merge.
+// row is one contiguous sweep.  A chunk piece's partial is its output over its
+// own keys, already divided by its sum l_i, in bf16: it enters with weight
+// l_i 2^(m_i - M).  Pieces are taken B at a time (2, 4 or 8, the smallest
+// that takes the tile's pieces in one batch, up to 8): every lane issues all
+// loads of a batch (each piece's max and sum, the same address for the row's
+// lanes, and its 8 bytes of the piece's output) before using any, so a batch
+// costs one memory round trip; batches fold into a running max, sum and
+// output as in the decode merge.
 constexpr int kChunkMergeBatch = 8;  // the largest chunk-merge batch
 
 template <int D, int G>
 __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ merges, int block,
                                                  const int32_t* __restrict__ qsl, int num_q_heads,
-                                                 int num_kv_heads, const Partials& part,
+                                                 int num_kv_heads, const ChunkPartials& part,
                                                  uint16_t* __restrict__ out,
                                                  float* __restrict__ lse) {
   constexpr int LPR = D / 4;             // lanes per row
@@ -130,14 +132,14 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
     constexpr int B = decltype(bsz)::value;
     for (int i0 = 0; i0 < n; i0 += B) {
       float mi[B], lv[B];
-      float4 a[B];
+      uint2 a[B];
 #pragma unroll
       for (int i = 0; i < B; ++i) {
         const bool in = i0 + i < n;
         const int64_t pr = base + (int64_t)(in ? i0 + i : i0) * stride;
         mi[i] = in ? part.m[pr] : neg_inf();
         lv[i] = part.l[pr];
-        a[i] = *reinterpret_cast<const float4*>(part.acc + pr * D + d);
+        a[i] = *reinterpret_cast<const uint2*>(part.out + pr * D + d);
       }
       float Mb = M;
 #pragma unroll
@@ -147,9 +149,10 @@ __device__ __forceinline__ void merge_chunk_rows(const int32_t* __restrict__ mer
       o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
 #pragma unroll
       for (int i = 0; i < B; ++i) {
-        const float w = fast_exp2(mi[i] - Mb);  // 0 for the padding entries
-        L += w * lv[i];
-        o.x += w * a[i].x; o.y += w * a[i].y; o.z += w * a[i].z; o.w += w * a[i].w;
+        const float w = fast_exp2(mi[i] - Mb) * lv[i];  // 0 for the padding entries
+        L += w;
+        o.x += w * bf16_lo(a[i].x); o.y += w * bf16_hi(a[i].x);
+        o.z += w * bf16_lo(a[i].y); o.w += w * bf16_hi(a[i].y);
       }
       M = Mb;
     }
@@ -175,7 +178,7 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(
     const int32_t* __restrict__ dmerges, int num_decode_pairs, const int32_t* __restrict__ cmerges,
     int chunk_blocks, const int32_t* __restrict__ qsl, int num_q_heads, int num_kv_heads,
-    Partials dws, Partials cws, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    Partials dws, ChunkPartials cws, uint16_t* __restrict__ out, float* __restrict__ lse) {
   if ((int)blockIdx.x < chunk_blocks) {
     merge_chunk_rows<D, G>(cmerges, blockIdx.x, qsl, num_q_heads, num_kv_heads, cws, out, lse);
     return;
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
 
 hipError_t launch_merges(const int32_t* dmerges, int num_decode_merges, const int32_t* cmerges,
                          int num_chunk_merges, const int32_t* qsl, int num_q_heads,
-                         int num_kv_heads, int head_dim, Partials dws, Partials cws, void* out,
+                         int num_kv_heads, int head_dim, Partials dws, ChunkPartials cws, void* out,
                          float* lse, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   const int chunk_blocks =

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64 * chunk_waves(D), 8 / chunk_waves(D)) void mixed
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ tiles, int num_tiles, const int32_t* __restrict__ splits,
     int num_items, int num_q_heads, int num_kv_heads, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, Partials cpart, Partials dpart,
+    uint16_t* __restrict__ out, float* __restrict__ lse, ChunkPartials cpart, Partials dpart,
     int decode_lead) {
   const int w = blockIdx.x;
   const int chunk_wgs = num_tiles * num_kv_heads;
@@ -51,7 +51,7 @@ static void launch_mixed_t(const void* q, const void* kc, const void* vc, const 
                            int bt_stride, const int32_t* qsl, const int32_t* ctx,
                            const int32_t* tiles, int num_tiles, const int32_t* splits,
                            int num_splits, int hq, int hkv, float sl2, void* out, float* lse,
-                           Partials cpart, Partials dpart, hipStream_t stream) {
+                           ChunkPartials cpart, Partials dpart, hipStream_t stream) {
   // a run-time group (G = 0) of more than 16 heads takes a wave per 16 heads
   const int items = num_splits * hkv * (G > 0 ? 1 : decode_column_blocks(hq / hkv));
   constexpr int W = chunk_waves(D);  // decode items per workgroup
@@ -69,7 +69,7 @@ hipError_t launch_mixed(const void* q, const void* k_cache, const void* v_cache,
                         int bt_stride, const int32_t* qsl, const int32_t* ctx,
                         const int32_t* tiles, int num_tiles, const int32_t* splits, int num_splits,
                         int num_q_heads, int num_kv_heads, int head_dim, float scale_log2,
-                        void* out, float* lse, Partials cpart, Partials dpart,
+                        void* out, float* lse, ChunkPartials cpart, Partials dpart,
                         hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   // G = 0 instances: any other group, read at run time

@@ -70,10 +70,11 @@ inline bool supported_kv_heads(int h) { return h >= 1 && h <= kMaxKvHeads; }
 
 namespace cpa {
 
-// Byte offsets of the fp32 partial-result regions inside the caller's
-// workspace.  Decode slot: acc [Hq][D], m [Hq], l [Hq].  Chunk slot: acc
-// [Hkv][R rows][D], m and l [Hkv][R], R = chunk_rows(D).  Max values are
-// stored in log2 units of the scaled score.
+// Byte offsets of the partial-result regions inside the caller's workspace.
+// Decode slot: acc [Hq][D], m [Hq], l [Hq], fp32 (acc unnormalised).  Chunk
+// slot: out [Hkv][R rows][D] bf16 (each piece's output divided by its own
+// sum), m and l [Hkv][R] fp32, R = chunk_rows(D).  Max values are stored in
+// log2 units of the scaled score.
 struct WorkspaceLayout {
   size_t dec_acc, dec_m, dec_l, chk_acc, chk_m, chk_l, total;
 };
@@ -88,7 +89,7 @@ inline WorkspaceLayout workspace_layout(int64_t dec_slots, int64_t chk_slots, in
   w.dec_acc = at; at += up(dr * head_dim * 4);
   w.dec_m = at;   at += up(dr * 4);
   w.dec_l = at;   at += up(dr * 4);
-  w.chk_acc = at; at += up(cr * head_dim * 4);
+  w.chk_acc = at; at += up(cr * head_dim * 2);
   w.chk_m = at;   at += up(cr * 4);
   w.chk_l = at;   at += up(cr * 4);
   w.total = at;

@@ -160,7 +160,7 @@ typedef struct {
   int32_t num_chunk_tiles;     /* one workgroup per (tile, KV head) */
   int32_t num_chunk_merges;    /* chunk tiles whose prefix keys were split in several pieces */
   int32_t num_decode_partials; /* decode partial slots: num_q_heads x (head_dim + 2) fp32 each */
-  int32_t num_chunk_partials;  /* chunk partial slots: num_kv_heads x R x (head_dim + 2) fp32 */
+  int32_t num_chunk_partials;  /* chunk partial slots: num_kv_heads x R x (head_dim bf16 + 2 fp32) */
 } cpa_plan_counts_t;
 
 /* Host arrays filled by cpa_build_metadata; the caller provides them with the
@@ -243,11 +243,13 @@ int cpa_append_kv(const void* k_new, const void* v_new, const int32_t* d_query_s
 
 /*
  * cpa_workspace_size -- bytes of device workspace cpa_attention needs for a
- * plan with these counts: fp32 partial sums plus the running max and sum of
- * every split piece, i.e. (num_decode_partials * num_q_heads +
- * num_chunk_partials * num_kv_heads * R) * (head_dim + 2) * 4 bytes (R, the
- * rows of a chunk tile: 256 at head_dim 128, 128 at 64), each region rounded
- * up to 256 bytes.  0 when nothing is split.
+ * plan with these counts: the partial results of every split piece, with its
+ * running max and sum in fp32.  A decode piece keeps its unnormalised fp32
+ * output, a chunk piece its output divided by its own sum in bf16:
+ * num_decode_partials * num_q_heads * (head_dim + 2) * 4 bytes plus
+ * num_chunk_partials * num_kv_heads * R * (head_dim * 2 + 2 * 4) bytes (R,
+ * the rows of a chunk tile: 256 at head_dim 128, 128 at 64), each of the six
+ * regions rounded up to 256 bytes.  0 when nothing is split.
  */
 size_t cpa_workspace_size(const cpa_plan_counts_t* counts, int num_q_heads, int num_kv_heads,
                           int head_dim);
@@ -290,7 +292,7 @@ int cpa_attention(const void* q, const void* k_cache, const void* v_cache,
  * harnesses that forbid hipMalloc.
  *
  * Same arguments, meaning and results as cpa_attention, without workspace /
- * workspace_bytes: the fp32 partial results of split pieces live in a
+ * workspace_bytes: the partial results of split pieces live in a
  * file-scope device array of CPA_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
  * library, one copy per GPU, held until the process ends.  The call itself
  * allocates nothing (no hipMalloc, no hipFree); the first call on a device

@@ -439,12 +439,13 @@ def test_builder_valid_block_table_accepted(lib):
 def test_workspace_size(lib):
     up = lambda b: math.ceil(b / 256) * 256
     c = cpa.cpa_plan_counts_t(5, 2, 3, 1, 7, 3)
-    # chunk slots: 8 KV heads x R rows (256 at head_dim 128, 128 at 64)
+    # decode slots: fp32 acc, m, l per query head; chunk slots: 8 KV heads x R
+    # rows (256 at head_dim 128, 128 at 64), bf16 outputs and fp32 m, l
     want = (up(7 * 32 * 128 * 4) + 2 * up(7 * 32 * 4)
-            + up(3 * 8 * 256 * 128 * 4) + 2 * up(3 * 8 * 256 * 4))
+            + up(3 * 8 * 256 * 128 * 2) + 2 * up(3 * 8 * 256 * 4))
     assert cpa.cpa_workspace_size(c, 32, 8, 128) == want
     want64 = (up(7 * 32 * 64 * 4) + 2 * up(7 * 32 * 4)
-              + up(3 * 8 * 128 * 64 * 4) + 2 * up(3 * 8 * 128 * 4))
+              + up(3 * 8 * 128 * 64 * 2) + 2 * up(3 * 8 * 128 * 4))
     assert cpa.cpa_workspace_size(c, 32, 8, 64) == want64
     c0 = cpa.cpa_plan_counts_t(5, 0, 3, 0, 0, 0)
     assert cpa.cpa_workspace_size(c0, 32, 8, 128) == 0
