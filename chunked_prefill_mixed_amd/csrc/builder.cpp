@@ -122,8 +122,8 @@ std::vector<int32_t> pieces_within(const std::vector<int64_t>& tile_keys, int nu
   }
 }
 
-// Keys' worth of time a piece of a split tile costs beyond its own keys (its
-// fp32 partial write and the merge's read of it), and what a plan with any
+// Keys' worth of time a piece of a split tile costs beyond its own keys
+// (writing its partial output and the merge's read of it), and what a plan with any
 // split tile costs once more for the merging.  Both were fitted to same-box
 // timings: a one-round step whose causal tiles run up to twice the mean (a
 // 2048-token chunk at prefix 0) gains less from splitting than its merges
