@@ -530,15 +530,16 @@ def test_config_end_to_end(config):
         del ds
 
 
-@pytest.mark.parametrize("config", [4, 5])
-def test_kv_shard_end_to_end(config):
-    """One GPU's share of the long-context and heavy-mixed steps split 8 ways
-    by KV head (4 query heads on 1 KV head: the planner cuts the few chunk
-    tiles into key pieces to fill the GPU), every instance: the pool
-    bit-exact and every token against the oracle."""
+@pytest.mark.parametrize("config,shard", [(4, 8), (5, 8), (5, 4), (5, 2)])
+def test_kv_shard_end_to_end(config, shard):
+    """One GPU's share of the long-context and heavy-mixed steps split 8, 4 or
+    2 ways by KV head (4 query heads on 1, 2 or 4 KV heads: the planner deals
+    the pieces over the XCD ranges of a head and cuts uneven tiles into two
+    or three rounds of key pieces), every instance: the pool bit-exact and
+    every token against the oracle."""
     import torch
     for inst in range(workloads.num_instances(config)):
-        w = workloads.make_workload(config, inst, kv_shard=8)
+        w = workloads.make_workload(config, inst, kv_shard=shard)
         ds = DeviceStep(w)
         print(f"config {config} instance {inst}: {w.name}, {ds.num_tokens} tokens", flush=True)
         ds.run()
