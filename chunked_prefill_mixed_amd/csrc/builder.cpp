@@ -77,8 +77,8 @@ int adaptive_cap(int base_chunk, int num_decodes) {
 // longest wave: pick the fewest rounds k of R waves (R = decode_waves_target,
 // one per SIMD) for which pieces of at most 64 pages exist, then the
 // smallest page count p such that the rows, each cut into ceil(pages/p)
-// pieces, give at most k * R waves (piece x KV head x block of 16 query heads
-// of the group, one block for G <= 16).  Every wave then
+// pieces, give at most k * R waves (piece x KV head x 32 query heads of the
+// group: one wave for G <= 32).  Every wave then
 // starts in pass 1..k and no wave reads more than p pages.  p is kept at 8 pages or
 // more: a shorter piece is mostly start-up latency and lengthens the merge.
 int pick_piece_pages(const std::vector<int64_t>& row_pages, int waves_per_piece, int head_dim) {
@@ -321,7 +321,7 @@ extern "C" int cpa_build_metadata(const cpa_req_t* reqs, int n_reqs, const cpa_b
   const int piece_pages =
       split ? 0
             : pick_piece_pages(row_pages,
-                               params->num_kv_heads * cpa::decode_column_blocks(group),
+                               params->num_kv_heads * cpa::decode_group_waves(group),
                                params->head_dim);
   std::vector<int32_t> dsplits, dmerges, tiles;
   int partials = 0;

@@ -1,5 +1,5 @@
-// Split-KV decode kernel: one wave per (key piece, KV head, block of 16 query
-// heads of the group), 4 per workgroup.
+// Split-KV decode kernel: one wave per (key piece, KV head, 32 query heads of
+// the group), 4 per workgroup.
 // The body and its design are in decode_body.h.
 
 #include "decode_body.h"
@@ -20,8 +20,8 @@ template <int D, int G>
 static void launch_decode_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
                             int bt_stride, const int32_t* splits, int num_splits, int hq, int hkv,
                             float sl2, void* out, float* lse, Partials ws, hipStream_t stream) {
-  // a run-time group (G = 0) of more than 16 heads takes a wave per 16 heads
-  const int items = num_splits * hkv * (G > 0 ? 1 : decode_column_blocks(hq / hkv));
+  // a run-time group (G = 0) of more than 32 heads takes a wave per 32 heads
+  const int items = num_splits * hkv * (G > 0 ? 1 : decode_group_waves(hq / hkv));
   hipLaunchKernelGGL((decode_kernel<D, G>), dim3((items + kDecodeWaves - 1) / kDecodeWaves),
                      dim3(64 * kDecodeWaves), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,

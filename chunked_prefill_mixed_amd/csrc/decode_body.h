@@ -17,10 +17,11 @@
 //                                      of step kk (pieces 4kk..4kk+3 of all 16
 //                                      keys) is one contiguous 1 KB load;
 //                                      column n of Q^T holds query head n of
-//                                      the group (16 per wave: a group of more
-//                                      takes one wave per 16 heads; columns
-//                                      past the group repeat a head and are
-//                                      never stored)
+//                                      the group (16 per block; a run-time
+//                                      group holds two blocks per wave against
+//                                      the same K/V, one wave per 32 heads;
+//                                      columns past the group repeat a head
+//                                      and are never stored)
 //   O^T[D][16 cols] += V^T P^T         v_mfma_f32_16x16x16_bf16, D/16 blocks;
 //                                      V pages are stored transposed ([D][16])
 //                                      so each lane loads its A operand as 8
@@ -71,32 +72,43 @@ __device__ __forceinline__ void decode_body(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int item = first_item + wave;  // wave w of the workgroup takes item first_item + w
   if (item >= num_items) return;  // whole wave; no workgroup barrier below
-  // query heads per KV head: compiled in (at most 8, one block of columns), or
-  // (G = 0) read at run time, in ceil(G / 16) blocks of 16 columns, each block
-  // its own item: item = (piece x KV head) x blocks + block
+  // query heads per KV head: compiled in (at most 8, one block of 16
+  // columns), or (G = 0) read at run time, in ceil(G / 16) blocks of 16
+  // columns, up to NB of them per wave against the same K/V registers:
+  // item = (piece x KV head) x waves + wave of the group
   static_assert(G >= 0 && G <= kDecodeCols, "compiled groups fit one block of columns");
+  constexpr int NB = G > 0 ? 1 : kDecodeWaveBlocks;
   const int grp = G > 0 ? G : num_q_heads / num_kv_heads;
-  const int ncb = G > 0 ? 1 : decode_column_blocks(grp);
-  const int cb = G > 0 ? 0 : item % ncb;
-  const int pk = G > 0 ? item : item / ncb;
+  const int nwv = G > 0 ? 1 : decode_group_waves(grp);
+  const int wv = G > 0 ? 0 : item % nwv;
+  const int pk = G > 0 ? item : item / nwv;
   const int g = pk % num_kv_heads;
   const int4 e = reinterpret_cast<const int4*>(splits)[pk / num_kv_heads];
   const int row = e.x, kv_begin = e.y, kv_end = e.z, slot = e.w;
   // decode rows come first and hold one token each, so row s is packed token s
   const int t = row;
-  const int n = lane & 15;                 // column of S^T and O^T
-  const int col = kDecodeCols * cb + n;    // the column's query head within the group
+  const int n = lane & 15;   // column of S^T and O^T
   const int g4 = lane >> 4;  // lane group: d pieces of S^T, keys 4*g4..+4 of P^T and O^T
-  // columns past the group repeat a head of it and are never stored
+  // blocks of this wave that hold heads of the group (wave-uniform: the last
+  // wave of an odd block count holds one)
+  const bool two = NB > 1 && decode_column_blocks(grp) - NB * wv > 1;
+  // block b's column n holds query head col[b] of the group; columns past the
+  // group repeat a head of it and are never stored
   constexpr int kGroup = G > 0 ? G : 1;  // the compiled group (a divisor in the G > 0 path)
-  const int hq = g * grp + (G > 0 ? n % kGroup : min(col, grp - 1));
+  int col[NB], hq[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    col[b] = kDecodeCols * (NB * wv + b) + n;
+    hq[b] = g * grp + (G > 0 ? n % kGroup : min(col[b], grp - 1));
+  }
 
   // B operand of S^T: Q[hq][32 kk + 8 g4 .. +8]
-  uint4 qf[KK];
-  {
-    const uint16_t* qrow = q + ((int64_t)t * num_q_heads + hq) * D + 8 * g4;
+  uint4 qf[NB][KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+  for (int b = 0; b < NB; ++b) {
+    const uint16_t* qrow = q + ((int64_t)t * num_q_heads + hq[b]) * D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[b][kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
 
   const int32_t* btrow = bt + (int64_t)row * bt_stride;
@@ -123,60 +135,79 @@ __device__ __forceinline__ void decode_body(
     for (int mb = 0; mb < MB; ++mb) vd[mb] = buffer_load8<kNonTemporal>(vr, vbyte + 512 * mb);
   };
 
-  float m = neg_inf(), lsum = 0.f;
-  f32x4_t acc[MB];
+  float m[NB], lsum[NB];
+  f32x4_t acc[NB][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) {
+    m[b] = neg_inf();
+    lsum[b] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[b][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
+  // one block's softmax and O^T update for the page, from its S^T
+  auto softmax_pv = [&](int b, f32x4_t s, const uint2 (&vc)[MB]) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    // move the reference max only when this page exceeds it by more than 2^8
+    // (always on the first page, where m is -inf)
+    const bool grow = (mx - m[b]) * scale_log2 > 8.f;
+    if (__any(grow)) {
+      // rare: rescale the running sums; the empty asm keeps the compiler from
+      // hoisting this out of the branch and running it on every page
+      asm volatile("" ::: "memory");
+      const float mn = grow ? mx : m[b];
+      const float alpha = fast_exp2((m[b] - mn) * scale_log2);
+      m[b] = mn;
+      lsum[b] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[b][mb] *= alpha;
+    }
+    const float msc = m[b] * scale_log2;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], scale_log2, -msc));
+    lsum[b] += (p[0] + p[1]) + (p[2] + p[3]);
+    const uint2 pb = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(short4_t, vc[mb]), __builtin_bit_cast(short4_t, pb), acc[b][mb], 0,
+          0, 0);
+  };
   auto compute_page = [&](int i, const uint4 (&kc)[KK], uint2 (&vc)[MB]) {
     const int key0 = (pg0 + i) * kBlock;
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t s[NB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[kk]),
-                                                  __builtin_bit_cast(bf16x8_t, qf[kk]), s, 0, 0,
-                                                  0);
+    for (int b = 0; b < NB; ++b) {
+      s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (b > 0 && !two) continue;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[kk]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[b][kk]),
+                                                       s[b], 0, 0, 0);
+    }
     // the piece's last page (or one past it): mask keys at or past kv_end,
     // and zero their V entries (unwritten or sentinel data must not reach
     // P*V, where 0 * NaN would not vanish).  The test is wave-uniform.
     if (key0 + kBlock > kv_end) {
       const int nvalid = kv_end - key0 - 4 * g4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r >= nvalid) s[r] = neg_inf();
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (r >= nvalid) s[b][r] = neg_inf();
       const uint32_t keep0 = (nvalid > 0 ? 0xFFFFu : 0u) | (nvalid > 1 ? 0xFFFF0000u : 0u);
       const uint32_t keep1 = (nvalid > 2 ? 0xFFFFu : 0u) | (nvalid > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) vc[mb] = make_uint2(vc[mb].x & keep0, vc[mb].y & keep1);
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    // move the reference max only when this page exceeds it by more than 2^8
-    // (always on the first page, where m is -inf)
-    const bool grow = (mx - m) * scale_log2 > 8.f;
-    if (__any(grow)) {
-      // rare: rescale the running sums; the empty asm keeps the compiler from
-      // hoisting this out of the branch and running it on every page
-      asm volatile("" ::: "memory");
-      const float mn = grow ? mx : m;
-      const float alpha = fast_exp2((m - mn) * scale_log2);
-      m = mn;
-      lsum *= alpha;
+    softmax_pv(0, s[0], vc);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
-    }
-    const float msc = m * scale_log2;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], scale_log2, -msc));
-    lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    const uint2 pb = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vc[mb]),
-                                                          __builtin_bit_cast(short4_t, pb),
-                                                          acc[mb], 0, 0, 0);
+    for (int b = 1; b < NB; ++b)
+      if (two) softmax_pv(b, s[b], vc);
   };
 
   // pages in groups of kStages with no early exit: pages past the piece end
@@ -195,31 +226,40 @@ __device__ __forceinline__ void decode_body(
     }
   }
 
-  // column sums over the 4 lane groups (each summed its own keys)
-  lsum += xor_lane(lsum, 16);
-  lsum += xor_lane(lsum, 32);
-  if (col >= grp) return;
+  // column sums over the 4 lane groups (each summed its own keys), with every
+  // lane active
+  float ls[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    ls[b] = lsum[b] + xor_lane(lsum[b], 16);
+    ls[b] += xor_lane(ls[b], 32);
+  }
   const int d0 = 4 * g4;  // this lane's O^T rows inside each 16-row block
-  if (slot < 0) {
-    const float inv = 1.f / lsum;
-    uint16_t* orow = out + ((int64_t)t * num_q_heads + hq) * D + d0;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      *reinterpret_cast<uint2*>(orow + 16 * mb) =
-          make_uint2(pack_bf16x2(acc[mb][0] * inv, acc[mb][1] * inv),
-                     pack_bf16x2(acc[mb][2] * inv, acc[mb][3] * inv));
-    if (lse && g4 == 0)
-      lse[(int64_t)t * num_q_heads + hq] = (m * scale_log2 + __log2f(lsum)) * kLn2;
-  } else {
-    const int64_t ph = (int64_t)slot * num_q_heads + hq;
-    float* arow = ws.acc + ph * D + d0;
+  for (int b = 0; b < NB; ++b) {
+    if (b > 0 && !two) break;
+    if (col[b] >= grp) continue;
+    if (slot < 0) {
+      const float inv = 1.f / ls[b];
+      uint16_t* orow = out + ((int64_t)t * num_q_heads + hq[b]) * D + d0;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      *reinterpret_cast<float4*>(arow + 16 * mb) =
-          make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-    if (g4 == 0) {
-      ws.m[ph] = m * scale_log2;
-      ws.l[ph] = lsum;
+      for (int mb = 0; mb < MB; ++mb)
+        *reinterpret_cast<uint2*>(orow + 16 * mb) =
+            make_uint2(pack_bf16x2(acc[b][mb][0] * inv, acc[b][mb][1] * inv),
+                       pack_bf16x2(acc[b][mb][2] * inv, acc[b][mb][3] * inv));
+      if (lse && g4 == 0)
+        lse[(int64_t)t * num_q_heads + hq[b]] = (m[b] * scale_log2 + __log2f(ls[b])) * kLn2;
+    } else {
+      const int64_t ph = (int64_t)slot * num_q_heads + hq[b];
+      float* arow = ws.acc + ph * D + d0;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        *reinterpret_cast<float4*>(arow + 16 * mb) =
+            make_float4(acc[b][mb][0], acc[b][mb][1], acc[b][mb][2], acc[b][mb][3]);
+      if (g4 == 0) {
+        ws.m[ph] = m[b] * scale_log2;
+        ws.l[ph] = ls[b];
+      }
     }
   }
 }

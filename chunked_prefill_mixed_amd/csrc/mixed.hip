@@ -52,8 +52,8 @@ static void launch_mixed_t(const void* q, const void* kc, const void* vc, const 
                            const int32_t* tiles, int num_tiles, const int32_t* splits,
                            int num_splits, int hq, int hkv, float sl2, void* out, float* lse,
                            ChunkPartials cpart, Partials dpart, hipStream_t stream) {
-  // a run-time group (G = 0) of more than 16 heads takes a wave per 16 heads
-  const int items = num_splits * hkv * (G > 0 ? 1 : decode_column_blocks(hq / hkv));
+  // a run-time group (G = 0) of more than 32 heads takes a wave per 32 heads
+  const int items = num_splits * hkv * (G > 0 ? 1 : decode_group_waves(hq / hkv));
   constexpr int W = chunk_waves(D);  // decode items per workgroup
   const int decode_wgs = (items + W - 1) / W;
   const int decode_lead = decode_wgs <= mixed_slots(D) ? (decode_wgs + 7) / 8 * 8 : 0;

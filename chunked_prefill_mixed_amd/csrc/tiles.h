@@ -44,11 +44,18 @@ inline int mixed_slots(int head_dim) { return 256 * (head_dim > 64 ? 1 : 3); }
 // (its last chunk_rows % G rows, if any, hold no query and store nothing).
 inline int chunk_tile_tokens(int group, int head_dim) { return chunk_rows(head_dim) / group; }
 
-// Query heads one decode wave serves: the 16 columns of its S^T product.  A
-// larger group takes ceil(G / 16) waves per (piece, KV head), one per block
-// of 16 heads.
+// Query heads one block of a decode wave serves: the 16 columns of its S^T
+// product.
 constexpr int kDecodeCols = 16;
 constexpr int decode_column_blocks(int group) { return (group + kDecodeCols - 1) / kDecodeCols; }
+// A wave of the run-time-group decode holds up to kDecodeWaveBlocks such
+// blocks against the same K/V registers, so a group of up to 32 heads reads
+// each page once; larger groups take ceil(blocks / 2) waves per (piece, KV
+// head).  The compiled groups (at most 8 heads) take one wave.
+constexpr int kDecodeWaveBlocks = 2;
+constexpr int decode_group_waves(int group) {
+  return (decode_column_blocks(group) + kDecodeWaveBlocks - 1) / kDecodeWaveBlocks;
+}
 
 // Any number of query heads per KV head up to one chunk tile's rows, so that
 // a tile holds at least one token.  G = 1, 2, 4 and 8 have kernels compiled

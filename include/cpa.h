@@ -41,7 +41,7 @@
  *     tile's rows R (256 at head_dim 128, 128 at 64); num_kv_heads at most
  *     256; block_size 16; bf16 only.  G = 1, 2, 4 and 8 run kernels compiled
  *     for them, any other G the same kernels with G read at run time; a
- *     decode piece takes one wave per 16 query heads of its group.
+ *     decode piece takes one wave per 32 query heads of its group.
  *
  * KV cache layout (one tensor each for K and V; the same page id in both)
  *   k_cache [num_blocks][num_kv_heads][head_dim/8][16][8]
@@ -155,7 +155,7 @@ typedef struct {
  * head_dim 64: floor(R / G) tokens, G = num_q_heads / num_kv_heads (when G does
  * not divide R, a tile's last R mod G rows hold no query). */
 typedef struct {
-  int32_t num_decode_splits;   /* one wave per (split, KV head, 16 query heads of the group) */
+  int32_t num_decode_splits;   /* one wave per (split, KV head, 32 query heads of the group) */
   int32_t num_decode_merges;   /* decode rows whose keys were split in several pieces */
   int32_t num_chunk_tiles;     /* one workgroup per (tile, KV head) */
   int32_t num_chunk_merges;    /* chunk tiles whose prefix keys were split in several pieces */

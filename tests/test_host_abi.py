@@ -247,15 +247,16 @@ def test_builder_plans_any_group(lib, G, D):
 
 
 def test_decode_pieces_count_the_waves_of_wide_groups(lib):
-    """A group of more than 16 heads takes one decode wave per 16 heads, so
-    the planner cuts the rows into fewer pieces for the same wave budget."""
+    """A group of more than 32 heads takes one decode wave per 32 heads (two
+    blocks of 16 columns per wave), so the planner cuts the rows into fewer
+    pieces for the same wave budget; up to 32 heads take one wave."""
     reqs = [oracle.Request(i, 3000 + 37 * i, 3001 + 37 * i, True) for i in range(40)]
     pieces = {}
-    for G in (16, 32, 64):
+    for G in (16, 32, 64, 128):
         m = cpa.cpa_build_metadata(reqs, token_budget=64, long_prefill_cap=0, num_q_heads=G,
                                    num_kv_heads=1, head_dim=128)
         pieces[G] = m["counts"].num_decode_splits
-    assert pieces[16] > pieces[32] > pieces[64] >= len(reqs)
+    assert pieces[16] == pieces[32] > pieces[64] > pieces[128] >= len(reqs)
 
 
 @pytest.mark.parametrize("policy", ["truncate", "defer", "quota"])
